@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark of the selective diagonal state-space scan on one MI355X.
+
+One step = one pass of the whole hot path over one batch: the forward with the
+per-step states H materialised, then the backward reverse sweep returning all six
+gradients, on the fp32 workload B=8, T=2048, D=768, DS=16 (synthetic seeded
+inputs, resident in HBM before timing starts).  ``value`` is B*T*D elements per
+second of that step.  The JSON line also carries:
+
+* ``roofline`` for the kernel pair that dominates the step, timed live with HIP
+  events on the stream the library launches on (torch's current stream);
+* ``cpu_baseline``: the fp64 CPU oracle timed on this host on the same workload;
+* ``fwd_only``: forward-only throughput on the three forward workloads
+  (fp32 8x1024x256x16; bf16 16x4096x1024x16; bf16 4x16384x2048x16 as 8 calls
+  carrying hT -> h0), each with its ALU roofline fraction.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-fwd-only]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published peaks and unit counts.
+HBM_PEAK_GBS = 8000.0
+CUS, CLOCK_GHZ = 256, 2.4
+# fp32 vector: 157.3 TFLOP/s = 128 fp32 lanes per CU per clock (256 CUs, 2.4 GHz), i.e.
+# 78.6e12 single-lane fp32 ops/s; plain v_fma_f32 / v_mul_f32 reach that rate on gfx950.
+FP32_LANES_PER_CU_CLK = 128
+VALU_LANE_OPS = CUS * FP32_LANES_PER_CU_CLK * CLOCK_GHZ * 1e9  # 78.6e12 / s
+# v_exp_f32 issues at a quarter of the fp32 lane rate: 32 lanes per CU per clock.
+EXP_RATE = CUS * (FP32_LANES_PER_CU_CLK // 4) * CLOCK_GHZ * 1e9  # 19.7e12 / s
+FWD_VALU_OPS_PER_STATE = 4  # delta*A, (delta x)*b, a*h+u, h*c+y
+FWD_EXP_PER_STATE = 1
+
+
+def alu_peak_states_per_s() -> float:
+    """(step, channel, state) updates per second if VALU and v_exp_f32 issue back to back."""
+    return 1.0 / (FWD_VALU_OPS_PER_STATE / VALU_LANE_OPS + FWD_EXP_PER_STATE / EXP_RATE)
+
+
+def fwd_alg_bytes(B, T, D, DS, s, with_H=False):
+    """Bytes the forward must move: x, delta in, y out; b, c in; A, h0 in, hT out; H out."""
+    n = B * T * D
+    byt = 3 * s * n + 2 * s * B * T * DS + 4 * D * DS + 2 * 4 * B * D * DS
+    if with_H:
+        byt += 4 * n * DS
+    return byt
+
+
+def bwd_alg_bytes(B, T, D, DS, s):
+    """Bytes the backward must move: dy, x, delta in; H in; gx, gdelta out; b, c in; gb, gc out;
+    A in, gA out; h0 in, gh0 out."""
+    n = B * T * D
+    return (3 * s * n + 4 * n * DS + 2 * 4 * n + 2 * s * B * T * DS + 2 * 4 * B * T * DS + 2 * 4 * D * DS
+            + 2 * 4 * B * D * DS)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fwd-only", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the scan runs on a single MI355X and this build has no multi-GPU "
+              f"path (asked for --gpus {args.gpus}).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import workloads
+    from selective_state_space_sscan_amd import sscan_bwd, sscan_bwd_workspace, sscan_fwd, sscan_fwd_workspace
+    from selective_state_space_sscan_amd import sscan_plan_select
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    w = workloads.get("fwd_bwd_f32")
+    B, T, D, DS = w.B, w.T, w.D, w.DS
+    print(f"bench: {w.name} {w.note} on {torch.cuda.get_device_name(dev)}", file=sys.stderr, flush=True)
+    inp = workloads.make_inputs(w)
+    g = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
+    f32 = dict(dtype=torch.float32, device=dev)
+    y = torch.empty((B, T, D), **f32)
+    hT = torch.empty((B, D, DS), **f32)
+    H = torch.empty((B, T, D, DS), **f32)
+    outs = (torch.empty((B, T, D), **f32), torch.empty((B, T, D), **f32), torch.empty((B, T, DS), **f32),
+            torch.empty((B, T, DS), **f32), torch.empty((D, DS), **f32), torch.empty((B, D, DS), **f32))
+    ws_f = torch.empty(max(1, sscan_fwd_workspace(B, T, D, DS)), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(max(1, sscan_bwd_workspace(B, T, D, DS)), dtype=torch.uint8, device=dev)
+    plan_f = sscan_plan_select(B, T, D, DS)
+    plan_b = sscan_plan_select(B, T, D, DS, backward=True)
+
+    def fwd():
+        sscan_fwd(g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"], y=y, hT=hT, H=H, workspace=ws_f)
+
+    def bwd():
+        sscan_bwd(g["dy"], g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"], H, None, workspace=ws_b, out=outs)
+
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        ev[k][0].record(stream)
+        fwd()
+        ev[k][1].record(stream)
+        bwd()
+        ev[k][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = np.array([ev[k][0].elapsed_time(ev[k][1]) for k in range(K)])
+    bwd_ms = np.array([ev[k][1].elapsed_time(ev[k][2]) for k in range(K)])
+    step_ms = ev[0][0].elapsed_time(ev[K - 1][2]) / K
+    elems = B * T * D
+    value = elems / (step_ms * 1e-3)
+
+    fbytes = fwd_alg_bytes(B, T, D, DS, 4, with_H=True)
+    bbytes = bwd_alg_bytes(B, T, D, DS, 4)
+    f_avg, b_avg = float(fwd_ms.mean()), float(bwd_ms.mean())
+    if b_avg >= f_avg:
+        dom, dom_bytes, dom_ms = "sscan_bwd (bwd sweep + partial-sum reduce)", bbytes, b_avg
+    else:
+        dom, dom_bytes, dom_ms = "sscan_fwd (forward writing H)", fbytes, f_avg
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+                "alg_bytes_per_launch": int(dom_bytes), "avg_launch_ms": round(dom_ms, 5)}
+    detail = {
+        "fwd_ms": round(f_avg, 5), "bwd_ms": round(b_avg, 5),
+        "fwd_elems_per_s": elems / (f_avg * 1e-3), "bwd_elems_per_s": elems / (b_avg * 1e-3),
+        "fwd_hbm_frac": round(fbytes / (f_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "bwd_hbm_frac": round(bbytes / (b_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "plan_fwd": {"lanes": plan_f.lanes, "chunks": plan_f.chunks},
+        "plan_bwd": {"lanes": plan_b.lanes},
+        "wall_s_timed": round(wall, 4),
+    }
+    print(f"bench: step {step_ms:.4f} ms (fwd {f_avg:.4f}, bwd {b_avg:.4f})", file=sys.stderr, flush=True)
+
+    fwd_only = None if args.no_fwd_only else bench_fwd_only(dev, args.warmup, max(5, K // 5))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, w)
+
+    line = {
+        "metric": "selective-scan fwd B*T*D/sec on 1 MI355X; % of HBM/VALU roofline; bwd B*T*D/sec",
+        "value": value, "unit": "B*T*D elements/s (forward with H + backward, one step)",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": step_ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "fwd+bwd B=8 T=2048 D=768 DS=16 fp32, H materialised, 6 gradients",
+                   "B": B, "T": T, "D": D, "DS": DS, "io": "f32"},
+        "roofline": roofline, "cpu_baseline": cpu, "detail": detail, "fwd_only": fwd_only,
+    }
+    print(json.dumps(line))
+    return 0
+
+
+def bench_fwd_only(dev, warmup, reps):
+    """Forward-only rates on the three forward workloads, against the ALU roofline."""
+    import torch
+
+    import workloads
+    from selective_state_space_sscan_amd import sscan_fwd, sscan_fwd_workspace, sscan_plan_select
+
+    out = {}
+    peak = alu_peak_states_per_s()
+    for name in ("fwd_f32", "fwd_bf16", "long_chunked_bf16"):
+        w = workloads.get(name)
+        inp = workloads.make_inputs(w)
+        dt = inp["x"].dtype
+        s = 2 if dt == torch.bfloat16 else 4
+        bounds = workloads.chunk_bounds(w.T, w.chunks)
+        tc = bounds[0][1] - bounds[0][0]
+        # rotate input copies so the 256 MB last-level cache cannot hold a small workload
+        footprint = fwd_alg_bytes(w.B, w.T, w.D, w.DS, s)
+        ncopy = max(1, min(16, int(512e6 // max(footprint, 1))))
+        sets = []
+        for _ in range(ncopy):
+            sets.append({k: (None if v is None else v.to(dev)) for k, v in inp.items()})
+        del inp
+        y = torch.empty((w.B, w.T, w.D), dtype=dt, device=dev)
+        hT = torch.empty((w.B, w.D, w.DS), dtype=torch.float32, device=dev)
+        hbuf = torch.empty((w.B, w.D, w.DS), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(1, sscan_fwd_workspace(w.B, tc, w.D, w.DS, dt)), dtype=torch.uint8, device=dev)
+        plan = sscan_plan_select(w.B, tc, w.D, w.DS, dt)
+
+        def run(g):
+            # consecutive calls carry the state; the two state buffers alternate so no
+            # call's hT output aliases its h0 input
+            h = g["h0"]
+            for i, (t0, t1) in enumerate(bounds):
+                sl = slice(t0, t1)
+                dst = (hbuf, hT)[i % 2]
+                sscan_fwd(g["x"][:, sl], g["delta"][:, sl], g["A"], g["b"][:, sl], g["c"][:, sl], h,
+                          y=y[:, sl], hT=dst, workspace=ws)
+                h = dst
+
+        for i in range(warmup):
+            run(sets[i % ncopy])
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            run(sets[i % ncopy])
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        elems = w.B * w.T * w.D
+        states = elems * w.DS
+        out[name] = {"workload": w.note, "calls": len(bounds), "plan": {"lanes": plan.lanes, "chunks": plan.chunks},
+                     "ms": round(ms, 5), "elems_per_s": elems / (ms * 1e-3),
+                     "alu_frac": round(states / (ms * 1e-3) / peak, 4),
+                     "hbm_frac": round(fwd_alg_bytes(w.B, w.T, w.D, w.DS, s) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        print(f"bench: fwd-only {name}: {ms:.4f} ms, {elems / (ms * 1e-3):.3e} elem/s", file=sys.stderr, flush=True)
+        del sets
+        torch.cuda.empty_cache()
+    out["alu_peak_states_per_s"] = peak
+    return out
+
+
+def cpu_baseline(inp, w):
+    """The fp64 oracle, as it stands, on this host: one forward + backward of the whole workload."""
+    import oracle
+
+    n = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.fwd(inp["x"], inp["delta"], inp["A"], inp["b"], inp["c"], inp["h0"], nthreads=n)
+    t1 = time.perf_counter()
+    oracle.bwd(inp["dy"], inp["x"], inp["delta"], inp["A"], inp["b"], inp["c"], inp["h0"], None, nthreads=n)
+    t2 = time.perf_counter()
+    elems = w.B * w.T * w.D
+    return {"value": elems / (t2 - t0), "unit": "B*T*D elements/s (forward + backward)", "cores": n, "kind": "oracle",
+            "sample": f"the whole {w.B}x{w.T}x{w.D}x{w.DS} workload, one forward (no H) + one backward "
+                      f"(which recomputes its states); fwd {t1 - t0:.3f} s, bwd {t2 - t1:.3f} s"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

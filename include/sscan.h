@@ -1,0 +1,142 @@
+/*
+ * sscan.h -- C ABI of libsscan, the selective diagonal state-space scan for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (page "pssa-100m/pssa_kernels.py", module docstring), for each
+ * batch row b, channel d, state n and step t = 0..T-1:
+ *
+ *     h[b,t,d,n] = exp(delta[b,t,d] * A[d,n]) * h[b,t-1,d,n] + delta[b,t,d] * b[b,t,n] * x[b,t,d]
+ *     y[b,t,d]   = sum_n h[b,t,d,n] * c[b,t,n]
+ *
+ * with h[b,-1,d,n] = h0[b,d,n] and hT[b,d,n] = h[b,T-1,d,n].  The per-token
+ * states H = h (B,T,D,DS) may be materialised so that the backward is a single
+ * reverse sweep (same page, the ScanFn forward); hT of one call is the h0 of
+ * the next when a sequence is split into consecutive calls (same page, module
+ * docstring: h0 carried across chunks).  The backward (same page, scan_bwd)
+ * returns the gradients of L = sum(dy*y) + sum(dhT*hT) with respect to x,
+ * delta, b, c, A and h0.  The page's backward has no dhT term; passing
+ * dhT = NULL reproduces it.
+ *
+ * Conventions shared by every entry point:
+ *  - Layouts are row-major with the last dimension contiguous:
+ *      x, delta, dy   : (B,T,D)    element (b,t,d) at b*x_bstride + t*D + d
+ *      y, gx, gdelta  : (B,T,D)    element (b,t,d) at b*y_bstride + t*D + d
+ *      b, c           : (B,T,DS)   element (b,t,n) at b*bc_bstride + t*DS + n
+ *      gb, gc         : (B,T,DS)   contiguous
+ *      A, gA          : (D,DS)     contiguous
+ *      h0, hT, dhT, gh0 : (B,D,DS) contiguous
+ *      H              : (B,T,D,DS) contiguous
+ *    Only the batch strides are free, so a T-slice of a longer sequence is a
+ *    valid argument (input or output) without a copy.
+ *  - dtypes: x, delta, b, c, y and dy have the descriptor's io dtype (fp32 or
+ *    bf16).  A, h0, hT, H, dhT and every gradient are fp32.  Arithmetic and
+ *    the state are fp32; y is rounded to bf16 with round-to-nearest-even.
+ *  - Memory: every pointer is device memory owned by the caller.  The library
+ *    allocates nothing; scratch space is the caller's workspace, sized by the
+ *    *_workspace query.  Inputs are never written.  Outputs are overwritten,
+ *    never accumulated into, and must not alias any input or each other.
+ *  - A, h0, hT, H, dhT, gA and gh0 must be 16-byte aligned; every other tensor
+ *    must be aligned to its element size (4 bytes for fp32, 2 for bf16); the
+ *    workspace to 16 bytes.
+ *  - Asynchrony: work is enqueued on `stream` (NULL = the default stream) and
+ *    the call returns without waiting.  Calls are thread-safe as long as
+ *    concurrent calls use distinct workspaces and outputs.
+ *  - Errors: every argument is validated before anything is enqueued.  A
+ *    non-zero status other than SSCAN_ERR_HIP means nothing was enqueued and
+ *    nothing was written.  SSCAN_ERR_HIP means the HIP runtime refused a
+ *    launch; outputs are then undefined.  sscan_last_error() gives a message
+ *    for the last failure on the calling thread.
+ */
+#ifndef SSCAN_H_
+#define SSCAN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSCAN_VERSION 1
+
+/* Element type of x, delta, b, c, y, dy. */
+typedef enum sscan_dtype { SSCAN_F32 = 0, SSCAN_BF16 = 1 } sscan_dtype;
+
+typedef enum sscan_status {
+  SSCAN_OK = 0,
+  SSCAN_ERR_NULL = 1,        /* a required pointer is NULL */
+  SSCAN_ERR_SHAPE = 2,       /* a negative size, or a batch stride shorter than one batch row */
+  SSCAN_ERR_DTYPE = 3,       /* io is not an sscan_dtype */
+  SSCAN_ERR_UNSUPPORTED = 4, /* DS not in {1,2,4,8,16}, a bad plan, or a size beyond 32-bit grid limits */
+  SSCAN_ERR_ALIGN = 5,       /* a pointer is not aligned to its element size */
+  SSCAN_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than the size the query returned */
+  SSCAN_ERR_HIP = 7          /* the HIP runtime reported an error */
+} sscan_status;
+
+/* Problem sizes and layout. */
+typedef struct sscan_desc {
+  int64_t B;          /* batch rows, >= 0 */
+  int64_t T;          /* steps in this call, >= 0 */
+  int64_t D;          /* channels, >= 0 */
+  int64_t DS;         /* states per channel: 1, 2, 4, 8 or 16 */
+  int32_t io;         /* sscan_dtype of x, delta, b, c, y, dy */
+  int32_t reserved;   /* must be 0 */
+  int64_t x_bstride;  /* elements between batch rows of x, delta, dy; 0 means T*D */
+  int64_t bc_bstride; /* elements between batch rows of b, c; 0 means T*DS */
+  int64_t y_bstride;  /* elements between batch rows of y, gx, gdelta; 0 means T*D */
+} sscan_desc;
+
+/* Launch plan.  Pass NULL wherever a plan is accepted to let the library choose. */
+typedef struct sscan_plan {
+  int32_t lanes;       /* lanes sharing one channel's DS states: 1,2,4,8,16 and <= DS; 0 = choose */
+  int32_t chunks;      /* forward only: T-chunks of the in-kernel two-level scan; 1 = single pass, 0 = choose */
+  int32_t reserved[6]; /* must be 0 */
+} sscan_plan;
+
+/* Forward.
+ *   x, delta (B,T,D) io; A (D,DS) fp32; b, c (B,T,DS) io; h0 (B,D,DS) fp32 or NULL (zeros).
+ *   y (B,T,D) io, required.  hT (B,D,DS) fp32 or NULL (not written).
+ *   H (B,T,D,DS) fp32 or NULL (not written); H[b,t] is the state after step t.
+ *   T == 0: y is empty and hT = h0 (zeros if h0 is NULL).  B == 0 or D == 0: nothing to do.
+ *   ws/ws_bytes: workspace of at least the size sscan_fwd_workspace reports (may be NULL if that is 0). */
+int sscan_fwd(const sscan_desc* desc, const sscan_plan* plan, const void* x, const void* delta,
+              const float* A, const void* b, const void* c, const float* h0, void* y, float* hT, float* H,
+              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Bytes of workspace sscan_fwd needs for (desc, plan) -> *bytes. */
+int sscan_fwd_workspace(const sscan_desc* desc, const sscan_plan* plan, size_t* bytes);
+
+/* Backward: gradients of L = sum(dy*y) + sum(dhT*hT) for the forward with the same inputs.
+ *   dy (B,T,D) io; dhT (B,D,DS) fp32 or NULL (zeros); x, delta, A, b, c, h0 as in sscan_fwd;
+ *   H (B,T,D,DS) fp32, the states the forward materialised, required when T > 0.
+ *   gx, gdelta (B,T,D) fp32; gb, gc (B,T,DS) fp32, summed over channels;
+ *   gA (D,DS) fp32, summed over batch rows and steps; gh0 (B,D,DS) fp32 or NULL (not written).
+ *   T == 0: gA = 0 and gh0 = dhT (zeros if NULL).  B == 0: gA = 0.
+ *   Gradient sums are formed in a fixed order, so results are bitwise reproducible run to run. */
+int sscan_bwd(const sscan_desc* desc, const sscan_plan* plan, const void* dy, const float* dhT, const void* x,
+              const void* delta, const float* A, const void* b, const void* c, const float* h0, const float* H,
+              float* gx, float* gdelta, float* gb, float* gc, float* gA, float* gh0, void* ws, size_t ws_bytes,
+              hipStream_t stream);
+
+/* Bytes of workspace sscan_bwd needs for (desc, plan) -> *bytes. */
+int sscan_bwd_workspace(const sscan_desc* desc, const sscan_plan* plan, size_t* bytes);
+
+/* The plan the library picks for desc (backward != 0: for sscan_bwd) -> *plan.  Uses no GPU. */
+int sscan_plan_select(const sscan_desc* desc, int backward, sscan_plan* plan);
+
+/* Static text for a status code. */
+const char* sscan_status_str(int status);
+
+/* Message describing the last failure on the calling thread ("" if none). */
+const char* sscan_last_error(void);
+
+/* SSCAN_VERSION of the built library. */
+int sscan_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSCAN_H_ */

@@ -1,0 +1,301 @@
+"""Python entry points of libsscan, named after the C ABI (include/sscan.h).
+
+These functions only marshal arguments: they check tensor placement and
+layout, let torch allocate outputs and workspace on the caller's device, and
+call the C library on torch's current HIP stream.  Every step of the scan
+runs in libsscan's gfx950 kernels.  Calls are asynchronous like any torch op.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import SScanError, sscan_desc, sscan_plan
+
+__all__ = ["sscan_fwd", "sscan_bwd", "sscan_fwd_workspace", "sscan_bwd_workspace", "sscan_plan_select",
+           "sscan_version", "SelectiveScan", "selective_scan", "SScanError", "Plan"]
+
+_IO = {torch.float32: _lib.SSCAN_F32, torch.bfloat16: _lib.SSCAN_BF16}
+
+
+class Plan:
+    """Launch plan override: ``lanes`` per channel and forward ``chunks`` (0 = library's choice)."""
+
+    def __init__(self, lanes: int = 0, chunks: int = 0):
+        self.lanes = int(lanes)
+        self.chunks = int(chunks)
+
+    def _c(self) -> sscan_plan:
+        p = sscan_plan()
+        p.lanes = self.lanes
+        p.chunks = self.chunks
+        return p
+
+    def __repr__(self):
+        return f"Plan(lanes={self.lanes}, chunks={self.chunks})"
+
+
+def _plan_ptr(plan: Optional[Plan]):
+    if plan is None:
+        return None, None
+    c = plan._c()
+    return c, ctypes.byref(c)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _batch_stride(t: torch.Tensor, name: str) -> int:
+    """Batch stride of a (B, R, C) tensor whose trailing (R, C) block is contiguous."""
+    if t.dim() != 3:
+        raise ValueError(f"{name} must be 3-D, got shape {tuple(t.shape)}")
+    B, R, C = t.shape
+    if C > 1 and t.stride(2) != 1 or R > 1 and t.stride(1) != C:
+        raise ValueError(f"{name}: the last two dimensions must be contiguous")
+    return t.stride(0) if B > 1 else R * C
+
+
+def _rows_view(t: torch.Tensor, name: str) -> Tuple[torch.Tensor, int]:
+    try:
+        return t, _batch_stride(t, name)
+    except ValueError:
+        t = t.contiguous()
+        return t, _batch_stride(t, name)
+
+
+def _same_stride(ts, names):
+    """Bring tensors that must share one batch stride to a common layout."""
+    strides = []
+    out = []
+    for t, n in zip(ts, names):
+        t, s = _rows_view(t, n)
+        out.append(t)
+        strides.append(s)
+    if len(set(strides)) > 1:
+        out = [t.contiguous() for t in out]
+        strides = [_batch_stride(t, n) for t, n in zip(out, names)]
+    return out, strides[0]
+
+
+def _desc(B, T, D, DS, io, x_bs=0, bc_bs=0, y_bs=0) -> sscan_desc:
+    d = sscan_desc()
+    d.B, d.T, d.D, d.DS, d.io = int(B), int(T), int(D), int(DS), int(io)
+    d.x_bstride, d.bc_bstride, d.y_bstride = int(x_bs), int(bc_bs), int(y_bs)
+    return d
+
+
+def _check_device(device: torch.device, **tensors):
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _f32_contig(t: Optional[torch.Tensor], shape, name):
+    if t is None:
+        return None
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.contiguous()
+
+
+def sscan_version() -> int:
+    return int(_lib.load().sscan_version())
+
+
+def sscan_plan_select(B: int, T: int, D: int, DS: int, io: torch.dtype = torch.float32, backward: bool = False) -> Plan:
+    lib = _lib.load()
+    d = _desc(B, T, D, DS, _IO[io])
+    p = sscan_plan()
+    _lib.check(lib.sscan_plan_select(ctypes.byref(d), int(bool(backward)), ctypes.byref(p)))
+    return Plan(p.lanes, p.chunks)
+
+
+def sscan_fwd_workspace(B: int, T: int, D: int, DS: int, io: torch.dtype = torch.float32,
+                        plan: Optional[Plan] = None) -> int:
+    lib = _lib.load()
+    d = _desc(B, T, D, DS, _IO[io])
+    _, pp = _plan_ptr(plan)
+    n = ctypes.c_size_t(0)
+    _lib.check(lib.sscan_fwd_workspace(ctypes.byref(d), pp, ctypes.byref(n)))
+    return int(n.value)
+
+
+def sscan_bwd_workspace(B: int, T: int, D: int, DS: int, io: torch.dtype = torch.float32,
+                        plan: Optional[Plan] = None) -> int:
+    lib = _lib.load()
+    d = _desc(B, T, D, DS, _IO[io])
+    _, pp = _plan_ptr(plan)
+    n = ctypes.c_size_t(0)
+    _lib.check(lib.sscan_bwd_workspace(ctypes.byref(d), pp, ctypes.byref(n)))
+    return int(n.value)
+
+
+def _workspace(nbytes: int, device, given: Optional[torch.Tensor]):
+    if nbytes == 0:
+        return None, 0
+    if given is not None:
+        if given.device != device or given.numel() * given.element_size() < nbytes:
+            raise ValueError(f"workspace must be a {nbytes}-byte buffer on {device}")
+        return given, given.numel() * given.element_size()
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def sscan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, b: torch.Tensor, c: torch.Tensor,
+              h0: Optional[torch.Tensor] = None, *, y: Optional[torch.Tensor] = None,
+              hT: Optional[torch.Tensor] = None, H: Optional[torch.Tensor] = None, return_H: bool = False,
+              plan: Optional[Plan] = None, workspace: Optional[torch.Tensor] = None):
+    """Forward scan.  Returns (y, hT) or, with ``return_H`` (or ``H`` given), (y, hT, H).
+
+    x, delta: (B,T,D) fp32 or bf16 (same dtype, may be T-slices of longer tensors);
+    A: (D,DS) fp32; b, c: (B,T,DS) same dtype as x; h0: (B,D,DS) fp32 or None (zeros).
+    y (optional out): (B,T,D) of x's dtype; hT (optional out): (B,D,DS) fp32;
+    H (optional out): (B,T,D,DS) fp32 per-step states.
+    """
+    lib = _lib.load()
+    if x.dtype not in _IO:
+        raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
+    for n_, t in (("delta", delta), ("b", b), ("c", c)):
+        if t.dtype != x.dtype:
+            raise TypeError(f"{n_} must have x's dtype {x.dtype}, got {t.dtype}")
+    device = x.device
+    if device.type != "cuda":
+        raise ValueError("sscan_fwd runs on a GPU: move the tensors to a HIP device")
+    B, T, D = x.shape
+    if A.dim() != 2 or A.shape[0] != D:
+        raise ValueError(f"A must have shape (D, DS) with D={D}, got {tuple(A.shape)}")
+    DS = A.shape[1]
+    if tuple(delta.shape) != (B, T, D) or tuple(b.shape) != (B, T, DS) or tuple(c.shape) != (B, T, DS):
+        raise ValueError("shape mismatch among x (B,T,D), delta (B,T,D), b and c (B,T,DS)")
+    _check_device(device, delta=delta, A=A, b=b, c=c, h0=h0, y=y, hT=hT, H=H)
+    (x, delta), x_bs = _same_stride([x, delta], ["x", "delta"])
+    (b, c), bc_bs = _same_stride([b, c], ["b", "c"])
+    A = _f32_contig(A, (D, DS), "A")
+    h0 = _f32_contig(h0, (B, D, DS), "h0")
+    if y is None:
+        y = torch.empty((B, T, D), dtype=x.dtype, device=device)
+    elif y.dtype != x.dtype or tuple(y.shape) != (B, T, D):
+        raise ValueError("y must have x's dtype and shape")
+    y_bs = _batch_stride(y, "y")
+    if hT is None:
+        hT = torch.empty((B, D, DS), dtype=torch.float32, device=device)
+    elif not hT.is_contiguous():
+        raise ValueError("hT must be contiguous")
+    if H is None and return_H:
+        H = torch.empty((B, T, D, DS), dtype=torch.float32, device=device)
+    if H is not None and (not H.is_contiguous() or tuple(H.shape) != (B, T, D, DS) or H.dtype != torch.float32):
+        raise ValueError("H must be a contiguous (B,T,D,DS) float32 tensor")
+    d = _desc(B, T, D, DS, _IO[x.dtype], x_bs, bc_bs, y_bs)
+    pc, pp = _plan_ptr(plan)
+    nws = ctypes.c_size_t(0)
+    _lib.check(lib.sscan_fwd_workspace(ctypes.byref(d), pp, ctypes.byref(nws)))
+    ws, wsn = _workspace(int(nws.value), device, workspace)
+    with torch.cuda.device(device):
+        st = lib.sscan_fwd(ctypes.byref(d), pp, _ptr(x), _ptr(delta), _ptr(A), _ptr(b), _ptr(c), _ptr(h0), _ptr(y),
+                           _ptr(hT), _ptr(H), _ptr(ws), ctypes.c_size_t(wsn), _stream(device))
+    _lib.check(st)
+    return (y, hT, H) if (return_H or H is not None) else (y, hT)
+
+
+def sscan_bwd(dy: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, b: torch.Tensor,
+              c: torch.Tensor, h0: Optional[torch.Tensor], H: torch.Tensor, dhT: Optional[torch.Tensor] = None, *,
+              need_gh0: bool = True, plan: Optional[Plan] = None, workspace: Optional[torch.Tensor] = None,
+              out: Optional[Tuple[torch.Tensor, ...]] = None):
+    """Backward scan.  Returns (gx, gdelta, gb, gc, gA, gh0), all float32 (gh0 None if not needed).
+
+    Gradients of sum(dy*y) + sum(dhT*hT); gb, gc are summed over channels and gA over
+    batch rows and steps.  H is the (B,T,D,DS) state tensor the forward materialised.
+    ``out`` may supply the six contiguous float32 output tensors (gh0 may be None).
+    """
+    lib = _lib.load()
+    if x.dtype not in _IO:
+        raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
+    for n_, t in (("dy", dy), ("delta", delta), ("b", b), ("c", c)):
+        if t.dtype != x.dtype:
+            raise TypeError(f"{n_} must have x's dtype {x.dtype}, got {t.dtype}")
+    device = x.device
+    if device.type != "cuda":
+        raise ValueError("sscan_bwd runs on a GPU: move the tensors to a HIP device")
+    B, T, D = x.shape
+    DS = A.shape[1]
+    if tuple(dy.shape) != (B, T, D) or tuple(delta.shape) != (B, T, D):
+        raise ValueError("dy and delta must have x's shape")
+    if tuple(b.shape) != (B, T, DS) or tuple(c.shape) != (B, T, DS):
+        raise ValueError("b and c must have shape (B,T,DS)")
+    _check_device(device, dy=dy, delta=delta, A=A, b=b, c=c, h0=h0, H=H, dhT=dhT)
+    (x, delta, dy), x_bs = _same_stride([x, delta, dy], ["x", "delta", "dy"])
+    (b, c), bc_bs = _same_stride([b, c], ["b", "c"])
+    A = _f32_contig(A, (D, DS), "A")
+    h0 = _f32_contig(h0, (B, D, DS), "h0")
+    dhT = _f32_contig(dhT, (B, D, DS), "dhT")
+    H = _f32_contig(H, (B, T, D, DS), "H")
+    f32 = dict(dtype=torch.float32, device=device)
+    if out is not None:
+        gx, gdelta, gb, gc, gA, gh0 = out
+        shapes = [(B, T, D), (B, T, D), (B, T, DS), (B, T, DS), (D, DS), (B, D, DS)]
+        for name, t, shp in zip(["gx", "gdelta", "gb", "gc", "gA", "gh0"], out, shapes):
+            if t is None and name == "gh0":
+                continue
+            if t is None or t.dtype != torch.float32 or tuple(t.shape) != shp or not t.is_contiguous() \
+                    or t.device != device:
+                raise ValueError(f"out {name} must be a contiguous float32 tensor of shape {shp} on {device}")
+    else:
+        gx = torch.empty((B, T, D), **f32)
+        gdelta = torch.empty((B, T, D), **f32)
+        gb = torch.empty((B, T, DS), **f32)
+        gc = torch.empty((B, T, DS), **f32)
+        gA = torch.empty((D, DS), **f32)
+        gh0 = torch.empty((B, D, DS), **f32) if need_gh0 else None
+    d = _desc(B, T, D, DS, _IO[x.dtype], x_bs, bc_bs, 0)
+    pc, pp = _plan_ptr(plan)
+    nws = ctypes.c_size_t(0)
+    _lib.check(lib.sscan_bwd_workspace(ctypes.byref(d), pp, ctypes.byref(nws)))
+    ws, wsn = _workspace(int(nws.value), device, workspace)
+    with torch.cuda.device(device):
+        st = lib.sscan_bwd(ctypes.byref(d), pp, _ptr(dy), _ptr(dhT), _ptr(x), _ptr(delta), _ptr(A), _ptr(b), _ptr(c),
+                           _ptr(h0), _ptr(H), _ptr(gx), _ptr(gdelta), _ptr(gb), _ptr(gc), _ptr(gA), _ptr(gh0),
+                           _ptr(ws), ctypes.c_size_t(wsn), _stream(device))
+    _lib.check(st)
+    return gx, gdelta, gb, gc, gA, gh0
+
+
+class SelectiveScan(torch.autograd.Function):
+    """Differentiable scan: (x, delta, A, b, c, h0) -> (y, hT), with gradients for hT too.
+
+    The forward keeps the per-step states H for a single reverse sweep in the backward.
+    """
+
+    @staticmethod
+    def forward(ctx, x, delta, A, b, c, h0=None):
+        y, hT, H = sscan_fwd(x, delta, A, b, c, h0, return_H=True)
+        ctx.save_for_backward(x, delta, A, b, c, h0, H)
+        ctx.has_h0 = h0 is not None
+        return y, hT
+
+    @staticmethod
+    def backward(ctx, dy, dhT):
+        x, delta, A, b, c, h0, H = ctx.saved_tensors
+        if dy is None:
+            dy = torch.zeros_like(x)
+        dy = dy.to(x.dtype)
+        gx, gdelta, gb, gc, gA, gh0 = sscan_bwd(dy, x, delta, A, b, c, h0, H,
+                                                None if dhT is None else dhT.float().contiguous(),
+                                                need_gh0=ctx.has_h0)
+        return (gx.to(x.dtype), gdelta.to(delta.dtype), gA, gb.to(b.dtype), gc.to(c.dtype),
+                gh0 if ctx.has_h0 else None)
+
+
+def selective_scan(x, delta, A, b, c, h0=None):
+    """Autograd-aware forward: returns (y, hT)."""
+    return SelectiveScan.apply(x, delta, A, b, c, h0)

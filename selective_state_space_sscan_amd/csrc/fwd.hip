@@ -1,0 +1,296 @@
+// Forward selective scan kernels for gfx950.
+//
+// Recurrence ("pssa-100m/pssa_kernels.py" page, module docstring and scan_fwd):
+//   h_t = exp(delta_t * A) * h_{t-1} + delta_t * b_t * x_t,   y_t = <h_t, c_t>.
+//
+// Work decomposition.  A workgroup of 256 threads owns one batch row and a tile of
+// CPW = 256/L channels; the L consecutive lanes of a channel each hold K = DS/L of its
+// fp32 states in VGPRs for the whole sequence.  Steps are processed in tiles of TB:
+// the workgroup loads the x / delta tile and the b / c rows of the tile with coalesced
+// loads (prefetched one tile ahead into registers), converts them to fp32 once and
+// parks (delta, delta*x) and b, c in LDS, where every lane of a channel reads them as a
+// broadcast.  Per (step, state) a lane does one v_exp_f32 and four fp32 ops; the
+// readout <h, c> is reduced over the L lanes with DPP and y is written back through
+// LDS so the store is coalesced.  Steps past the end of the sequence are padded with
+// delta = 0 and delta*x = 0, which leave the state bit-for-bit unchanged (exp2(0) = 1).
+//
+// Two-level scan along T (used when B*D*L lanes cannot fill the GPU).  The local pass
+// runs chunks 0..C-2 from a zero state and records, per (b, d, n), the chunk's decay
+// product exp(A * sum(delta)) (the product of its per-step decays) and its end state.
+// The carry kernel composes these pairs left to right from h0, h_in[k+1] =
+// P_k * h_in[k] + hloc_k, and the full pass reruns every chunk from its true start
+// state.  The decomposition is the associativity of the affine maps h -> a*h + u.
+#include "device_common.h"
+
+namespace sscan {
+namespace {
+
+template <int K>
+__device__ __forceinline__ void load_state(const float* __restrict__ p, float (&v)[K]) {
+  if constexpr (K % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < K / 4; ++q) {
+      const float4 t = reinterpret_cast<const float4*>(p)[q];
+      v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
+    }
+  } else if constexpr (K == 2) {
+    const float2 t = *reinterpret_cast<const float2*>(p);
+    v[0] = t.x; v[1] = t.y;
+  } else {
+    v[0] = p[0];
+  }
+}
+
+template <int K>
+__device__ __forceinline__ void store_state(float* __restrict__ p, const float (&v)[K]) {
+  if constexpr (K % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < K / 4; ++q)
+      reinterpret_cast<float4*>(p)[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+  } else if constexpr (K == 2) {
+    *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+  } else {
+    p[0] = v[0];
+  }
+}
+
+template <typename IO, int DS, int L, bool LOCAL>
+__global__ __launch_bounds__(kThreads) void fwd_kernel(const FwdParams p) {
+  constexpr int K = DS / L;
+  constexpr int CPW = kThreads / L;
+  constexpr int TB = fwd_tile_steps(L);
+  constexpr int TILE = TB * CPW;
+  constexpr int PER = TILE / kThreads;
+  constexpr int BC = TB * DS;
+  constexpr int PER_BC = (BC + kThreads - 1) / kThreads;
+  static_assert(TILE % kThreads == 0, "tile must split evenly over the workgroup");
+
+  __shared__ float2 s_dw[TILE];            // (delta, delta*x) at [step*CPW + channel]
+  __shared__ float s_b[BC];                // b at [step*DS + n]
+  __shared__ float s_c[BC];
+  __shared__ float s_y[LOCAL ? 1 : TILE];  // y at [step*CPW + channel]
+
+  const int tid = threadIdx.x;
+  const int ch = tid / L;
+  const int j = tid % L;
+  const int d0 = blockIdx.x * CPW;
+  const int bb = blockIdx.y;
+  const int chunk = blockIdx.z;
+  const int D = p.D;
+  const int t_begin = chunk * p.chunk_len;
+  const int t_end = min(p.T, t_begin + p.chunk_len);
+  const int d = d0 + ch;
+  const bool dvalid = d < D;
+
+  const IO* __restrict__ xg = static_cast<const IO*>(p.x) + (int64_t)bb * p.x_bs;
+  const IO* __restrict__ dg = static_cast<const IO*>(p.delta) + (int64_t)bb * p.x_bs;
+  const IO* __restrict__ bg = static_cast<const IO*>(p.b) + (int64_t)bb * p.bc_bs;
+  const IO* __restrict__ cg = static_cast<const IO*>(p.c) + (int64_t)bb * p.bc_bs;
+
+  const int64_t nstate = (int64_t)p.B * D * DS;
+  const int64_t soff = ((int64_t)bb * D + d) * DS + j * K;  // this lane's states in (B,D,DS)
+
+  float A2[K], h[K];
+  if (dvalid) {
+    load_state<K>(p.A + (int64_t)d * DS + j * K, A2);
+#pragma unroll
+    for (int i = 0; i < K; ++i) A2[i] *= kLog2e;
+    if (LOCAL || (chunk == 0 && p.h0 == nullptr)) {
+#pragma unroll
+      for (int i = 0; i < K; ++i) h[i] = 0.f;
+    } else if (chunk == 0) {
+      load_state<K>(p.h0 + soff, h);
+    } else {
+      load_state<K>(p.hin + (int64_t)(chunk - 1) * nstate + soff, h);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < K; ++i) { A2[i] = 0.f; h[i] = 0.f; }
+  }
+  double dsum = 0.0;  // local pass: sum of delta over the chunk
+
+  IO rx[PER], rd[PER], rb[PER_BC], rc[PER_BC];
+  auto load_tile = [&](int ts) {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int idx = tid + e * kThreads;
+      const int t = ts + idx / CPW;
+      const int dd = d0 + idx % CPW;
+      if (t < t_end && dd < D) {
+        rx[e] = xg[(int64_t)t * D + dd];
+        rd[e] = dg[(int64_t)t * D + dd];
+      } else {
+        rx[e] = IO{};
+        rd[e] = IO{};
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < PER_BC; ++e) {
+      const int idx = tid + e * kThreads;
+      const int t = ts + idx / DS;
+      if (idx < BC && t < t_end) {
+        rb[e] = bg[(int64_t)t * DS + idx % DS];
+        rc[e] = cg[(int64_t)t * DS + idx % DS];
+      } else {
+        rb[e] = IO{};
+        rc[e] = IO{};
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const float dl = to_f32(rd[e]);
+      s_dw[tid + e * kThreads] = make_float2(dl, dl * to_f32(rx[e]));
+    }
+#pragma unroll
+    for (int e = 0; e < PER_BC; ++e) {
+      const int idx = tid + e * kThreads;
+      if (idx < BC) {
+        s_b[idx] = to_f32(rb[e]);
+        s_c[idx] = to_f32(rc[e]);
+      }
+    }
+  };
+
+  const int nsteps_total = t_end - t_begin;
+  const int ntiles = nsteps_total > 0 ? (nsteps_total + TB - 1) / TB : 0;
+  if (ntiles > 0) load_tile(t_begin);
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int ts = t_begin + it * TB;
+    __syncthreads();  // the previous tile's LDS reads are complete
+    store_tile();
+    __syncthreads();
+    if (it + 1 < ntiles) load_tile(ts + TB);
+
+#pragma unroll 4
+    for (int tt = 0; tt < TB; ++tt) {
+      const float2 dw = s_dw[tt * CPW + ch];
+      float bv[K];
+      load_state<K>(&s_b[tt * DS + j * K], bv);
+      if constexpr (LOCAL) {
+        dsum += dw.x;
+#pragma unroll
+        for (int i = 0; i < K; ++i) {
+          const float a = exp2_hw(dw.x * A2[i]);
+          h[i] = fmaf(a, h[i], dw.y * bv[i]);
+        }
+      } else {
+        float cv[K];
+        load_state<K>(&s_c[tt * DS + j * K], cv);
+        float yp = 0.f;
+#pragma unroll
+        for (int i = 0; i < K; ++i) {
+          const float a = exp2_hw(dw.x * A2[i]);
+          h[i] = fmaf(a, h[i], dw.y * bv[i]);
+          yp = fmaf(h[i], cv[i], yp);
+        }
+        yp = group_sum<L>(yp);
+        if (j == 0) s_y[tt * CPW + ch] = yp;
+        if (p.H != nullptr && dvalid && ts + tt < t_end)
+          store_state<K>(p.H + (((int64_t)bb * p.T + ts + tt) * D + d) * DS + j * K, h);
+      }
+    }
+
+    if constexpr (!LOCAL) {
+      __syncthreads();
+      IO* __restrict__ yg = static_cast<IO*>(p.y) + (int64_t)bb * p.y_bs;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const int idx = tid + e * kThreads;
+        const int t = ts + idx / CPW;
+        const int dd = d0 + idx % CPW;
+        if (t < t_end && dd < D) yg[(int64_t)t * D + dd] = from_f32<IO>(s_y[idx]);
+      }
+    }
+  }
+
+  if (!dvalid) return;
+  if constexpr (LOCAL) {
+    float2* pr = p.pairs + (int64_t)chunk * nstate + soff;
+#pragma unroll
+    for (int i = 0; i < K; ++i) pr[i] = make_float2(exp2_hw(static_cast<float>(static_cast<double>(A2[i]) * dsum)), h[i]);
+  } else {
+    if (p.hT != nullptr && chunk == p.chunks - 1) store_state<K>(p.hT + soff, h);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void carry_kernel(const CarryParams p) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= p.n) return;
+  float h = p.h0 != nullptr ? p.h0[i] : 0.f;
+  for (int k = 0; k < p.chunks - 1; ++k) {
+    const float2 pr = p.pairs[(int64_t)k * p.n + i];
+    h = fmaf(pr.x, h, pr.y);
+    p.hin[(int64_t)k * p.n + i] = h;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void fill_kernel(float* __restrict__ dst, const float* __restrict__ src, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i < n) dst[i] = src != nullptr ? src[i] : 0.f;
+}
+
+template <typename IO, int DS, int L>
+hipError_t launch_fwd_t(bool local_pass, const FwdParams& p, dim3 grid, hipStream_t s) {
+  if (local_pass)
+    hipLaunchKernelGGL((fwd_kernel<IO, DS, L, true>), grid, dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((fwd_kernel<IO, DS, L, false>), grid, dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+template <typename IO, int DS>
+hipError_t launch_fwd_ds(int lanes, bool local_pass, const FwdParams& p, dim3 grid, hipStream_t s) {
+  switch (lanes) {
+    case 1: return launch_fwd_t<IO, DS, 1>(local_pass, p, grid, s);
+    case 2: if constexpr (DS >= 2) return launch_fwd_t<IO, DS, 2>(local_pass, p, grid, s); break;
+    case 4: if constexpr (DS >= 4) return launch_fwd_t<IO, DS, 4>(local_pass, p, grid, s); break;
+    case 8: if constexpr (DS >= 8) return launch_fwd_t<IO, DS, 8>(local_pass, p, grid, s); break;
+    case 16: if constexpr (DS >= 16) return launch_fwd_t<IO, DS, 16>(local_pass, p, grid, s); break;
+    default: break;
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename IO>
+hipError_t launch_fwd_io(int DS, int lanes, bool local_pass, const FwdParams& p, dim3 grid, hipStream_t s) {
+  switch (DS) {
+    case 1: return launch_fwd_ds<IO, 1>(lanes, local_pass, p, grid, s);
+    case 2: return launch_fwd_ds<IO, 2>(lanes, local_pass, p, grid, s);
+    case 4: return launch_fwd_ds<IO, 4>(lanes, local_pass, p, grid, s);
+    case 8: return launch_fwd_ds<IO, 8>(lanes, local_pass, p, grid, s);
+    case 16: return launch_fwd_ds<IO, 16>(lanes, local_pass, p, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fwd(int io, int DS, int lanes, bool local_pass, const FwdParams& p, dim3 grid, hipStream_t s) {
+  if (io == 0) return launch_fwd_io<float>(DS, lanes, local_pass, p, grid, s);
+  return launch_fwd_io<bf16_t>(DS, lanes, local_pass, p, grid, s);
+}
+
+hipError_t launch_carry(const CarryParams& p, hipStream_t s) {
+  const int64_t blocks = (p.n + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(carry_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill(float* dst, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, dst, nullptr, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, dst, src, n);
+  return hipGetLastError();
+}
+
+}  // namespace sscan

@@ -1,0 +1,334 @@
+// libsscan host side: argument validation, plan selection, workspace layout and
+// kernel launches.  Nothing here allocates device memory or synchronises.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <limits>
+
+#include "sscan.h"
+#include "sscan_internal.h"
+
+namespace {
+
+using sscan::kThreads;
+
+thread_local char g_last_error[256] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return SSCAN_OK;
+}
+
+// MI355X: 256 CUs x 4 SIMDs; one wave64 per SIMD is 65536 lanes.
+constexpr int64_t kLanesOneWavePerSimd = 65536;
+
+bool valid_ds(int64_t ds) { return ds == 1 || ds == 2 || ds == 4 || ds == 8 || ds == 16; }
+bool pow2_upto16(int64_t v) { return v == 1 || v == 2 || v == 4 || v == 8 || v == 16; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct Resolved {
+  int64_t B, T, D, DS;
+  int io;
+  int64_t x_bs, bc_bs, y_bs;
+  size_t io_size;
+};
+
+int resolve_desc(const sscan_desc* desc, Resolved* r) {
+  if (desc == nullptr) return fail(SSCAN_ERR_NULL, "desc is NULL");
+  if (desc->B < 0 || desc->T < 0 || desc->D < 0)
+    return fail(SSCAN_ERR_SHAPE, "negative size (B=%lld T=%lld D=%lld)", (long long)desc->B, (long long)desc->T,
+                (long long)desc->D);
+  if (!valid_ds(desc->DS)) return fail(SSCAN_ERR_UNSUPPORTED, "DS=%lld is not one of 1,2,4,8,16", (long long)desc->DS);
+  if (desc->io != SSCAN_F32 && desc->io != SSCAN_BF16) return fail(SSCAN_ERR_DTYPE, "io dtype %d is unknown", desc->io);
+  if (desc->reserved != 0) return fail(SSCAN_ERR_UNSUPPORTED, "desc.reserved must be 0");
+  const int64_t i32max = std::numeric_limits<int32_t>::max();
+  if (desc->T > i32max || desc->D > i32max || desc->B > 65535)
+    return fail(SSCAN_ERR_UNSUPPORTED, "sizes beyond grid limits (B <= 65535, T and D < 2^31)");
+  r->B = desc->B;
+  r->T = desc->T;
+  r->D = desc->D;
+  r->DS = desc->DS;
+  r->io = desc->io;
+  r->io_size = desc->io == SSCAN_F32 ? 4 : 2;
+  const int64_t row = desc->T * desc->D;
+  const int64_t bcrow = desc->T * desc->DS;
+  r->x_bs = desc->x_bstride == 0 ? row : desc->x_bstride;
+  r->bc_bs = desc->bc_bstride == 0 ? bcrow : desc->bc_bstride;
+  r->y_bs = desc->y_bstride == 0 ? row : desc->y_bstride;
+  if (r->x_bs < row) return fail(SSCAN_ERR_SHAPE, "x_bstride %lld < T*D = %lld", (long long)r->x_bs, (long long)row);
+  if (r->y_bs < row) return fail(SSCAN_ERR_SHAPE, "y_bstride %lld < T*D = %lld", (long long)r->y_bs, (long long)row);
+  if (r->bc_bs < bcrow)
+    return fail(SSCAN_ERR_SHAPE, "bc_bstride %lld < T*DS = %lld", (long long)r->bc_bs, (long long)bcrow);
+  return SSCAN_OK;
+}
+
+// Smallest lane count L (power of two, <= min(DS,16)) with B*D*L >= target lanes.
+int pick_lanes(const Resolved& r, int64_t target) {
+  const int64_t maxl = r.DS < 16 ? r.DS : 16;
+  int64_t l = 1;
+  while (l < maxl && r.B * r.D * l < target) l *= 2;
+  return (int)l;
+}
+
+int resolve_plan(const Resolved& r, const sscan_plan* plan, bool backward, int* lanes, int* chunks) {
+  if (plan != nullptr) {
+    for (int i = 0; i < 6; ++i)
+      if (plan->reserved[i] != 0) return fail(SSCAN_ERR_UNSUPPORTED, "plan.reserved must be 0");
+    if (plan->lanes != 0 && (!pow2_upto16(plan->lanes) || plan->lanes > r.DS))
+      return fail(SSCAN_ERR_UNSUPPORTED, "plan.lanes=%d must be a power of two <= min(DS,16)", plan->lanes);
+    if (plan->chunks < 0 || plan->chunks > 65535)
+      return fail(SSCAN_ERR_UNSUPPORTED, "plan.chunks=%d out of range", plan->chunks);
+    if (backward && plan->chunks > 1) return fail(SSCAN_ERR_UNSUPPORTED, "the backward runs a single pass");
+  }
+  int l = (plan != nullptr && plan->lanes != 0) ? plan->lanes : pick_lanes(r, backward ? 98304 : kLanesOneWavePerSimd);
+  int c = 1;
+  if (!backward) {
+    if (plan != nullptr && plan->chunks != 0) {
+      c = plan->chunks;
+    } else {
+      // Split the sequence when the single pass would leave at least half of the
+      // SIMDs idle; every chunk keeps at least 256 steps.
+      const int64_t lanes_total = r.B * r.D * l;
+      if (lanes_total > 0 && 2 * lanes_total <= kLanesOneWavePerSimd) {
+        int64_t want = ceil_div(kLanesOneWavePerSimd, lanes_total);
+        int64_t cap = r.T / 256;
+        if (want > cap) want = cap;
+        if (want > 16) want = 16;
+        if (want > 1) c = (int)want;
+      }
+    }
+    if (r.T > 0 && c > r.T) c = (int)r.T;
+    if (c < 1) c = 1;
+  }
+  *lanes = l;
+  *chunks = c;
+  return SSCAN_OK;
+}
+
+struct FwdLayout {
+  size_t pairs_off, hin_off, total;
+};
+
+FwdLayout fwd_layout(const Resolved& r, int chunks) {
+  FwdLayout L{0, 0, 0};
+  if (chunks <= 1) return L;
+  const size_t nstate = (size_t)(r.B * r.D * r.DS);
+  L.pairs_off = 0;
+  L.hin_off = align_up(L.pairs_off + (size_t)(chunks - 1) * nstate * sizeof(float2), 256);
+  L.total = align_up(L.hin_off + (size_t)(chunks - 1) * nstate * sizeof(float), 256);
+  return L;
+}
+
+struct BwdLayout {
+  size_t bc_off, a_off, total;
+  int64_t ntiles_d;
+};
+
+BwdLayout bwd_layout(const Resolved& r, int lanes) {
+  BwdLayout L{0, 0, 0, 0};
+  const int64_t cpw = kThreads / lanes;
+  L.ntiles_d = ceil_div(r.D, cpw);
+  L.bc_off = 0;
+  L.a_off = align_up((size_t)(L.ntiles_d * r.B * r.T * r.DS) * sizeof(float2), 256);
+  L.total = align_up(L.a_off + (size_t)(r.B * r.D * r.DS) * sizeof(float), 256);
+  return L;
+}
+
+bool misaligned(const void* p, size_t a) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) % a) != 0; }
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(SSCAN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int sscan_version(void) { return SSCAN_VERSION; }
+
+const char* sscan_last_error(void) { return g_last_error; }
+
+const char* sscan_status_str(int status) {
+  switch (status) {
+    case SSCAN_OK: return "ok";
+    case SSCAN_ERR_NULL: return "required pointer is NULL";
+    case SSCAN_ERR_SHAPE: return "invalid shape or stride";
+    case SSCAN_ERR_DTYPE: return "invalid dtype";
+    case SSCAN_ERR_UNSUPPORTED: return "unsupported size or plan";
+    case SSCAN_ERR_ALIGN: return "misaligned pointer";
+    case SSCAN_ERR_WORKSPACE: return "workspace missing or too small";
+    case SSCAN_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int sscan_plan_select(const sscan_desc* desc, int backward, sscan_plan* plan) {
+  Resolved r;
+  int st = resolve_desc(desc, &r);
+  if (st != SSCAN_OK) return st;
+  if (plan == nullptr) return fail(SSCAN_ERR_NULL, "plan is NULL");
+  int lanes, chunks;
+  st = resolve_plan(r, nullptr, backward != 0, &lanes, &chunks);
+  if (st != SSCAN_OK) return st;
+  memset(plan, 0, sizeof(*plan));
+  plan->lanes = lanes;
+  plan->chunks = chunks;
+  return ok();
+}
+
+int sscan_fwd_workspace(const sscan_desc* desc, const sscan_plan* plan, size_t* bytes) {
+  Resolved r;
+  int st = resolve_desc(desc, &r);
+  if (st != SSCAN_OK) return st;
+  if (bytes == nullptr) return fail(SSCAN_ERR_NULL, "bytes is NULL");
+  int lanes, chunks;
+  st = resolve_plan(r, plan, false, &lanes, &chunks);
+  if (st != SSCAN_OK) return st;
+  *bytes = (r.B == 0 || r.D == 0 || r.T == 0) ? 0 : fwd_layout(r, chunks).total;
+  return ok();
+}
+
+int sscan_bwd_workspace(const sscan_desc* desc, const sscan_plan* plan, size_t* bytes) {
+  Resolved r;
+  int st = resolve_desc(desc, &r);
+  if (st != SSCAN_OK) return st;
+  if (bytes == nullptr) return fail(SSCAN_ERR_NULL, "bytes is NULL");
+  int lanes, chunks;
+  st = resolve_plan(r, plan, true, &lanes, &chunks);
+  if (st != SSCAN_OK) return st;
+  *bytes = (r.B == 0 || r.D == 0 || r.T == 0) ? 0 : bwd_layout(r, lanes).total;
+  return ok();
+}
+
+int sscan_fwd(const sscan_desc* desc, const sscan_plan* plan, const void* x, const void* delta, const float* A,
+              const void* b, const void* c, const float* h0, void* y, float* hT, float* H, void* ws, size_t ws_bytes,
+              hipStream_t stream) {
+  Resolved r;
+  int st = resolve_desc(desc, &r);
+  if (st != SSCAN_OK) return st;
+  int lanes, chunks;
+  st = resolve_plan(r, plan, false, &lanes, &chunks);
+  if (st != SSCAN_OK) return st;
+  if (r.B == 0 || r.D == 0) return ok();
+  const bool steps = r.T > 0;
+  if (steps && (x == nullptr || delta == nullptr || A == nullptr || b == nullptr || c == nullptr || y == nullptr))
+    return fail(SSCAN_ERR_NULL, "x, delta, A, b, c and y are required when T > 0");
+  const size_t es = r.io_size;
+  if (misaligned(x, es) || misaligned(delta, es) || misaligned(b, es) || misaligned(c, es) || misaligned(y, es))
+    return fail(SSCAN_ERR_ALIGN, "io tensors must be aligned to their element size");
+  if (misaligned(A, 16) || misaligned(h0, 16) || misaligned(hT, 16) || misaligned(H, 16))
+    return fail(SSCAN_ERR_ALIGN, "A, h0, hT and H must be 16-byte aligned");
+  if (!steps) {
+    if (hT == nullptr) return ok();
+    const hipError_t e = sscan::launch_copy_or_zero(hT, h0, r.B * r.D * r.DS, stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "hT <- h0");
+  }
+  const FwdLayout lay = fwd_layout(r, chunks);
+  if (lay.total > 0) {
+    if (ws == nullptr || ws_bytes < lay.total)
+      return fail(SSCAN_ERR_WORKSPACE, "forward needs %zu workspace bytes, got %zu", lay.total, ws_bytes);
+    if (misaligned(ws, 16)) return fail(SSCAN_ERR_ALIGN, "workspace must be 16-byte aligned");
+  }
+
+  sscan::FwdParams p{};
+  p.x = x; p.delta = delta; p.A = A; p.b = b; p.c = c; p.h0 = h0; p.y = y; p.hT = hT; p.H = H;
+  p.x_bs = r.x_bs; p.bc_bs = r.bc_bs; p.y_bs = r.y_bs;
+  p.B = (int32_t)r.B; p.T = (int32_t)r.T; p.D = (int32_t)r.D;
+  p.chunks = chunks;
+  p.chunk_len = (int32_t)ceil_div(r.T, chunks);
+  const int64_t cpw = kThreads / lanes;
+  const unsigned ntiles_d = (unsigned)ceil_div(r.D, cpw);
+  hipError_t e;
+  if (chunks > 1) {
+    char* wsb = static_cast<char*>(ws);
+    p.pairs = reinterpret_cast<float2*>(wsb + lay.pairs_off);
+    p.hin = reinterpret_cast<const float*>(wsb + lay.hin_off);
+    e = sscan::launch_fwd(r.io, (int)r.DS, lanes, true, p, dim3(ntiles_d, (unsigned)r.B, (unsigned)(chunks - 1)), stream);
+    if (e != hipSuccess) return hip_fail(e, "forward local pass");
+    sscan::CarryParams cp{};
+    cp.pairs = p.pairs;
+    cp.h0 = h0;
+    cp.hin = reinterpret_cast<float*>(wsb + lay.hin_off);
+    cp.n = r.B * r.D * r.DS;
+    cp.chunks = chunks;
+    e = sscan::launch_carry(cp, stream);
+    if (e != hipSuccess) return hip_fail(e, "chunk carry");
+  }
+  e = sscan::launch_fwd(r.io, (int)r.DS, lanes, false, p, dim3(ntiles_d, (unsigned)r.B, (unsigned)chunks), stream);
+  if (e != hipSuccess) return hip_fail(e, "forward pass");
+  return ok();
+}
+
+int sscan_bwd(const sscan_desc* desc, const sscan_plan* plan, const void* dy, const float* dhT, const void* x,
+              const void* delta, const float* A, const void* b, const void* c, const float* h0, const float* H,
+              float* gx, float* gdelta, float* gb, float* gc, float* gA, float* gh0, void* ws, size_t ws_bytes,
+              hipStream_t stream) {
+  Resolved r;
+  int st = resolve_desc(desc, &r);
+  if (st != SSCAN_OK) return st;
+  int lanes, chunks;
+  st = resolve_plan(r, plan, true, &lanes, &chunks);
+  if (st != SSCAN_OK) return st;
+  const bool steps = r.T > 0 && r.B > 0;
+  if (r.D > 0 && gA == nullptr) return fail(SSCAN_ERR_NULL, "gA is required");
+  if (steps && r.D > 0 &&
+      (dy == nullptr || x == nullptr || delta == nullptr || A == nullptr || b == nullptr || c == nullptr ||
+       H == nullptr || gx == nullptr || gdelta == nullptr || gb == nullptr || gc == nullptr))
+    return fail(SSCAN_ERR_NULL, "dy, x, delta, A, b, c, H, gx, gdelta, gb and gc are required when T > 0");
+  if (steps && r.D == 0 && (gb == nullptr || gc == nullptr))
+    return fail(SSCAN_ERR_NULL, "gb and gc are required when T > 0");
+  const size_t es = r.io_size;
+  if (misaligned(dy, es) || misaligned(x, es) || misaligned(delta, es) || misaligned(b, es) || misaligned(c, es))
+    return fail(SSCAN_ERR_ALIGN, "io tensors must be aligned to their element size");
+  if (misaligned(gx, 4) || misaligned(gdelta, 4) || misaligned(gb, 4) || misaligned(gc, 4))
+    return fail(SSCAN_ERR_ALIGN, "gradient tensors must be 4-byte aligned");
+  if (misaligned(A, 16) || misaligned(h0, 16) || misaligned(H, 16) || misaligned(dhT, 16) || misaligned(gA, 16) ||
+      misaligned(gh0, 16))
+    return fail(SSCAN_ERR_ALIGN, "A, h0, H, dhT, gA and gh0 must be 16-byte aligned");
+
+  if (!steps || r.D == 0) {
+    // No step to sweep: gA = 0, gh0 = dhT (zeros if absent); gb, gc over D = 0 channels are 0.
+    hipError_t e = sscan::launch_fill(gA, r.D * r.DS, stream);
+    if (e == hipSuccess && gh0 != nullptr) e = sscan::launch_copy_or_zero(gh0, dhT, r.B * r.D * r.DS, stream);
+    if (e == hipSuccess && steps && r.D == 0) {
+      e = sscan::launch_fill(gb, r.B * r.T * r.DS, stream);
+      if (e == hipSuccess) e = sscan::launch_fill(gc, r.B * r.T * r.DS, stream);
+    }
+    return e == hipSuccess ? ok() : hip_fail(e, "backward without steps");
+  }
+
+  const BwdLayout lay = bwd_layout(r, lanes);
+  if (ws == nullptr || ws_bytes < lay.total)
+    return fail(SSCAN_ERR_WORKSPACE, "backward needs %zu workspace bytes, got %zu", lay.total, ws_bytes);
+  if (misaligned(ws, 16)) return fail(SSCAN_ERR_ALIGN, "workspace must be 16-byte aligned");
+
+  char* wsb = static_cast<char*>(ws);
+  sscan::BwdParams p{};
+  p.dy = dy; p.dhT = dhT; p.x = x; p.delta = delta; p.A = A; p.b = b; p.c = c; p.h0 = h0; p.H = H;
+  p.gx = gx; p.gdelta = gdelta; p.gh0 = gh0;
+  p.part_bc = reinterpret_cast<float2*>(wsb + lay.bc_off);
+  p.part_A = reinterpret_cast<float*>(wsb + lay.a_off);
+  p.x_bs = r.x_bs; p.bc_bs = r.bc_bs; p.y_bs = r.y_bs;
+  p.B = (int32_t)r.B; p.T = (int32_t)r.T; p.D = (int32_t)r.D;
+  p.ntiles_d = (int32_t)lay.ntiles_d;
+  hipError_t e = sscan::launch_bwd(r.io, (int)r.DS, lanes, p, dim3((unsigned)lay.ntiles_d, (unsigned)r.B, 1), stream);
+  if (e != hipSuccess) return hip_fail(e, "backward sweep");
+  sscan::ReduceParams q{};
+  q.part_bc = p.part_bc; q.part_A = p.part_A; q.gb = gb; q.gc = gc; q.gA = gA;
+  q.B = p.B; q.T = p.T; q.D = p.D; q.DS = (int32_t)r.DS; q.ntiles_d = p.ntiles_d;
+  e = sscan::launch_bwd_reduce(q, stream);
+  if (e != hipSuccess) return hip_fail(e, "backward reduce");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+// Internal definitions shared by the host side and the gfx950 kernels of libsscan.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sscan {
+
+constexpr int kThreads = 256;  // every kernel runs 256-thread workgroups (4 wave64)
+
+// Storage type for bf16 I/O: the raw 16 bits.
+struct bf16_t {
+  uint16_t bits;
+};
+
+// Steps staged per tile.  The forward stages (delta, delta*x) per (step, channel),
+// 4096 of them per tile, at most 64 steps; the backward stages (delta, x, dy, delta*x),
+// 1024 per tile, at most 32 steps.  Both keep a workgroup's LDS under 64 KiB.
+__host__ __device__ constexpr int fwd_tile_steps(int lanes) {
+  return (4096 / (kThreads / lanes)) < 64 ? (4096 / (kThreads / lanes)) : 64;
+}
+__host__ __device__ constexpr int bwd_tile_steps(int lanes) {
+  return (1024 / (kThreads / lanes)) < 32 ? (1024 / (kThreads / lanes)) : 32;
+}
+
+struct FwdParams {
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* b;
+  const void* c;
+  const float* h0;     // may be null
+  void* y;             // may be null only in the local pass
+  float* hT;           // may be null
+  float* H;            // may be null
+  float2* pairs;       // two-level scan: (decay product, local end state) per chunk, (C-1,B,D,DS)
+  const float* hin;    // two-level scan: start state of chunks 1..C-1, (C-1,B,D,DS)
+  int64_t x_bs;        // batch stride of x, delta (elements)
+  int64_t bc_bs;       // batch stride of b, c (elements)
+  int64_t y_bs;        // batch stride of y (elements)
+  int32_t B, T, D;
+  int32_t chunk_len;   // steps per chunk (T when there is a single chunk)
+  int32_t chunks;      // number of chunks C
+};
+
+struct CarryParams {
+  const float2* pairs;  // (C-1,B,D,DS)
+  const float* h0;      // may be null
+  float* hin;           // (C-1,B,D,DS)
+  int64_t n;            // B*D*DS
+  int32_t chunks;
+};
+
+struct BwdParams {
+  const void* dy;
+  const float* dhT;    // may be null
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* b;
+  const void* c;
+  const float* h0;     // may be null
+  const float* H;
+  float* gx;
+  float* gdelta;
+  float* gh0;          // may be null
+  float2* part_bc;     // (ntiles_d, B, T, DS): per-workgroup (gb, gc) partial sums
+  float* part_A;       // (B, D, DS): per-batch-row gA partial sums
+  int64_t x_bs;        // x, delta, dy
+  int64_t bc_bs;       // b, c
+  int64_t y_bs;        // gx, gdelta
+  int32_t B, T, D;
+  int32_t ntiles_d;
+};
+
+struct ReduceParams {
+  const float2* part_bc;
+  const float* part_A;
+  float* gb;
+  float* gc;
+  float* gA;
+  int32_t B, T, D, DS;
+  int32_t ntiles_d;
+};
+
+// Launchers (defined in the .hip translation units).  Each returns a hipError_t.
+hipError_t launch_fwd(int io, int DS, int lanes, bool local_pass, const FwdParams& p, dim3 grid, hipStream_t s);
+hipError_t launch_carry(const CarryParams& p, hipStream_t s);
+hipError_t launch_bwd(int io, int DS, int lanes, const BwdParams& p, dim3 grid, hipStream_t s);
+hipError_t launch_bwd_reduce(const ReduceParams& p, hipStream_t s);
+hipError_t launch_fill(float* dst, int64_t n, hipStream_t s);                         // dst[i] = 0
+hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t s);  // src ? copy : zero
+
+}  // namespace sscan

@@ -1,0 +1,171 @@
+"""Host-side checks of the C ABI: the library loads without a GPU, exports every
+function include/sscan.h declares, and rejects bad arguments before it touches
+the HIP runtime.  Every call here fails validation, so nothing is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from selective_state_space_sscan_amd import _lib
+from selective_state_space_sscan_amd._lib import sscan_desc, sscan_plan
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sscan.h")
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_WS, E_HIP = range(8)
+FAKE = 0x100000  # a 16-byte aligned address that is never dereferenced: validation fails first
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char\s*\*|const char\s*\*)\s*\**\s*(sscan_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def desc(B=2, T=8, D=16, DS=4, io=0, **kw):
+    d = sscan_desc()
+    d.B, d.T, d.D, d.DS, d.io = B, T, D, DS, io
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def fwd(lib, d, plan=None, x=FAKE, delta=FAKE, A=FAKE, b=FAKE, c=FAKE, h0=None, y=FAKE, hT=FAKE, H=None, ws=None,
+        ws_bytes=0):
+    v = lambda p: None if p is None else ctypes.c_void_p(p)
+    return lib.sscan_fwd(None if d is None else ctypes.byref(d), None if plan is None else ctypes.byref(plan), v(x),
+                         v(delta), v(A), v(b), v(c), v(h0), v(y), v(hT), v(H), v(ws), ctypes.c_size_t(ws_bytes), None)
+
+
+def bwd(lib, d, dy=FAKE, x=FAKE, delta=FAKE, A=FAKE, b=FAKE, c=FAKE, h0=None, H=FAKE, gx=FAKE, gd=FAKE, gb=FAKE,
+        gc=FAKE, gA=FAKE, gh0=None, ws=None, ws_bytes=0):
+    v = lambda p: None if p is None else ctypes.c_void_p(p)
+    return lib.sscan_bwd(ctypes.byref(d), None, v(dy), None, v(x), v(delta), v(A), v(b), v(c), v(h0), v(H), v(gx),
+                         v(gd), v(gb), v(gc), v(gA), v(gh0), v(ws), ctypes.c_size_t(ws_bytes), None)
+
+
+def test_header_declares_the_expected_functions():
+    assert header_functions() == sorted(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_version_and_status_strings(lib):
+    assert lib.sscan_version() == 1
+    for s in range(8):
+        assert lib.sscan_status_str(s)
+    assert lib.sscan_status_str(99) == b"unknown status"
+
+
+def test_struct_layout_matches_header():
+    assert ctypes.sizeof(sscan_desc) == 8 * 4 + 4 * 2 + 8 * 3
+    assert ctypes.sizeof(sscan_plan) == 4 * 8
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), E_SHAPE), (dict(T=-3), E_SHAPE), (dict(D=-1), E_SHAPE),
+    (dict(DS=3), E_UNSUP), (dict(DS=32), E_UNSUP), (dict(DS=0), E_UNSUP),
+    (dict(io=2), E_DTYPE), (dict(reserved=1), E_UNSUP), (dict(B=70000), E_UNSUP),
+    (dict(x_bstride=10), E_SHAPE), (dict(bc_bstride=5), E_SHAPE), (dict(y_bstride=100), E_SHAPE),
+])
+def test_descriptor_validation(lib, kw, status):
+    assert fwd(lib, desc(**kw)) == status
+    assert lib.sscan_last_error()
+
+
+def test_null_descriptor(lib):
+    assert fwd(lib, None) == E_NULL
+    n = ctypes.c_size_t()
+    assert lib.sscan_fwd_workspace(None, None, ctypes.byref(n)) == E_NULL
+
+
+@pytest.mark.parametrize("missing", ["x", "delta", "A", "b", "c", "y"])
+def test_forward_required_pointers(lib, missing):
+    assert fwd(lib, desc(), **{missing: None}) == E_NULL
+
+
+@pytest.mark.parametrize("arg,addr", [("x", FAKE + 2), ("y", FAKE + 1), ("A", FAKE + 4), ("H", FAKE + 8),
+                                      ("h0", FAKE + 4), ("hT", FAKE + 12)])
+def test_forward_alignment(lib, arg, addr):
+    assert fwd(lib, desc(), **{arg: addr}) == E_ALIGN
+
+
+def test_bf16_io_needs_only_two_byte_alignment_but_not_odd(lib):
+    assert fwd(lib, desc(io=1), x=FAKE + 1) == E_ALIGN
+
+
+def test_plan_validation(lib):
+    p = sscan_plan()
+    p.lanes = 3
+    assert fwd(lib, desc(), plan=p) == E_UNSUP
+    p.lanes = 8  # more lanes than DS=4 states
+    assert fwd(lib, desc(), plan=p) == E_UNSUP
+    p.lanes = 0
+    p.chunks = -1
+    assert fwd(lib, desc(), plan=p) == E_UNSUP
+    p.chunks = 0
+    p.reserved[2] = 1
+    assert fwd(lib, desc(), plan=p) == E_UNSUP
+
+
+def test_forward_workspace_required_for_chunked_plan(lib):
+    p = sscan_plan()
+    p.lanes, p.chunks = 4, 4
+    n = ctypes.c_size_t()
+    d = desc(B=2, T=64, D=16, DS=4)
+    assert lib.sscan_fwd_workspace(ctypes.byref(d), ctypes.byref(p), ctypes.byref(n)) == OK
+    assert n.value > 0
+    assert fwd(lib, d, plan=p) == E_WS
+    assert fwd(lib, d, plan=p, ws=FAKE, ws_bytes=n.value - 1) == E_WS
+
+
+def test_backward_validation(lib):
+    assert bwd(lib, desc(), H=None) == E_NULL
+    assert bwd(lib, desc(), gA=None) == E_NULL
+    assert bwd(lib, desc(), dy=None) == E_NULL
+    assert bwd(lib, desc(), gA=FAKE + 4) == E_ALIGN
+    assert bwd(lib, desc(), gx=FAKE + 2) == E_ALIGN
+    assert bwd(lib, desc()) == E_WS  # workspace is always needed when there are steps
+    p = sscan_plan()
+    p.chunks = 2
+    d = desc()
+    assert lib.sscan_bwd(ctypes.byref(d), ctypes.byref(p), *([None] * 15), None, ctypes.c_size_t(0), None) == E_UNSUP
+
+
+def test_empty_problems_need_no_pointers(lib):
+    # B == 0 or D == 0: nothing to compute and nothing to write in the forward.
+    assert fwd(lib, desc(B=0), x=None, delta=None, A=None, b=None, c=None, y=None, hT=None) == OK
+    assert fwd(lib, desc(D=0), x=None, delta=None, A=None, b=None, c=None, y=None, hT=None) == OK
+    # T == 0 with no hT requested: nothing to write.
+    assert fwd(lib, desc(T=0), x=None, delta=None, A=None, b=None, c=None, y=None, hT=None) == OK
+
+
+def test_plan_select_and_workspace_sizes(lib):
+    cases = {(16, 4096, 1024, 16): 4, (4, 2048, 2048, 16): 8, (8, 2048, 768, 16): 16, (1, 64, 16, 4): 4}
+    for (B, T, D, DS), lanes in cases.items():
+        d = desc(B=B, T=T, D=D, DS=DS)
+        p = sscan_plan()
+        assert lib.sscan_plan_select(ctypes.byref(d), 0, ctypes.byref(p)) == OK
+        assert p.lanes == lanes, (B, T, D, DS, p.lanes)
+    # the small fp32 workload splits its sequence to fill the GPU
+    d = desc(B=8, T=1024, D=256, DS=16)
+    p = sscan_plan()
+    assert lib.sscan_plan_select(ctypes.byref(d), 0, ctypes.byref(p)) == OK
+    assert p.lanes == 16 and p.chunks == 2
+    # backward partial buffers: one (gb, gc) pair per channel tile, step and state, plus gA per batch row
+    d = desc(B=8, T=2048, D=768, DS=16)
+    n = ctypes.c_size_t()
+    assert lib.sscan_bwd_workspace(ctypes.byref(d), None, ctypes.byref(n)) == OK
+    tiles = (768 + 15) // 16
+    assert n.value >= tiles * 8 * 2048 * 16 * 8 + 8 * 768 * 16 * 4
