@@ -70,6 +70,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fwd-only", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 3 times (to scale HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the scan runs on a single MI355X and this build has no multi-GPU "
@@ -78,6 +80,16 @@ def main() -> int:
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": src.numel() * 4, "bytes_written": dst.numel() * 4,
+                          "launches": 3}))
+        return 0
 
     import workloads
     from selective_state_space_sscan_amd import sscan_bwd, sscan_bwd_workspace, sscan_fwd, sscan_fwd_workspace

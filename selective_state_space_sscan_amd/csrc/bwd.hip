@@ -31,25 +31,28 @@ namespace {
 
 template <int K>
 __device__ __forceinline__ void load_k(const float* __restrict__ p, float (&v)[K]) {
-  if constexpr (K % 4 == 0) {
-#pragma unroll
-    for (int q = 0; q < K / 4; ++q) {
-      const float4 t = reinterpret_cast<const float4*>(p)[q];
-      v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
-    }
-  } else if constexpr (K == 2) {
-    const float2 t = *reinterpret_cast<const float2*>(p);
-    v[0] = t.x; v[1] = t.y;
-  } else {
-    v[0] = p[0];
-  }
+  lds_load_vec<K>(p, v);  // plain vector load; also valid for global memory
 }
 
-// Steps of H per prefetch sub-block: at most 32 floats per lane, and at least two
-// sub-blocks per tile so the two buffers alternate at compile-time positions.
+// Steps per batch: the decays of a batch are formed together, then the adjoint carry
+// runs through it, then the per-step gradient terms and their sums.  S*K <= 8 and at
+// least two batches per tile.
 template <int K, int TB>
-__host__ __device__ constexpr int h_block_steps() {
-  return (32 / K) < (TB / 2) ? (32 / K) : (TB / 2);
+__host__ __device__ constexpr int bwd_batch_steps() {
+  return (8 / K) < 1 ? 1 : ((8 / K) < (TB / 2) ? (8 / K) : (TB / 2));
+}
+
+// Reduce-scatter of per-lane values over the four 16-lane rows of a wave for a pair of
+// items: afterwards row 0 holds the 4-row total of b0, row 1 of b1, row 2 of c0 and
+// row 3 of c1.  The gfx950 row-swap permutes exchange halves between two registers.
+__device__ __forceinline__ float rows_reduce_scatter(float b0, float c0, float b1, float c1) {
+  auto p0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(b0), __float_as_uint(c0), false, false);
+  auto p1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(b1), __float_as_uint(c1), false, false);
+  // lanes 0-31: b summed over rows (r, r+2); lanes 32-63: c summed likewise
+  const float v0 = __uint_as_float(p0[0]) + __uint_as_float(p0[1]);
+  const float v1 = __uint_as_float(p1[0]) + __uint_as_float(p1[1]);
+  auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v0), __float_as_uint(v1), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
 template <typename IO, int DS, int L>
@@ -62,38 +65,49 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(const BwdParams p) {
   constexpr int BC = TB * DS;
   constexpr int PER_BC = (BC + kThreads - 1) / kThreads;
   constexpr int NWAVE = kThreads / 64;
-  constexpr int HB = h_block_steps<K, TB>();
+  constexpr int S = bwd_batch_steps<K, TB>();
+  constexpr int HB = (2 * S) < (TB / 2) ? (2 * S) : (TB / 2);  // steps of H per prefetch block
   constexpr int NSUB = TB / HB;
-  static_assert(TILE % kThreads == 0 && TB % HB == 0, "tile shape");
-  static_assert(NSUB % 2 == 0, "sub-blocks per tile must be even");
+  constexpr int NBAT = HB / S;
+  constexpr int NITEM = S * K;
+  constexpr uint32_t ES = sizeof(IO);
+  static_assert(TILE % kThreads == 0 && TB % HB == 0 && HB % S == 0, "tile shape");
+  static_assert(NSUB % 2 == 0, "H blocks per tile must be even");
+  static_assert(NITEM % 2 == 0, "items per batch must pair up");
 
-  __shared__ float4 s_in[TILE];         // (delta, x, dy, delta*x) at [step*CPW + channel]
+  __shared__ float4 s_in[TILE];              // (delta, x, dy, delta*x) at [step*CPW + channel]
   __shared__ float s_b[BC];
   __shared__ float s_c[BC];
-  __shared__ float2 s_gxd[TILE];        // (gx, gdelta)
-  __shared__ float2 s_red[NWAVE * BC];  // per-wave (gb, gc) sums at [wave*BC + step*DS + n]
+  __shared__ float2 s_gxd[TILE];             // (gx, gdelta)
+  __shared__ float s_red[2 * NWAVE * BC];    // per-wave gb sums, then per-wave gc sums
+
+  const int lin = xcd_grouped(blockIdx.x, gridDim.x, p.xcd_group);
+  const int dtile = lin % p.ntiles_d;
+  const int bb = lin / p.ntiles_d;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int row = lane >> 4;
   const int ch = tid / L;
   const int j = tid % L;
-  const int d0 = blockIdx.x * CPW;
-  const int bb = blockIdx.y;
+  const int d0 = dtile * CPW;
   const int D = p.D;
   const int T = p.T;
   const int d = d0 + ch;
   const bool dvalid = d < D;
 
-  const IO* __restrict__ xg = static_cast<const IO*>(p.x) + (int64_t)bb * p.x_bs;
-  const IO* __restrict__ dg = static_cast<const IO*>(p.delta) + (int64_t)bb * p.x_bs;
-  const IO* __restrict__ yg = static_cast<const IO*>(p.dy) + (int64_t)bb * p.x_bs;
-  const IO* __restrict__ bg = static_cast<const IO*>(p.b) + (int64_t)bb * p.bc_bs;
-  const IO* __restrict__ cg = static_cast<const IO*>(p.c) + (int64_t)bb * p.bc_bs;
-  // this lane's states of step t live at Hrow + t * (D*DS)
-  const int64_t hstride = (int64_t)D * DS;
-  const float* __restrict__ Hrow = p.H + (int64_t)bb * T * hstride + (int64_t)d * DS + j * K;
+  const IO* xrow = static_cast<const IO*>(p.x) + (int64_t)bb * p.x_bs;
+  const IO* drow = static_cast<const IO*>(p.delta) + (int64_t)bb * p.x_bs;
+  const IO* yrow = static_cast<const IO*>(p.dy) + (int64_t)bb * p.x_bs;
+  const IO* brow = static_cast<const IO*>(p.b) + (int64_t)bb * p.bc_bs;
+  const IO* crow = static_cast<const IO*>(p.c) + (int64_t)bb * p.bc_bs;
+  float* gxrow = p.gx + (int64_t)bb * p.y_bs;
+  float* gdrow = p.gdelta + (int64_t)bb * p.y_bs;
+  const float* Hrow = p.H + (int64_t)bb * T * D * DS;
   const int64_t soff = ((int64_t)bb * D + d) * DS + j * K;
+  const uint32_t hstep = static_cast<uint32_t>(D) * DS * 4u;
+  const uint32_t hlane = dvalid ? static_cast<uint32_t>(d * DS + j * K) * 4u : kOutOfRange;
 
   float Av[K], A2[K], G[K], gA[K], hcur[K];
 #pragma unroll
@@ -101,7 +115,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(const BwdParams p) {
   if (dvalid) {
     load_k<K>(p.A + (int64_t)d * DS + j * K, Av);
     if (p.dhT != nullptr) load_k<K>(p.dhT + soff, G);
-    if (T > 0) load_k<K>(Hrow + (int64_t)(T - 1) * hstride, hcur);
+    if (T > 0) load_k<K>(Hrow + (int64_t)(T - 1) * D * DS + d * DS + j * K, hcur);
   }
 #pragma unroll
   for (int i = 0; i < K; ++i) A2[i] = Av[i] * kLog2e;
@@ -109,68 +123,66 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(const BwdParams p) {
   const int ntiles = (T + TB - 1) / TB;
 
   // ---- staged step inputs (one tile ahead) ----
-  IO rx[PER], rd[PER], ry[PER], rb[PER_BC], rc[PER_BC];
+  uint32_t xoff[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int idx = tid + e * kThreads;
+    const int dd = d0 + idx % CPW;
+    xoff[e] = dd < D ? static_cast<uint32_t>((idx / CPW) * D + dd) * ES : kOutOfRange;
+  }
+  uint32_t bcoff[PER_BC];
+#pragma unroll
+  for (int e = 0; e < PER_BC; ++e) {
+    const int idx = tid + e * kThreads;
+    bcoff[e] = idx < BC ? static_cast<uint32_t>(idx) * ES : kOutOfRange;
+  }
+  float rx[PER], rd[PER], ry[PER], rb[PER_BC], rc[PER_BC];
   auto load_tile = [&](int ts) {
+    const int rows = min(TB, T - ts);
+    const rsrc_t rX = make_rsrc(xrow + (int64_t)ts * D, static_cast<uint32_t>(rows * D) * ES);
+    const rsrc_t rD = make_rsrc(drow + (int64_t)ts * D, static_cast<uint32_t>(rows * D) * ES);
+    const rsrc_t rY = make_rsrc(yrow + (int64_t)ts * D, static_cast<uint32_t>(rows * D) * ES);
+    const rsrc_t rB = make_rsrc(brow + (int64_t)ts * DS, static_cast<uint32_t>(rows * DS) * ES);
+    const rsrc_t rC = make_rsrc(crow + (int64_t)ts * DS, static_cast<uint32_t>(rows * DS) * ES);
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-      const int idx = tid + e * kThreads;
-      const int t = ts + idx / CPW;
-      const int dd = d0 + idx % CPW;
-      if (t < T && dd < D) {
-        const int64_t o = (int64_t)t * D + dd;
-        rx[e] = xg[o];
-        rd[e] = dg[o];
-        ry[e] = yg[o];
-      } else {
-        rx[e] = IO{}; rd[e] = IO{}; ry[e] = IO{};
-      }
+      rx[e] = buf_load_elem<IO>(rX, xoff[e]);
+      rd[e] = buf_load_elem<IO>(rD, xoff[e]);
+      ry[e] = buf_load_elem<IO>(rY, xoff[e]);
     }
 #pragma unroll
     for (int e = 0; e < PER_BC; ++e) {
-      const int idx = tid + e * kThreads;
-      const int t = ts + idx / DS;
-      if (idx < BC && t < T) {
-        rb[e] = bg[(int64_t)t * DS + idx % DS];
-        rc[e] = cg[(int64_t)t * DS + idx % DS];
-      } else {
-        rb[e] = IO{}; rc[e] = IO{};
-      }
+      rb[e] = buf_load_elem<IO>(rB, bcoff[e]);
+      rc[e] = buf_load_elem<IO>(rC, bcoff[e]);
     }
   };
   auto store_tile = [&]() {
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const float dl = to_f32(rd[e]);
-      const float xv = to_f32(rx[e]);
-      s_in[tid + e * kThreads] = make_float4(dl, xv, to_f32(ry[e]), dl * xv);
-    }
+    for (int e = 0; e < PER; ++e) s_in[tid + e * kThreads] = make_float4(rd[e], rx[e], ry[e], rd[e] * rx[e]);
 #pragma unroll
     for (int e = 0; e < PER_BC; ++e) {
       const int idx = tid + e * kThreads;
-      if (idx < BC) {
-        s_b[idx] = to_f32(rb[e]);
-        s_c[idx] = to_f32(rc[e]);
+      if (BC % kThreads == 0 || idx < BC) {
+        s_b[idx] = rb[e];
+        s_c[idx] = rc[e];
       }
     }
   };
 
-  // ---- H_{t-1} for one sub-block of HB steps, prefetched one sub-block ahead ----
-  // Sub-block (tile it, sub s) covers steps ts + s*HB + [0, HB); its entry r holds H_{t-1}
-  // for t = ts + s*HB + r, i.e. h0 for t = 0 and 0 for steps outside [1, T].
+  // ---- H_{t-1} for a block of HB steps starting at step tf, prefetched a block ahead ----
+  // Entry r holds H_{tf+r-1}: h0 for step 0, and 0 for steps outside [1, T].
   float hbuf[2][HB][K];
-  auto load_hblock = [&](float (&dst)[HB][K], int tfirst) {
+  auto load_hblock = [&](float (&dst)[HB][K], int tf) {
+    const int t_lo = max(tf - 1, 0);
+    const int t_hi = min(tf - 1 + HB, T);  // exclusive
+    const rsrc_t rH = make_rsrc(Hrow + (int64_t)t_lo * D * DS, static_cast<uint32_t>(max(t_hi - t_lo, 0)) * hstep);
 #pragma unroll
     for (int r = 0; r < HB; ++r) {
-      const int tp = tfirst + r - 1;  // index of the state to read
-      if (dvalid && tp >= 0 && tp < T) {
-        load_k<K>(Hrow + (int64_t)tp * hstride, dst[r]);
-      } else if (dvalid && tp == -1 && p.h0 != nullptr) {
-        load_k<K>(p.h0 + soff, dst[r]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < K; ++i) dst[r][i] = 0.f;
-      }
+      const int tp = tf - 1 + r;
+      const uint32_t off = (tp >= 0) ? hlane + static_cast<uint32_t>(tp - t_lo) * hstep : kOutOfRange;
+      buf_load_vec<K>(rH, off, dst[r]);
     }
+    if (tf == 0 && p.h0 != nullptr && dvalid) load_k<K>(p.h0 + soff, dst[0]);
   };
 
   if (ntiles > 0) {
@@ -187,82 +199,116 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(const BwdParams p) {
     if (it > 0) load_tile(ts - TB);
 
 #pragma unroll
-    for (int s = NSUB - 1; s >= 0; --s) {
-      // Sub-blocks are consumed in one global sequence; an even number precede each
-      // tile, so the buffer roles depend only on s.
-      float (&cur)[HB][K] = hbuf[(NSUB - 1 - s) & 1];
-      float (&nxt)[HB][K] = hbuf[((NSUB - 1 - s) & 1) ^ 1];
-      // prefetch the next sub-block in sweep order
-      if (s > 0) {
-        load_hblock(nxt, ts + (s - 1) * HB);
+    for (int sb = NSUB - 1; sb >= 0; --sb) {
+      // An even number of H blocks precede each tile, so buffer roles depend only on sb.
+      float (&cur)[HB][K] = hbuf[(NSUB - 1 - sb) & 1];
+      float (&nxt)[HB][K] = hbuf[((NSUB - 1 - sb) & 1) ^ 1];
+      if (sb > 0) {
+        load_hblock(nxt, ts + (sb - 1) * HB);
       } else if (it > 0) {
         load_hblock(nxt, ts - TB + (NSUB - 1) * HB);
       }
 
 #pragma unroll
-      for (int r = HB - 1; r >= 0; --r) {
-        const int tt = s * HB + r;
-        const float4 in = s_in[tt * CPW + ch];  // (delta, x, dy, delta*x)
-        float bv[K], cv[K];
-        load_k<K>(&s_b[tt * DS + j * K], bv);
-        load_k<K>(&s_c[tt * DS + j * K], cv);
-        float S = 0.f, gd = 0.f;
-        float gbp[K], gcp[K];
+      for (int bt = NBAT - 1; bt >= 0; --bt) {
+        const int tt0 = sb * HB + bt * S;  // first step of the batch within the tile
+        // phase A: decays of the batch
+        float a[S][K], g[S][K], cv[S][K];
+        float4 in[S];
 #pragma unroll
-        for (int i = 0; i < K; ++i) {
-          const float a = exp2_hw(in.x * A2[i]);
-          const float g = fmaf(in.z, cv[i], G[i]);
-          S = fmaf(g, bv[i], S);
-          G[i] = a * g;
-          const float q = G[i] * cur[r][i];
-          gd = fmaf(Av[i], q, gd);
-          gA[i] = fmaf(in.x, q, gA[i]);
-          gbp[i] = g * in.w;
-          gcp[i] = in.z * hcur[i];
-          hcur[i] = cur[r][i];
+        for (int s = 0; s < S; ++s) {
+          in[s] = s_in[(tt0 + s) * CPW + ch];
+          lds_load_vec<K>(&s_c[(tt0 + s) * DS + j * K], cv[s]);
+#pragma unroll
+          for (int i = 0; i < K; ++i) a[s][i] = exp2_hw(in[s].x * A2[i]);
         }
-        S = group_sum<L>(S);
-        gd = group_sum<L>(gd);
-        if (j == 0) s_gxd[tt * CPW + ch] = make_float2(in.x * S, fmaf(in.y, S, gd));
+        // phase B: the adjoint carry, last step first; a[s] becomes the carry a_t g_t
 #pragma unroll
-        for (int i = 0; i < K; ++i) {
-          gbp[i] = cross_row_sum(row_channel_sum<L>(gbp[i]));
-          gcp[i] = cross_row_sum(row_channel_sum<L>(gcp[i]));
+        for (int s = S - 1; s >= 0; --s) {
+#pragma unroll
+          for (int i = 0; i < K; ++i) {
+            g[s][i] = fmaf(in[s].z, cv[s][i], G[i]);
+            G[i] = a[s][i] * g[s][i];
+            a[s][i] = G[i];
+          }
         }
-        if (lane < L) {
+        // phase C: gradient terms of each step
+        float Sl[S], gdl[S], gbv[S][K], gcv[S][K];
 #pragma unroll
-          for (int i = 0; i < K; ++i) s_red[wave * BC + tt * DS + j * K + i] = make_float2(gbp[i], gcp[i]);
+        for (int s = 0; s < S; ++s) {
+          float bv[K];
+          lds_load_vec<K>(&s_b[(tt0 + s) * DS + j * K], bv);
+          const float(&hp)[K] = cur[bt * S + s];                          // H_{t-1}
+          const float(&ht)[K] = (s == S - 1) ? hcur : cur[bt * S + s + 1];  // H_t
+          float sl = 0.f, gd = 0.f;
+#pragma unroll
+          for (int i = 0; i < K; ++i) {
+            sl = fmaf(g[s][i], bv[i], sl);
+            const float q = a[s][i] * hp[i];
+            gd = fmaf(Av[i], q, gd);
+            gA[i] = fmaf(in[s].x, q, gA[i]);
+            gbv[s][i] = g[s][i] * in[s].w;
+            gcv[s][i] = in[s].z * ht[i];
+          }
+          Sl[s] = sl;
+          gdl[s] = gd;
+        }
+#pragma unroll
+        for (int i = 0; i < K; ++i) hcur[i] = cur[bt * S][i];
+        // phase D: sums over each channel's states -> gx, gdelta
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          const float st = group_sum<L>(Sl[s]);
+          const float gt = group_sum<L>(gdl[s]);
+          s_gxd[(tt0 + s) * CPW + ch] = make_float2(in[s].x * st, fmaf(in[s].y, st, gt));
+        }
+        // phase E: sums over the channels of the wave -> one (gb, gc) slot per wave
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+#pragma unroll
+          for (int i = 0; i < K; ++i) {
+            gbv[s][i] = row_channel_sum<L>(gbv[s][i]);
+            gcv[s][i] = row_channel_sum<L>(gcv[s][i]);
+          }
+        }
+#pragma unroll
+        for (int it2 = 0; it2 < NITEM; it2 += 2) {
+          const int s_a = it2 / K, i_a = it2 % K;
+          const int s_b2 = (it2 + 1) / K, i_b = (it2 + 1) % K;
+          const float v = rows_reduce_scatter(gbv[s_a][i_a], gcv[s_a][i_a], gbv[s_b2][i_b], gcv[s_b2][i_b]);
+          const int sel = row & 1;
+          const int ss = sel ? s_b2 : s_a;
+          const int ii = sel ? i_b : i_a;
+          s_red[(row >> 1) * (NWAVE * BC) + wave * BC + (tt0 + ss) * DS + j * K + ii] = v;
         }
       }
     }
 
     __syncthreads();
+    {
+      const int rows = min(TB, T - ts);
+      const rsrc_t rGX = make_rsrc(gxrow + (int64_t)ts * D, static_cast<uint32_t>(rows * D) * 4u);
+      const rsrc_t rGD = make_rsrc(gdrow + (int64_t)ts * D, static_cast<uint32_t>(rows * D) * 4u);
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int idx = tid + e * kThreads;
-      const int t = ts + idx / CPW;
-      const int dd = d0 + idx % CPW;
-      if (t < T && dd < D) {
-        const float2 v = s_gxd[idx];
-        const int64_t o = (int64_t)bb * p.y_bs + (int64_t)t * D + dd;
-        p.gx[o] = v.x;
-        p.gdelta[o] = v.y;
+      for (int e = 0; e < PER; ++e) {
+        const float2 v = s_gxd[tid + e * kThreads];
+        const uint32_t off = xoff[e] == kOutOfRange ? kOutOfRange : xoff[e] / ES * 4u;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v.x), rGX, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v.y), rGD, off, 0, 0);
       }
-    }
-    float2* __restrict__ part = p.part_bc + ((int64_t)blockIdx.x * p.B + bb) * T * DS;
+      float2* __restrict__ part = p.part_bc + ((int64_t)dtile * p.B + bb) * T * DS + (int64_t)ts * DS;
 #pragma unroll
-    for (int e = 0; e < PER_BC; ++e) {
-      const int idx = tid + e * kThreads;
-      const int t = ts + idx / DS;
-      if (idx < BC && t < T) {
-        float2 acc = s_red[idx];
+      for (int e = 0; e < PER_BC; ++e) {
+        const int idx = tid + e * kThreads;
+        if (idx < BC && ts + idx / DS < T) {
+          float sb = s_red[idx], sc = s_red[NWAVE * BC + idx];
 #pragma unroll
-        for (int w = 1; w < NWAVE; ++w) {
-          const float2 v = s_red[w * BC + idx];
-          acc.x += v.x;
-          acc.y += v.y;
+          for (int w = 1; w < NWAVE; ++w) {
+            sb += s_red[w * BC + idx];
+            sc += s_red[NWAVE * BC + w * BC + idx];
+          }
+          part[idx] = make_float2(sb, sc);
         }
-        part[(int64_t)t * DS + idx % DS] = acc;
       }
     }
   }
@@ -305,13 +351,13 @@ __global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(const ReduceParams
 }
 
 template <typename IO, int DS, int L>
-hipError_t launch_bwd_t(const BwdParams& p, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((bwd_kernel<IO, DS, L>), grid, dim3(kThreads), 0, s, p);
+hipError_t launch_bwd_t(const BwdParams& p, unsigned blocks, hipStream_t s) {
+  hipLaunchKernelGGL((bwd_kernel<IO, DS, L>), dim3(blocks), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
 template <typename IO, int DS>
-hipError_t launch_bwd_ds(int lanes, const BwdParams& p, dim3 grid, hipStream_t s) {
+hipError_t launch_bwd_ds(int lanes, const BwdParams& p, unsigned grid, hipStream_t s) {
   switch (lanes) {
     case 1: return launch_bwd_t<IO, DS, 1>(p, grid, s);
     case 2: if constexpr (DS >= 2) return launch_bwd_t<IO, DS, 2>(p, grid, s); break;
@@ -324,7 +370,7 @@ hipError_t launch_bwd_ds(int lanes, const BwdParams& p, dim3 grid, hipStream_t s
 }
 
 template <typename IO>
-hipError_t launch_bwd_io(int DS, int lanes, const BwdParams& p, dim3 grid, hipStream_t s) {
+hipError_t launch_bwd_io(int DS, int lanes, const BwdParams& p, unsigned grid, hipStream_t s) {
   switch (DS) {
     case 1: return launch_bwd_ds<IO, 1>(lanes, p, grid, s);
     case 2: return launch_bwd_ds<IO, 2>(lanes, p, grid, s);
@@ -337,7 +383,7 @@ hipError_t launch_bwd_io(int DS, int lanes, const BwdParams& p, dim3 grid, hipSt
 
 }  // namespace
 
-hipError_t launch_bwd(int io, int DS, int lanes, const BwdParams& p, dim3 grid, hipStream_t s) {
+hipError_t launch_bwd(int io, int DS, int lanes, const BwdParams& p, unsigned grid, hipStream_t s) {
   if (io == 0) return launch_bwd_io<float>(DS, lanes, p, grid, s);
   return launch_bwd_io<bf16_t>(DS, lanes, p, grid, s);
 }

@@ -27,9 +27,105 @@ __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) {
   return r;
 }
 
+// ---- bounded buffer access --------------------------------------------------------
+// A raw buffer resource covers [base, base + bytes).  Loads outside it return 0 and
+// stores outside it are dropped by the hardware, so tails need no branches.
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+constexpr uint32_t kOutOfRange = 0x80000000u;  // an offset beyond every resource this library builds
+constexpr int kRsrcWord3 = 0x00020000;         // raw 32-bit data, gfx9 family
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRsrcWord3);
+}
+
+__device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t off, float*) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t off, bf16_t*) {
+  return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0)) << 16);
+}
+// Load one element of type IO at byte offset `off` and widen it to fp32.
 template <typename IO>
-__device__ __forceinline__ float load_f32(const IO* p) {
-  return to_f32(*p);
+__device__ __forceinline__ float buf_load_elem(rsrc_t r, uint32_t off) {
+  return buf_load_f32(r, off, static_cast<IO*>(nullptr));
+}
+
+__device__ __forceinline__ void buf_store_elem(rsrc_t r, uint32_t off, float v, float*) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store_elem(rsrc_t r, uint32_t off, float v, bf16_t*) {
+  __builtin_amdgcn_raw_buffer_store_b16(from_f32<bf16_t>(v).bits, r, off, 0, 0);
+}
+template <typename IO>
+__device__ __forceinline__ void buf_store_io(rsrc_t r, uint32_t off, float v) {
+  buf_store_elem(r, off, v, static_cast<IO*>(nullptr));
+}
+
+// K consecutive fp32 values at byte offset off.
+template <int K>
+__device__ __forceinline__ void buf_load_vec(rsrc_t r, uint32_t off, float (&v)[K]) {
+  if constexpr (K % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < K / 4; ++q) {
+      const auto t = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * q, 0, 0);
+      v[4 * q] = __uint_as_float(t[0]); v[4 * q + 1] = __uint_as_float(t[1]);
+      v[4 * q + 2] = __uint_as_float(t[2]); v[4 * q + 3] = __uint_as_float(t[3]);
+    }
+  } else if constexpr (K == 2) {
+    const auto t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    v[0] = __uint_as_float(t[0]); v[1] = __uint_as_float(t[1]);
+  } else {
+    v[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+  }
+}
+
+template <int K>
+__device__ __forceinline__ void buf_store_vec(rsrc_t r, uint32_t off, const float (&v)[K]) {
+  if constexpr (K % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < K / 4; ++q) {
+      __attribute__((ext_vector_type(4))) uint32_t t;
+      t[0] = __float_as_uint(v[4 * q]); t[1] = __float_as_uint(v[4 * q + 1]);
+      t[2] = __float_as_uint(v[4 * q + 2]); t[3] = __float_as_uint(v[4 * q + 3]);
+      __builtin_amdgcn_raw_buffer_store_b128(t, r, off + 16 * q, 0, 0);
+    }
+  } else if constexpr (K == 2) {
+    __attribute__((ext_vector_type(2))) uint32_t t;
+    t[0] = __float_as_uint(v[0]); t[1] = __float_as_uint(v[1]);
+    __builtin_amdgcn_raw_buffer_store_b64(t, r, off, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[0]), r, off, 0, 0);
+  }
+}
+
+// K consecutive fp32 values from LDS.
+template <int K>
+__device__ __forceinline__ void lds_load_vec(const float* p, float (&v)[K]) {
+  if constexpr (K % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < K / 4; ++q) {
+      const float4 t = reinterpret_cast<const float4*>(p)[q];
+      v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
+    }
+  } else if constexpr (K == 2) {
+    const float2 t = *reinterpret_cast<const float2*>(p);
+    v[0] = t.x; v[1] = t.y;
+  } else {
+    v[0] = p[0];
+  }
+}
+
+// ---- XCD-aware workgroup order -------------------------------------------------------
+// Workgroups are dispatched to the 8 XCDs round-robin by linear id, and each XCD has its
+// own L2.  Remap linear ids so that G consecutive logical tiles (which share 128-byte
+// lines of x, delta and y) run on one XCD.  Bijective on [0, n).
+__device__ __forceinline__ int xcd_grouped(int lin, int n, int G) {
+  const int span = 8 * G;
+  const int full = (n / span) * span;
+  if (G <= 1 || lin >= full) return lin;
+  const int base = lin - lin % span;
+  const int r = lin - base;
+  return base + (r % 8) * G + r / 8;
 }
 
 // Hardware base-2 exponential (v_exp_f32).

@@ -27,18 +27,7 @@ namespace {
 
 template <int K>
 __device__ __forceinline__ void load_state(const float* __restrict__ p, float (&v)[K]) {
-  if constexpr (K % 4 == 0) {
-#pragma unroll
-    for (int q = 0; q < K / 4; ++q) {
-      const float4 t = reinterpret_cast<const float4*>(p)[q];
-      v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
-    }
-  } else if constexpr (K == 2) {
-    const float2 t = *reinterpret_cast<const float2*>(p);
-    v[0] = t.x; v[1] = t.y;
-  } else {
-    v[0] = p[0];
-  }
+  lds_load_vec<K>(p, v);  // plain vector load; also valid for global memory
 }
 
 template <int K>
@@ -54,6 +43,13 @@ __device__ __forceinline__ void store_state(float* __restrict__ p, const float (
   }
 }
 
+// Steps whose decays and injections are formed together before the serial update:
+// at most 32 floats per array per lane, at most 16 steps.
+template <int K, int TB>
+__host__ __device__ constexpr int fwd_batch_steps() {
+  return (32 / K) < 16 ? ((32 / K) < TB ? (32 / K) : TB) : (16 < TB ? 16 : TB);
+}
+
 template <typename IO, int DS, int L, bool LOCAL>
 __global__ __launch_bounds__(kThreads) void fwd_kernel(const FwdParams p) {
   constexpr int K = DS / L;
@@ -63,29 +59,37 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(const FwdParams p) {
   constexpr int PER = TILE / kThreads;
   constexpr int BC = TB * DS;
   constexpr int PER_BC = (BC + kThreads - 1) / kThreads;
-  static_assert(TILE % kThreads == 0, "tile must split evenly over the workgroup");
+  constexpr int S = fwd_batch_steps<K, TB>();
+  constexpr uint32_t ES = sizeof(IO);
+  static_assert(TILE % kThreads == 0 && TB % S == 0, "tile shape");
 
   __shared__ float2 s_dw[TILE];            // (delta, delta*x) at [step*CPW + channel]
   __shared__ float s_b[BC];                // b at [step*DS + n]
   __shared__ float s_c[BC];
   __shared__ float s_y[LOCAL ? 1 : TILE];  // y at [step*CPW + channel]
 
+  const int lin = xcd_grouped(blockIdx.x, gridDim.x, p.xcd_group);
+  const int dtile = lin % p.ntiles_d;
+  const int rest = lin / p.ntiles_d;
+  const int bb = rest % p.B;
+  const int chunk = rest / p.B;
+
   const int tid = threadIdx.x;
   const int ch = tid / L;
   const int j = tid % L;
-  const int d0 = blockIdx.x * CPW;
-  const int bb = blockIdx.y;
-  const int chunk = blockIdx.z;
   const int D = p.D;
+  const int d0 = dtile * CPW;
   const int t_begin = chunk * p.chunk_len;
   const int t_end = min(p.T, t_begin + p.chunk_len);
   const int d = d0 + ch;
   const bool dvalid = d < D;
 
-  const IO* __restrict__ xg = static_cast<const IO*>(p.x) + (int64_t)bb * p.x_bs;
-  const IO* __restrict__ dg = static_cast<const IO*>(p.delta) + (int64_t)bb * p.x_bs;
-  const IO* __restrict__ bg = static_cast<const IO*>(p.b) + (int64_t)bb * p.bc_bs;
-  const IO* __restrict__ cg = static_cast<const IO*>(p.c) + (int64_t)bb * p.bc_bs;
+  const IO* xrow = static_cast<const IO*>(p.x) + (int64_t)bb * p.x_bs;
+  const IO* drow = static_cast<const IO*>(p.delta) + (int64_t)bb * p.x_bs;
+  const IO* brow = static_cast<const IO*>(p.b) + (int64_t)bb * p.bc_bs;
+  const IO* crow = static_cast<const IO*>(p.c) + (int64_t)bb * p.bc_bs;
+  IO* yrow = static_cast<IO*>(p.y) + (int64_t)bb * p.y_bs;
+  float* Hrow = p.H + (int64_t)bb * p.T * D * DS;
 
   const int64_t nstate = (int64_t)p.B * D * DS;
   const int64_t soff = ((int64_t)bb * D + d) * DS + j * K;  // this lane's states in (B,D,DS)
@@ -109,46 +113,51 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(const FwdParams p) {
   }
   double dsum = 0.0;  // local pass: sum of delta over the chunk
 
-  IO rx[PER], rd[PER], rb[PER_BC], rc[PER_BC];
+  // Per-thread element offsets inside an x/delta/y tile (rows beyond the tile end fall
+  // outside the resource; columns beyond D are forced out of range).
+  uint32_t xoff[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int idx = tid + e * kThreads;
+    const int dd = d0 + idx % CPW;
+    xoff[e] = dd < D ? static_cast<uint32_t>((idx / CPW) * D + dd) * ES : kOutOfRange;
+  }
+  uint32_t bcoff[PER_BC];
+#pragma unroll
+  for (int e = 0; e < PER_BC; ++e) {
+    const int idx = tid + e * kThreads;
+    bcoff[e] = idx < BC ? static_cast<uint32_t>(idx) * ES : kOutOfRange;
+  }
+  const uint32_t hstep = static_cast<uint32_t>(D) * DS * 4u;  // bytes between steps of H
+  const uint32_t hlane = dvalid ? static_cast<uint32_t>(d * DS + j * K) * 4u : kOutOfRange;
+
+  float rx[PER], rd[PER], rb[PER_BC], rc[PER_BC];
   auto load_tile = [&](int ts) {
+    const int rows = min(TB, t_end - ts);
+    const rsrc_t rX = make_rsrc(xrow + (int64_t)ts * D, static_cast<uint32_t>(rows * D) * ES);
+    const rsrc_t rD = make_rsrc(drow + (int64_t)ts * D, static_cast<uint32_t>(rows * D) * ES);
+    const rsrc_t rB = make_rsrc(brow + (int64_t)ts * DS, static_cast<uint32_t>(rows * DS) * ES);
+    const rsrc_t rC = make_rsrc(crow + (int64_t)ts * DS, static_cast<uint32_t>(rows * DS) * ES);
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-      const int idx = tid + e * kThreads;
-      const int t = ts + idx / CPW;
-      const int dd = d0 + idx % CPW;
-      if (t < t_end && dd < D) {
-        rx[e] = xg[(int64_t)t * D + dd];
-        rd[e] = dg[(int64_t)t * D + dd];
-      } else {
-        rx[e] = IO{};
-        rd[e] = IO{};
-      }
+      rx[e] = buf_load_elem<IO>(rX, xoff[e]);
+      rd[e] = buf_load_elem<IO>(rD, xoff[e]);
     }
 #pragma unroll
     for (int e = 0; e < PER_BC; ++e) {
-      const int idx = tid + e * kThreads;
-      const int t = ts + idx / DS;
-      if (idx < BC && t < t_end) {
-        rb[e] = bg[(int64_t)t * DS + idx % DS];
-        rc[e] = cg[(int64_t)t * DS + idx % DS];
-      } else {
-        rb[e] = IO{};
-        rc[e] = IO{};
-      }
+      rb[e] = buf_load_elem<IO>(rB, bcoff[e]);
+      rc[e] = buf_load_elem<IO>(rC, bcoff[e]);
     }
   };
   auto store_tile = [&]() {
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const float dl = to_f32(rd[e]);
-      s_dw[tid + e * kThreads] = make_float2(dl, dl * to_f32(rx[e]));
-    }
+    for (int e = 0; e < PER; ++e) s_dw[tid + e * kThreads] = make_float2(rd[e], rd[e] * rx[e]);
 #pragma unroll
     for (int e = 0; e < PER_BC; ++e) {
       const int idx = tid + e * kThreads;
-      if (idx < BC) {
-        s_b[idx] = to_f32(rb[e]);
-        s_c[idx] = to_f32(rc[e]);
+      if (BC % kThreads == 0 || idx < BC) {
+        s_b[idx] = rb[e];
+        s_c[idx] = rc[e];
       }
     }
   };
@@ -159,50 +168,65 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(const FwdParams p) {
 
   for (int it = 0; it < ntiles; ++it) {
     const int ts = t_begin + it * TB;
+    const int rows = min(TB, t_end - ts);
     __syncthreads();  // the previous tile's LDS reads are complete
     store_tile();
     __syncthreads();
     if (it + 1 < ntiles) load_tile(ts + TB);
 
-#pragma unroll 4
-    for (int tt = 0; tt < TB; ++tt) {
-      const float2 dw = s_dw[tt * CPW + ch];
-      float bv[K];
-      load_state<K>(&s_b[tt * DS + j * K], bv);
+    const rsrc_t rH = make_rsrc(Hrow + (int64_t)ts * D * DS, static_cast<uint32_t>(rows) * hstep);
+#pragma unroll 1
+    for (int s0 = 0; s0 < TB; s0 += S) {
+      // decays and injections of S steps: independent of the state, issued together
+      float a[S][K], u[S][K];
+      float dl[S];
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const float2 dw = s_dw[(s0 + s) * CPW + ch];
+        float bv[K];
+        lds_load_vec<K>(&s_b[(s0 + s) * DS + j * K], bv);
+#pragma unroll
+        for (int i = 0; i < K; ++i) {
+          a[s][i] = exp2_hw(dw.x * A2[i]);
+          u[s][i] = dw.y * bv[i];
+        }
+        dl[s] = dw.x;
+      }
+      // the serial part: one fma per (step, state); a[s] then holds the state after step s
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+#pragma unroll
+        for (int i = 0; i < K; ++i) {
+          h[i] = fmaf(a[s][i], h[i], u[s][i]);
+          a[s][i] = h[i];
+        }
+      }
       if constexpr (LOCAL) {
-        dsum += dw.x;
 #pragma unroll
-        for (int i = 0; i < K; ++i) {
-          const float a = exp2_hw(dw.x * A2[i]);
-          h[i] = fmaf(a, h[i], dw.y * bv[i]);
-        }
+        for (int s = 0; s < S; ++s) dsum += dl[s];
       } else {
-        float cv[K];
-        load_state<K>(&s_c[tt * DS + j * K], cv);
-        float yp = 0.f;
+        // readouts of S steps, independent of each other
 #pragma unroll
-        for (int i = 0; i < K; ++i) {
-          const float a = exp2_hw(dw.x * A2[i]);
-          h[i] = fmaf(a, h[i], dw.y * bv[i]);
-          yp = fmaf(h[i], cv[i], yp);
+        for (int s = 0; s < S; ++s) {
+          float cv[K];
+          lds_load_vec<K>(&s_c[(s0 + s) * DS + j * K], cv);
+          float yp = 0.f;
+#pragma unroll
+          for (int i = 0; i < K; ++i) yp = fmaf(a[s][i], cv[i], yp);
+          s_y[(s0 + s) * CPW + ch] = group_sum<L>(yp);  // every lane of the channel holds the sum
         }
-        yp = group_sum<L>(yp);
-        if (j == 0) s_y[tt * CPW + ch] = yp;
-        if (p.H != nullptr && dvalid && ts + tt < t_end)
-          store_state<K>(p.H + (((int64_t)bb * p.T + ts + tt) * D + d) * DS + j * K, h);
+        if (p.H != nullptr) {
+#pragma unroll
+          for (int s = 0; s < S; ++s) buf_store_vec<K>(rH, hlane + static_cast<uint32_t>(s0 + s) * hstep, a[s]);
+        }
       }
     }
 
     if constexpr (!LOCAL) {
       __syncthreads();
-      IO* __restrict__ yg = static_cast<IO*>(p.y) + (int64_t)bb * p.y_bs;
+      const rsrc_t rY = make_rsrc(yrow + (int64_t)ts * D, static_cast<uint32_t>(rows * D) * ES);
 #pragma unroll
-      for (int e = 0; e < PER; ++e) {
-        const int idx = tid + e * kThreads;
-        const int t = ts + idx / CPW;
-        const int dd = d0 + idx % CPW;
-        if (t < t_end && dd < D) yg[(int64_t)t * D + dd] = from_f32<IO>(s_y[idx]);
-      }
+      for (int e = 0; e < PER; ++e) buf_store_io<IO>(rY, xoff[e], s_y[tid + e * kThreads]);
     }
   }
 
@@ -210,7 +234,8 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(const FwdParams p) {
   if constexpr (LOCAL) {
     float2* pr = p.pairs + (int64_t)chunk * nstate + soff;
 #pragma unroll
-    for (int i = 0; i < K; ++i) pr[i] = make_float2(exp2_hw(static_cast<float>(static_cast<double>(A2[i]) * dsum)), h[i]);
+    for (int i = 0; i < K; ++i)
+      pr[i] = make_float2(exp2_hw(static_cast<float>(static_cast<double>(A2[i]) * dsum)), h[i]);
   } else {
     if (p.hT != nullptr && chunk == p.chunks - 1) store_state<K>(p.hT + soff, h);
   }
@@ -233,16 +258,16 @@ __global__ __launch_bounds__(kThreads) void fill_kernel(float* __restrict__ dst,
 }
 
 template <typename IO, int DS, int L>
-hipError_t launch_fwd_t(bool local_pass, const FwdParams& p, dim3 grid, hipStream_t s) {
+hipError_t launch_fwd_t(bool local_pass, const FwdParams& p, unsigned blocks, hipStream_t s) {
   if (local_pass)
-    hipLaunchKernelGGL((fwd_kernel<IO, DS, L, true>), grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((fwd_kernel<IO, DS, L, true>), dim3(blocks), dim3(kThreads), 0, s, p);
   else
-    hipLaunchKernelGGL((fwd_kernel<IO, DS, L, false>), grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((fwd_kernel<IO, DS, L, false>), dim3(blocks), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
 template <typename IO, int DS>
-hipError_t launch_fwd_ds(int lanes, bool local_pass, const FwdParams& p, dim3 grid, hipStream_t s) {
+hipError_t launch_fwd_ds(int lanes, bool local_pass, const FwdParams& p, unsigned grid, hipStream_t s) {
   switch (lanes) {
     case 1: return launch_fwd_t<IO, DS, 1>(local_pass, p, grid, s);
     case 2: if constexpr (DS >= 2) return launch_fwd_t<IO, DS, 2>(local_pass, p, grid, s); break;
@@ -255,7 +280,7 @@ hipError_t launch_fwd_ds(int lanes, bool local_pass, const FwdParams& p, dim3 gr
 }
 
 template <typename IO>
-hipError_t launch_fwd_io(int DS, int lanes, bool local_pass, const FwdParams& p, dim3 grid, hipStream_t s) {
+hipError_t launch_fwd_io(int DS, int lanes, bool local_pass, const FwdParams& p, unsigned grid, hipStream_t s) {
   switch (DS) {
     case 1: return launch_fwd_ds<IO, 1>(lanes, local_pass, p, grid, s);
     case 2: return launch_fwd_ds<IO, 2>(lanes, local_pass, p, grid, s);
@@ -268,7 +293,7 @@ hipError_t launch_fwd_io(int DS, int lanes, bool local_pass, const FwdParams& p,
 
 }  // namespace
 
-hipError_t launch_fwd(int io, int DS, int lanes, bool local_pass, const FwdParams& p, dim3 grid, hipStream_t s) {
+hipError_t launch_fwd(int io, int DS, int lanes, bool local_pass, const FwdParams& p, unsigned grid, hipStream_t s) {
   if (io == 0) return launch_fwd_io<float>(DS, lanes, local_pass, p, grid, s);
   return launch_fwd_io<bf16_t>(DS, lanes, local_pass, p, grid, s);
 }

@@ -52,8 +52,10 @@ int resolve_desc(const sscan_desc* desc, Resolved* r) {
   if (desc->io != SSCAN_F32 && desc->io != SSCAN_BF16) return fail(SSCAN_ERR_DTYPE, "io dtype %d is unknown", desc->io);
   if (desc->reserved != 0) return fail(SSCAN_ERR_UNSUPPORTED, "desc.reserved must be 0");
   const int64_t i32max = std::numeric_limits<int32_t>::max();
-  if (desc->T > i32max || desc->D > i32max || desc->B > 65535)
-    return fail(SSCAN_ERR_UNSUPPORTED, "sizes beyond grid limits (B <= 65535, T and D < 2^31)");
+  // Kernels address one tile of a batch row with 32-bit byte offsets: D*DS <= 2^22 keeps
+  // every such offset (at most 64 steps of states) below 2^30.
+  if (desc->T > i32max || desc->D * desc->DS > (int64_t(1) << 22) || desc->B > 65535)
+    return fail(SSCAN_ERR_UNSUPPORTED, "sizes beyond addressing limits (B <= 65535, T < 2^31, D*DS <= 2^22)");
   r->B = desc->B;
   r->T = desc->T;
   r->D = desc->D;
@@ -142,6 +144,13 @@ BwdLayout bwd_layout(const Resolved& r, int lanes) {
   L.a_off = align_up((size_t)(L.ntiles_d * r.B * r.T * r.DS) * sizeof(float2), 256);
   L.total = align_up(L.a_off + (size_t)(r.B * r.D * r.DS) * sizeof(float), 256);
   return L;
+}
+
+// Channel tiles whose x / delta / y rows share one 128-byte line are kept on one XCD.
+int xcd_group(int lanes, size_t io_size) {
+  const int64_t seg = (int64_t)(kThreads / lanes) * (int64_t)io_size;  // bytes of a tile row
+  int64_t g = seg >= 128 ? 1 : 128 / seg;
+  return (int)(g > 8 ? 8 : g);
 }
 
 bool misaligned(const void* p, size_t a) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) % a) != 0; }
@@ -247,13 +256,17 @@ int sscan_fwd(const sscan_desc* desc, const sscan_plan* plan, const void* x, con
   p.chunks = chunks;
   p.chunk_len = (int32_t)ceil_div(r.T, chunks);
   const int64_t cpw = kThreads / lanes;
-  const unsigned ntiles_d = (unsigned)ceil_div(r.D, cpw);
+  const int64_t ntiles_d = ceil_div(r.D, cpw);
+  p.ntiles_d = (int32_t)ntiles_d;
+  p.xcd_group = xcd_group(lanes, r.io_size);
+  if (ntiles_d * r.B * chunks > std::numeric_limits<int32_t>::max())
+    return fail(SSCAN_ERR_UNSUPPORTED, "too many workgroups");
   hipError_t e;
   if (chunks > 1) {
     char* wsb = static_cast<char*>(ws);
     p.pairs = reinterpret_cast<float2*>(wsb + lay.pairs_off);
     p.hin = reinterpret_cast<const float*>(wsb + lay.hin_off);
-    e = sscan::launch_fwd(r.io, (int)r.DS, lanes, true, p, dim3(ntiles_d, (unsigned)r.B, (unsigned)(chunks - 1)), stream);
+    e = sscan::launch_fwd(r.io, (int)r.DS, lanes, true, p, (unsigned)(ntiles_d * r.B * (chunks - 1)), stream);
     if (e != hipSuccess) return hip_fail(e, "forward local pass");
     sscan::CarryParams cp{};
     cp.pairs = p.pairs;
@@ -264,7 +277,7 @@ int sscan_fwd(const sscan_desc* desc, const sscan_plan* plan, const void* x, con
     e = sscan::launch_carry(cp, stream);
     if (e != hipSuccess) return hip_fail(e, "chunk carry");
   }
-  e = sscan::launch_fwd(r.io, (int)r.DS, lanes, false, p, dim3(ntiles_d, (unsigned)r.B, (unsigned)chunks), stream);
+  e = sscan::launch_fwd(r.io, (int)r.DS, lanes, false, p, (unsigned)(ntiles_d * r.B * chunks), stream);
   if (e != hipSuccess) return hip_fail(e, "forward pass");
   return ok();
 }
@@ -321,7 +334,9 @@ int sscan_bwd(const sscan_desc* desc, const sscan_plan* plan, const void* dy, co
   p.x_bs = r.x_bs; p.bc_bs = r.bc_bs; p.y_bs = r.y_bs;
   p.B = (int32_t)r.B; p.T = (int32_t)r.T; p.D = (int32_t)r.D;
   p.ntiles_d = (int32_t)lay.ntiles_d;
-  hipError_t e = sscan::launch_bwd(r.io, (int)r.DS, lanes, p, dim3((unsigned)lay.ntiles_d, (unsigned)r.B, 1), stream);
+  p.xcd_group = xcd_group(lanes, r.io_size);
+  if (lay.ntiles_d * r.B > std::numeric_limits<int32_t>::max()) return fail(SSCAN_ERR_UNSUPPORTED, "too many workgroups");
+  hipError_t e = sscan::launch_bwd(r.io, (int)r.DS, lanes, p, (unsigned)(lay.ntiles_d * r.B), stream);
   if (e != hipSuccess) return hip_fail(e, "backward sweep");
   sscan::ReduceParams q{};
   q.part_bc = p.part_bc; q.part_A = p.part_A; q.gb = gb; q.gc = gc; q.gA = gA;

@@ -41,6 +41,8 @@ struct FwdParams {
   int32_t B, T, D;
   int32_t chunk_len;   // steps per chunk (T when there is a single chunk)
   int32_t chunks;      // number of chunks C
+  int32_t ntiles_d;    // channel tiles per batch row
+  int32_t xcd_group;   // consecutive channel tiles kept on one XCD
 };
 
 struct CarryParams {
@@ -71,6 +73,7 @@ struct BwdParams {
   int64_t y_bs;        // gx, gdelta
   int32_t B, T, D;
   int32_t ntiles_d;
+  int32_t xcd_group;
 };
 
 struct ReduceParams {
@@ -84,9 +87,9 @@ struct ReduceParams {
 };
 
 // Launchers (defined in the .hip translation units).  Each returns a hipError_t.
-hipError_t launch_fwd(int io, int DS, int lanes, bool local_pass, const FwdParams& p, dim3 grid, hipStream_t s);
+hipError_t launch_fwd(int io, int DS, int lanes, bool local_pass, const FwdParams& p, unsigned blocks, hipStream_t s);
 hipError_t launch_carry(const CarryParams& p, hipStream_t s);
-hipError_t launch_bwd(int io, int DS, int lanes, const BwdParams& p, dim3 grid, hipStream_t s);
+hipError_t launch_bwd(int io, int DS, int lanes, const BwdParams& p, unsigned blocks, hipStream_t s);
 hipError_t launch_bwd_reduce(const ReduceParams& p, hipStream_t s);
 hipError_t launch_fill(float* dst, int64_t n, hipStream_t s);                         // dst[i] = 0
 hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t s);  // src ? copy : zero
