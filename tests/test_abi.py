@@ -152,7 +152,7 @@ def test_empty_problems_need_no_pointers(lib):
 
 
 def test_plan_select_and_workspace_sizes(lib):
-    cases = {(16, 4096, 1024, 16): 4, (4, 2048, 2048, 16): 8, (8, 2048, 768, 16): 16, (1, 64, 16, 4): 4}
+    cases = {(16, 4096, 1024, 16): 8, (4, 2048, 2048, 16): 8, (8, 2048, 768, 16): 8, (1, 64, 16, 4): 4}
     for (B, T, D, DS), lanes in cases.items():
         d = desc(B=B, T=T, D=D, DS=DS)
         p = sscan_plan()
@@ -162,7 +162,9 @@ def test_plan_select_and_workspace_sizes(lib):
     d = desc(B=8, T=1024, D=256, DS=16)
     p = sscan_plan()
     assert lib.sscan_plan_select(ctypes.byref(d), 0, ctypes.byref(p)) == OK
-    assert p.lanes == 16 and p.chunks == 2
+    assert p.lanes == 8 and p.chunks == 4
+    assert lib.sscan_plan_select(ctypes.byref(d), 1, ctypes.byref(p)) == OK
+    assert p.lanes == 16 and p.chunks == 1
     # backward partial buffers: one (gb, gc) pair per channel tile, step and state, plus gA per batch row
     d = desc(B=8, T=2048, D=768, DS=16)
     n = ctypes.c_size_t()
