@@ -91,7 +91,7 @@ typedef struct sscan_desc {
 /* Launch plan.  Pass NULL wherever a plan is accepted to let the library choose. */
 typedef struct sscan_plan {
   int32_t lanes;       /* lanes sharing one channel's DS states: 1,2,4,8,16 and <= DS; 0 = choose */
-  int32_t chunks;      /* forward only: T-chunks of the in-kernel two-level scan; 1 = single pass, 0 = choose */
+  int32_t chunks;      /* T-chunks of the in-kernel two-level scan (forward) or sweep (backward); 1 = single pass, 0 = choose */
   int32_t reserved[6]; /* must be 0 */
 } sscan_plan;
 

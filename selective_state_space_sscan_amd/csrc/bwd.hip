@@ -35,11 +35,11 @@ __device__ __forceinline__ void load_k(const float* __restrict__ p, float (&v)[K
 }
 
 // Steps per batch: the decays of a batch are formed together, then the adjoint carry
-// runs through it, then the per-step gradient terms and their sums.  S*K <= 8 and at
-// least two batches per tile.
+// runs through it, then the per-step gradient terms and their sums.  S*K <= 4 (so three
+// waves fit on a SIMD) and at least two batches per tile.
 template <int K, int TB>
 __host__ __device__ constexpr int bwd_batch_steps() {
-  return (8 / K) < 1 ? 1 : ((8 / K) < (TB / 2) ? (8 / K) : (TB / 2));
+  return (4 / K) < 2 ? ((K == 1) ? 2 : 1) : ((4 / K) < (TB / 2) ? (4 / K) : (TB / 2));
 }
 
 // Reduce-scatter of per-lane values over the four 16-lane rows of a wave for a pair of
@@ -56,7 +56,7 @@ __device__ __forceinline__ float rows_reduce_scatter(float b0, float c0, float b
 }
 
 template <typename IO, int DS, int L>
-__global__ __launch_bounds__(kThreads) void bwd_kernel(const BwdParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 16 && L == 16 ? 3 : (DS / L >= 8 ? 1 : 2)))) void bwd_kernel(const BwdParams p) {
   constexpr int K = DS / L;
   constexpr int CPW = kThreads / L;
   constexpr int TB = bwd_tile_steps(L);
@@ -83,7 +83,9 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(const BwdParams p) {
 
   const int lin = xcd_grouped(blockIdx.x, gridDim.x, p.xcd_group);
   const int dtile = lin % p.ntiles_d;
-  const int bb = lin / p.ntiles_d;
+  const int rest = lin / p.ntiles_d;
+  const int bb = rest % p.B;
+  const int chunk = rest / p.B;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -94,8 +96,11 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(const BwdParams p) {
   const int d0 = dtile * CPW;
   const int D = p.D;
   const int T = p.T;
+  const int t_lo = chunk * p.chunk_len;           // this workgroup's steps: [t_lo, t_hi)
+  const int t_hi = min(T, t_lo + p.chunk_len);
   const int d = d0 + ch;
   const bool dvalid = d < D;
+  const int64_t nstate = (int64_t)p.B * D * DS;
 
   const IO* xrow = static_cast<const IO*>(p.x) + (int64_t)bb * p.x_bs;
   const IO* drow = static_cast<const IO*>(p.delta) + (int64_t)bb * p.x_bs;
@@ -114,13 +119,18 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(const BwdParams p) {
   for (int i = 0; i < K; ++i) { Av[i] = 0.f; G[i] = 0.f; gA[i] = 0.f; hcur[i] = 0.f; }
   if (dvalid) {
     load_k<K>(p.A + (int64_t)d * DS + j * K, Av);
-    if (p.dhT != nullptr) load_k<K>(p.dhT + soff, G);
-    if (T > 0) load_k<K>(Hrow + (int64_t)(T - 1) * D * DS + d * DS + j * K, hcur);
+    // the adjoint entering this chunk from the right: dhT for the last chunk, else the
+    // composed carry of the chunks after it
+    if (chunk < p.chunks - 1)
+      load_k<K>(p.gin + (int64_t)chunk * nstate + soff, G);
+    else if (p.dhT != nullptr)
+      load_k<K>(p.dhT + soff, G);
+    if (t_hi > t_lo) load_k<K>(Hrow + (int64_t)(t_hi - 1) * D * DS + d * DS + j * K, hcur);
   }
 #pragma unroll
   for (int i = 0; i < K; ++i) A2[i] = Av[i] * kLog2e;
 
-  const int ntiles = (T + TB - 1) / TB;
+  const int ntiles = t_hi > t_lo ? (t_hi - t_lo + TB - 1) / TB : 0;
 
   // ---- staged step inputs (one tile ahead) ----
   uint32_t xoff[PER];
@@ -138,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(const BwdParams p) {
   }
   float rx[PER], rd[PER], ry[PER], rb[PER_BC], rc[PER_BC];
   auto load_tile = [&](int ts) {
-    const int rows = min(TB, T - ts);
+    const int rows = min(TB, t_hi - ts);
     const rsrc_t rX = make_rsrc(xrow + (int64_t)ts * D, static_cast<uint32_t>(rows * D) * ES);
     const rsrc_t rD = make_rsrc(drow + (int64_t)ts * D, static_cast<uint32_t>(rows * D) * ES);
     const rsrc_t rY = make_rsrc(yrow + (int64_t)ts * D, static_cast<uint32_t>(rows * D) * ES);
@@ -173,26 +183,26 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(const BwdParams p) {
   // Entry r holds H_{tf+r-1}: h0 for step 0, and 0 for steps outside [1, T].
   float hbuf[2][HB][K];
   auto load_hblock = [&](float (&dst)[HB][K], int tf) {
-    const int t_lo = max(tf - 1, 0);
-    const int t_hi = min(tf - 1 + HB, T);  // exclusive
-    const rsrc_t rH = make_rsrc(Hrow + (int64_t)t_lo * D * DS, static_cast<uint32_t>(max(t_hi - t_lo, 0)) * hstep);
+    const int h_lo = max(tf - 1, 0);
+    const int h_hi = min(tf - 1 + HB, T);  // exclusive
+    const rsrc_t rH = make_rsrc(Hrow + (int64_t)h_lo * D * DS, static_cast<uint32_t>(max(h_hi - h_lo, 0)) * hstep);
 #pragma unroll
     for (int r = 0; r < HB; ++r) {
       const int tp = tf - 1 + r;
-      const uint32_t off = (tp >= 0) ? hlane + static_cast<uint32_t>(tp - t_lo) * hstep : kOutOfRange;
+      const uint32_t off = (tp >= 0) ? hlane + static_cast<uint32_t>(tp - h_lo) * hstep : kOutOfRange;
       buf_load_vec<K>(rH, off, dst[r]);
     }
     if (tf == 0 && p.h0 != nullptr && dvalid) load_k<K>(p.h0 + soff, dst[0]);
   };
 
   if (ntiles > 0) {
-    const int ts_last = (ntiles - 1) * TB;
+    const int ts_last = t_lo + (ntiles - 1) * TB;
     load_tile(ts_last);
     load_hblock(hbuf[0], ts_last + (NSUB - 1) * HB);
   }
 
   for (int it = ntiles - 1; it >= 0; --it) {
-    const int ts = it * TB;
+    const int ts = t_lo + it * TB;
     __syncthreads();  // previous tile's LDS users are done
     store_tile();
     __syncthreads();
@@ -286,7 +296,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(const BwdParams p) {
 
     __syncthreads();
     {
-      const int rows = min(TB, T - ts);
+      const int rows = min(TB, t_hi - ts);
       const rsrc_t rGX = make_rsrc(gxrow + (int64_t)ts * D, static_cast<uint32_t>(rows * D) * 4u);
       const rsrc_t rGD = make_rsrc(gdrow + (int64_t)ts * D, static_cast<uint32_t>(rows * D) * 4u);
 #pragma unroll
@@ -300,7 +310,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(const BwdParams p) {
 #pragma unroll
       for (int e = 0; e < PER_BC; ++e) {
         const int idx = tid + e * kThreads;
-        if (idx < BC && ts + idx / DS < T) {
+        if (idx < BC && ts + idx / DS < t_hi) {
           float sb = s_red[idx], sc = s_red[NWAVE * BC + idx];
 #pragma unroll
           for (int w = 1; w < NWAVE; ++w) {
@@ -314,18 +324,151 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(const BwdParams p) {
   }
 
   if (!dvalid) return;
-  float* pa = p.part_A + soff;
+  float* pa = p.part_A + (int64_t)chunk * nstate + soff;
 #pragma unroll
   for (int i = 0; i < K; ++i) pa[i] = gA[i];
-  if (p.gh0 != nullptr) {
+  if (p.gh0 != nullptr && chunk == 0) {
     float* g0 = p.gh0 + soff;
 #pragma unroll
     for (int i = 0; i < K; ++i) g0[i] = G[i];
   }
 }
 
+// Local pass of the two-level reverse sweep: chunk k (1..C-1) runs its steps from a zero
+// adjoint and records, per (b, d, n), its decay product exp(A * sum(delta)) and the carry
+// it hands to the chunk before it.  The carry map of a chunk is G -> P G + Gloc.
+template <typename IO, int DS, int L>
+__global__ __launch_bounds__(kThreads) void bwd_local_kernel(const BwdParams p) {
+  constexpr int K = DS / L;
+  constexpr int CPW = kThreads / L;
+  constexpr int TB = fwd_tile_steps(L);
+  constexpr int TILE = TB * CPW;
+  constexpr int PER = TILE / kThreads;
+  constexpr int BC = TB * DS;
+  constexpr int PER_BC = (BC + kThreads - 1) / kThreads;
+  constexpr int S = (16 / K) < 1 ? 1 : ((16 / K) < TB ? (16 / K) : TB);
+  constexpr uint32_t ES = sizeof(IO);
+  static_assert(TILE % kThreads == 0 && TB % S == 0, "tile shape");
+
+  __shared__ float2 s_dd[TILE];  // (delta, dy) at [step*CPW + channel]
+  __shared__ float s_c[BC];
+
+  const int lin = xcd_grouped(blockIdx.x, gridDim.x, p.xcd_group);
+  const int dtile = lin % p.ntiles_d;
+  const int rest = lin / p.ntiles_d;
+  const int bb = rest % p.B;
+  const int chunk = 1 + rest / p.B;
+
+  const int tid = threadIdx.x;
+  const int ch = tid / L;
+  const int j = tid % L;
+  const int d0 = dtile * CPW;
+  const int D = p.D;
+  const int t_lo = chunk * p.chunk_len;
+  const int t_hi = min(p.T, t_lo + p.chunk_len);
+  const int d = d0 + ch;
+  const bool dvalid = d < D;
+  const int64_t nstate = (int64_t)p.B * D * DS;
+  const int64_t soff = ((int64_t)bb * D + d) * DS + j * K;
+
+  const IO* drow = static_cast<const IO*>(p.delta) + (int64_t)bb * p.x_bs;
+  const IO* yrow = static_cast<const IO*>(p.dy) + (int64_t)bb * p.x_bs;
+  const IO* crow = static_cast<const IO*>(p.c) + (int64_t)bb * p.bc_bs;
+
+  float A2[K], G[K];
+  if (dvalid) {
+    load_k<K>(p.A + (int64_t)d * DS + j * K, A2);
+  } else {
+#pragma unroll
+    for (int i = 0; i < K; ++i) A2[i] = 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < K; ++i) { A2[i] *= kLog2e; G[i] = 0.f; }
+  double dsum = 0.0;
+
+  uint32_t xoff[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int idx = tid + e * kThreads;
+    const int dd = d0 + idx % CPW;
+    xoff[e] = dd < D ? static_cast<uint32_t>((idx / CPW) * D + dd) * ES : kOutOfRange;
+  }
+  uint32_t bcoff[PER_BC];
+#pragma unroll
+  for (int e = 0; e < PER_BC; ++e) {
+    const int idx = tid + e * kThreads;
+    bcoff[e] = idx < BC ? static_cast<uint32_t>(idx) * ES : kOutOfRange;
+  }
+  float rd[PER], ry[PER], rc[PER_BC];
+  auto load_tile = [&](int ts) {
+    const int rows = min(TB, t_hi - ts);
+    const rsrc_t rD = make_rsrc(drow + (int64_t)ts * D, static_cast<uint32_t>(rows * D) * ES);
+    const rsrc_t rY = make_rsrc(yrow + (int64_t)ts * D, static_cast<uint32_t>(rows * D) * ES);
+    const rsrc_t rC = make_rsrc(crow + (int64_t)ts * DS, static_cast<uint32_t>(rows * DS) * ES);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      rd[e] = buf_load_elem<IO>(rD, xoff[e]);
+      ry[e] = buf_load_elem<IO>(rY, xoff[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < PER_BC; ++e) rc[e] = buf_load_elem<IO>(rC, bcoff[e]);
+  };
+
+  const int ntiles = t_hi > t_lo ? (t_hi - t_lo + TB - 1) / TB : 0;
+  if (ntiles > 0) load_tile(t_lo + (ntiles - 1) * TB);
+  for (int it = ntiles - 1; it >= 0; --it) {
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < PER; ++e) s_dd[tid + e * kThreads] = make_float2(rd[e], ry[e]);
+#pragma unroll
+    for (int e = 0; e < PER_BC; ++e) {
+      const int idx = tid + e * kThreads;
+      if (BC % kThreads == 0 || idx < BC) s_c[idx] = rc[e];
+    }
+    __syncthreads();
+    if (it > 0) load_tile(t_lo + (it - 1) * TB);
+#pragma unroll 1
+    for (int s0 = TB - S; s0 >= 0; s0 -= S) {
+      float a[S][K];
+      float2 dd[S];
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        dd[s] = s_dd[(s0 + s) * CPW + ch];
+#pragma unroll
+        for (int i = 0; i < K; ++i) a[s][i] = exp2_hw(dd[s].x * A2[i]);
+      }
+#pragma unroll
+      for (int s = S - 1; s >= 0; --s) {
+        float cv[K];
+        lds_load_vec<K>(&s_c[(s0 + s) * DS + j * K], cv);
+#pragma unroll
+        for (int i = 0; i < K; ++i) G[i] = a[s][i] * fmaf(dd[s].y, cv[i], G[i]);
+        dsum += dd[s].x;
+      }
+    }
+  }
+  if (!dvalid) return;
+  float2* pr = p.pairs + (int64_t)(chunk - 1) * nstate + soff;
+#pragma unroll
+  for (int i = 0; i < K; ++i)
+    pr[i] = make_float2(exp2_hw(static_cast<float>(static_cast<double>(A2[i]) * dsum)), G[i]);
+}
+
+// Right-to-left composition of the chunk carry maps: gin[k] is the adjoint entering chunk
+// k from the right (chunk C-1 receives dhT).
+__global__ __launch_bounds__(kThreads) void bwd_carry_kernel(const BwdCarryParams p) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= p.n) return;
+  float G = p.dhT != nullptr ? p.dhT[i] : 0.f;
+  for (int k = p.chunks - 1; k >= 1; --k) {
+    const float2 pr = p.pairs[(int64_t)(k - 1) * p.n + i];
+    G = fmaf(pr.x, G, pr.y);
+    p.gin[(int64_t)(k - 1) * p.n + i] = G;
+  }
+}
+
 // gb, gc: add the per-workgroup partials over channel tiles in ascending tile order.
-// gA: add the per-batch-row partials in ascending batch order.
+// gA: add the per-(chunk, batch row) partials in ascending order.
 __global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(const ReduceParams p) {
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   const int64_t nbc = (int64_t)p.B * p.T * p.DS;
@@ -345,47 +488,56 @@ __global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(const ReduceParams
   } else if (i < nbc + nA) {
     const int64_t e = i - nbc;
     float s = 0.f;
-    for (int bb = 0; bb < p.B; ++bb) s += p.part_A[(int64_t)bb * nA + e];
+    for (int k = 0; k < p.chunks * p.B; ++k) s += p.part_A[(int64_t)k * nA + e];
     p.gA[e] = s;
   }
 }
 
 template <typename IO, int DS, int L>
-hipError_t launch_bwd_t(const BwdParams& p, unsigned blocks, hipStream_t s) {
-  hipLaunchKernelGGL((bwd_kernel<IO, DS, L>), dim3(blocks), dim3(kThreads), 0, s, p);
+hipError_t launch_bwd_t(bool local_pass, const BwdParams& p, unsigned blocks, hipStream_t s) {
+  if (local_pass)
+    hipLaunchKernelGGL((bwd_local_kernel<IO, DS, L>), dim3(blocks), dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((bwd_kernel<IO, DS, L>), dim3(blocks), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
 template <typename IO, int DS>
-hipError_t launch_bwd_ds(int lanes, const BwdParams& p, unsigned grid, hipStream_t s) {
+hipError_t launch_bwd_ds(int lanes, bool local_pass, const BwdParams& p, unsigned grid, hipStream_t s) {
   switch (lanes) {
-    case 1: return launch_bwd_t<IO, DS, 1>(p, grid, s);
-    case 2: if constexpr (DS >= 2) return launch_bwd_t<IO, DS, 2>(p, grid, s); break;
-    case 4: if constexpr (DS >= 4) return launch_bwd_t<IO, DS, 4>(p, grid, s); break;
-    case 8: if constexpr (DS >= 8) return launch_bwd_t<IO, DS, 8>(p, grid, s); break;
-    case 16: if constexpr (DS >= 16) return launch_bwd_t<IO, DS, 16>(p, grid, s); break;
+    case 1: return launch_bwd_t<IO, DS, 1>(local_pass, p, grid, s);
+    case 2: if constexpr (DS >= 2) return launch_bwd_t<IO, DS, 2>(local_pass, p, grid, s); break;
+    case 4: if constexpr (DS >= 4) return launch_bwd_t<IO, DS, 4>(local_pass, p, grid, s); break;
+    case 8: if constexpr (DS >= 8) return launch_bwd_t<IO, DS, 8>(local_pass, p, grid, s); break;
+    case 16: if constexpr (DS >= 16) return launch_bwd_t<IO, DS, 16>(local_pass, p, grid, s); break;
     default: break;
   }
   return hipErrorInvalidValue;
 }
 
 template <typename IO>
-hipError_t launch_bwd_io(int DS, int lanes, const BwdParams& p, unsigned grid, hipStream_t s) {
+hipError_t launch_bwd_io(int DS, int lanes, bool local_pass, const BwdParams& p, unsigned grid, hipStream_t s) {
   switch (DS) {
-    case 1: return launch_bwd_ds<IO, 1>(lanes, p, grid, s);
-    case 2: return launch_bwd_ds<IO, 2>(lanes, p, grid, s);
-    case 4: return launch_bwd_ds<IO, 4>(lanes, p, grid, s);
-    case 8: return launch_bwd_ds<IO, 8>(lanes, p, grid, s);
-    case 16: return launch_bwd_ds<IO, 16>(lanes, p, grid, s);
+    case 1: return launch_bwd_ds<IO, 1>(lanes, local_pass, p, grid, s);
+    case 2: return launch_bwd_ds<IO, 2>(lanes, local_pass, p, grid, s);
+    case 4: return launch_bwd_ds<IO, 4>(lanes, local_pass, p, grid, s);
+    case 8: return launch_bwd_ds<IO, 8>(lanes, local_pass, p, grid, s);
+    case 16: return launch_bwd_ds<IO, 16>(lanes, local_pass, p, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_bwd(int io, int DS, int lanes, const BwdParams& p, unsigned grid, hipStream_t s) {
-  if (io == 0) return launch_bwd_io<float>(DS, lanes, p, grid, s);
-  return launch_bwd_io<bf16_t>(DS, lanes, p, grid, s);
+hipError_t launch_bwd(int io, int DS, int lanes, bool local_pass, const BwdParams& p, unsigned grid, hipStream_t s) {
+  if (io == 0) return launch_bwd_io<float>(DS, lanes, local_pass, p, grid, s);
+  return launch_bwd_io<bf16_t>(DS, lanes, local_pass, p, grid, s);
+}
+
+hipError_t launch_bwd_carry(const BwdCarryParams& p, hipStream_t s) {
+  const int64_t blocks = (p.n + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(bwd_carry_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_bwd_reduce(const ReduceParams& p, hipStream_t s) {

@@ -90,14 +90,32 @@ int resolve_plan(const Resolved& r, const sscan_plan* plan, bool backward, int* 
       return fail(SSCAN_ERR_UNSUPPORTED, "plan.lanes=%d must be a power of two <= min(DS,16)", plan->lanes);
     if (plan->chunks < 0 || plan->chunks > 65535)
       return fail(SSCAN_ERR_UNSUPPORTED, "plan.chunks=%d out of range", plan->chunks);
-    if (backward && plan->chunks > 1) return fail(SSCAN_ERR_UNSUPPORTED, "the backward runs a single pass");
   }
   // Measured on MI355X: the forward runs best with 8 lanes per channel (two states per
   // lane) on every size tried, the backward with one state per lane.
   int l = (plan != nullptr && plan->lanes != 0) ? plan->lanes
                                                 : (backward ? pick_lanes(r, 98304) : (int)(r.DS < 8 ? r.DS : 8));
   int c = 1;
-  if (!backward) {
+  if (backward) {
+    if (plan != nullptr && plan->chunks != 0) {
+      c = plan->chunks;
+    } else {
+      // Split the reverse sweep until there are three waves per SIMD (one state per lane
+      // leaves 1.5 at 8x2048x768x16, and half the SIMDs would run two); every chunk keeps
+      // at least four tiles.
+      const int64_t lanes_total = r.B * r.D * l;
+      const int64_t tb = sscan::bwd_tile_steps(l);
+      if (lanes_total > 0 && lanes_total < 3 * kLanesOneWavePerSimd) {
+        int64_t want = ceil_div(3 * kLanesOneWavePerSimd, lanes_total);
+        int64_t cap = r.T / (4 * tb);
+        if (want > cap) want = cap;
+        if (want > 16) want = 16;
+        if (want > 1) c = (int)want;
+      }
+    }
+    if (r.T > 0 && c > r.T) c = (int)r.T;
+    if (c < 1) c = 1;
+  } else {
     if (plan != nullptr && plan->chunks != 0) {
       c = plan->chunks;
     } else {
@@ -135,17 +153,24 @@ FwdLayout fwd_layout(const Resolved& r, int chunks) {
 }
 
 struct BwdLayout {
-  size_t bc_off, a_off, total;
-  int64_t ntiles_d;
+  size_t bc_off, a_off, pairs_off, gin_off, total;
+  int64_t ntiles_d, chunk_len, chunks;
 };
 
-BwdLayout bwd_layout(const Resolved& r, int lanes) {
-  BwdLayout L{0, 0, 0, 0};
+// Chunks of the reverse sweep are whole tiles long; the last one takes the remainder.
+BwdLayout bwd_layout(const Resolved& r, int lanes, int chunks) {
+  BwdLayout L{};
   const int64_t cpw = kThreads / lanes;
+  const int64_t tb = sscan::bwd_tile_steps(lanes);
   L.ntiles_d = ceil_div(r.D, cpw);
+  L.chunk_len = r.T > 0 ? ceil_div(ceil_div(r.T, chunks), tb) * tb : tb;
+  L.chunks = r.T > 0 ? ceil_div(r.T, L.chunk_len) : 1;
+  const size_t nstate = (size_t)(r.B * r.D * r.DS);
   L.bc_off = 0;
   L.a_off = align_up((size_t)(L.ntiles_d * r.B * r.T * r.DS) * sizeof(float2), 256);
-  L.total = align_up(L.a_off + (size_t)(r.B * r.D * r.DS) * sizeof(float), 256);
+  L.pairs_off = align_up(L.a_off + (size_t)L.chunks * nstate * sizeof(float), 256);
+  L.gin_off = align_up(L.pairs_off + (size_t)(L.chunks - 1) * nstate * sizeof(float2), 256);
+  L.total = align_up(L.gin_off + (size_t)(L.chunks - 1) * nstate * sizeof(float), 256);
   return L;
 }
 
@@ -218,7 +243,7 @@ int sscan_bwd_workspace(const sscan_desc* desc, const sscan_plan* plan, size_t* 
   int lanes, chunks;
   st = resolve_plan(r, plan, true, &lanes, &chunks);
   if (st != SSCAN_OK) return st;
-  *bytes = (r.B == 0 || r.D == 0 || r.T == 0) ? 0 : bwd_layout(r, lanes).total;
+  *bytes = (r.B == 0 || r.D == 0 || r.T == 0) ? 0 : bwd_layout(r, lanes, chunks).total;
   return ok();
 }
 
@@ -323,7 +348,7 @@ int sscan_bwd(const sscan_desc* desc, const sscan_plan* plan, const void* dy, co
     return e == hipSuccess ? ok() : hip_fail(e, "backward without steps");
   }
 
-  const BwdLayout lay = bwd_layout(r, lanes);
+  const BwdLayout lay = bwd_layout(r, lanes, chunks);
   if (ws == nullptr || ws_bytes < lay.total)
     return fail(SSCAN_ERR_WORKSPACE, "backward needs %zu workspace bytes, got %zu", lay.total, ws_bytes);
   if (misaligned(ws, 16)) return fail(SSCAN_ERR_ALIGN, "workspace must be 16-byte aligned");
@@ -334,16 +359,34 @@ int sscan_bwd(const sscan_desc* desc, const sscan_plan* plan, const void* dy, co
   p.gx = gx; p.gdelta = gdelta; p.gh0 = gh0;
   p.part_bc = reinterpret_cast<float2*>(wsb + lay.bc_off);
   p.part_A = reinterpret_cast<float*>(wsb + lay.a_off);
+  p.pairs = reinterpret_cast<float2*>(wsb + lay.pairs_off);
+  p.gin = reinterpret_cast<const float*>(wsb + lay.gin_off);
+  p.chunk_len = (int32_t)lay.chunk_len;
+  p.chunks = (int32_t)lay.chunks;
   p.x_bs = r.x_bs; p.bc_bs = r.bc_bs; p.y_bs = r.y_bs;
   p.B = (int32_t)r.B; p.T = (int32_t)r.T; p.D = (int32_t)r.D;
   p.ntiles_d = (int32_t)lay.ntiles_d;
   p.xcd_group = xcd_group(lanes, r.io_size);
-  if (lay.ntiles_d * r.B > std::numeric_limits<int32_t>::max()) return fail(SSCAN_ERR_UNSUPPORTED, "too many workgroups");
-  hipError_t e = sscan::launch_bwd(r.io, (int)r.DS, lanes, p, (unsigned)(lay.ntiles_d * r.B), stream);
+  if (lay.ntiles_d * r.B * lay.chunks > std::numeric_limits<int32_t>::max())
+    return fail(SSCAN_ERR_UNSUPPORTED, "too many workgroups");
+  hipError_t e;
+  if (lay.chunks > 1) {
+    e = sscan::launch_bwd(r.io, (int)r.DS, lanes, true, p, (unsigned)(lay.ntiles_d * r.B * (lay.chunks - 1)), stream);
+    if (e != hipSuccess) return hip_fail(e, "backward local pass");
+    sscan::BwdCarryParams cp{};
+    cp.pairs = p.pairs;
+    cp.dhT = dhT;
+    cp.gin = reinterpret_cast<float*>(wsb + lay.gin_off);
+    cp.n = r.B * r.D * r.DS;
+    cp.chunks = (int32_t)lay.chunks;
+    e = sscan::launch_bwd_carry(cp, stream);
+    if (e != hipSuccess) return hip_fail(e, "backward chunk carry");
+  }
+  e = sscan::launch_bwd(r.io, (int)r.DS, lanes, false, p, (unsigned)(lay.ntiles_d * r.B * lay.chunks), stream);
   if (e != hipSuccess) return hip_fail(e, "backward sweep");
   sscan::ReduceParams q{};
   q.part_bc = p.part_bc; q.part_A = p.part_A; q.gb = gb; q.gc = gc; q.gA = gA;
-  q.B = p.B; q.T = p.T; q.D = p.D; q.DS = (int32_t)r.DS; q.ntiles_d = p.ntiles_d;
+  q.B = p.B; q.T = p.T; q.D = p.D; q.DS = (int32_t)r.DS; q.ntiles_d = p.ntiles_d; q.chunks = p.chunks;
   e = sscan::launch_bwd_reduce(q, stream);
   if (e != hipSuccess) return hip_fail(e, "backward reduce");
   return ok();

@@ -67,13 +67,25 @@ struct BwdParams {
   float* gdelta;
   float* gh0;          // may be null
   float2* part_bc;     // (ntiles_d, B, T, DS): per-workgroup (gb, gc) partial sums
-  float* part_A;       // (B, D, DS): per-batch-row gA partial sums
+  float* part_A;       // (chunks, B, D, DS): per-(chunk, batch row) gA partial sums
+  float2* pairs;       // two-level sweep: (decay product, local carry) of chunks 1..C-1, (C-1,B,D,DS)
+  const float* gin;    // two-level sweep: carry entering chunks 0..C-2 from the right, (C-1,B,D,DS)
   int64_t x_bs;        // x, delta, dy
   int64_t bc_bs;       // b, c
   int64_t y_bs;        // gx, gdelta
   int32_t B, T, D;
   int32_t ntiles_d;
   int32_t xcd_group;
+  int32_t chunk_len;   // steps per chunk, a multiple of the tile
+  int32_t chunks;
+};
+
+struct BwdCarryParams {
+  const float2* pairs;  // (C-1,B,D,DS)
+  const float* dhT;     // may be null
+  float* gin;           // (C-1,B,D,DS)
+  int64_t n;            // B*D*DS
+  int32_t chunks;
 };
 
 struct ReduceParams {
@@ -84,12 +96,14 @@ struct ReduceParams {
   float* gA;
   int32_t B, T, D, DS;
   int32_t ntiles_d;
+  int32_t chunks;
 };
 
 // Launchers (defined in the .hip translation units).  Each returns a hipError_t.
 hipError_t launch_fwd(int io, int DS, int lanes, bool local_pass, const FwdParams& p, unsigned blocks, hipStream_t s);
 hipError_t launch_carry(const CarryParams& p, hipStream_t s);
-hipError_t launch_bwd(int io, int DS, int lanes, const BwdParams& p, unsigned blocks, hipStream_t s);
+hipError_t launch_bwd(int io, int DS, int lanes, bool local_pass, const BwdParams& p, unsigned blocks, hipStream_t s);
+hipError_t launch_bwd_carry(const BwdCarryParams& p, hipStream_t s);
 hipError_t launch_bwd_reduce(const ReduceParams& p, hipStream_t s);
 hipError_t launch_fill(float* dst, int64_t n, hipStream_t s);                         // dst[i] = 0
 hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t s);  // src ? copy : zero

@@ -138,9 +138,21 @@ def test_backward_validation(lib):
     assert bwd(lib, desc(), gx=FAKE + 2) == E_ALIGN
     assert bwd(lib, desc()) == E_WS  # workspace is always needed when there are steps
     p = sscan_plan()
-    p.chunks = 2
+    p.chunks = -2
     d = desc()
     assert lib.sscan_bwd(ctypes.byref(d), ctypes.byref(p), *([None] * 15), None, ctypes.c_size_t(0), None) == E_UNSUP
+
+
+def test_backward_chunked_workspace_grows_with_chunks(lib):
+    d = desc(B=2, T=1000, D=64, DS=16)
+    sizes = []
+    for c in (1, 2, 4):
+        p = sscan_plan()
+        p.lanes, p.chunks = 16, c
+        n = ctypes.c_size_t()
+        assert lib.sscan_bwd_workspace(ctypes.byref(d), ctypes.byref(p), ctypes.byref(n)) == OK
+        sizes.append(n.value)
+    assert sizes[0] < sizes[1] < sizes[2]
 
 
 def test_empty_problems_need_no_pointers(lib):
@@ -164,7 +176,10 @@ def test_plan_select_and_workspace_sizes(lib):
     assert lib.sscan_plan_select(ctypes.byref(d), 0, ctypes.byref(p)) == OK
     assert p.lanes == 8 and p.chunks == 4
     assert lib.sscan_plan_select(ctypes.byref(d), 1, ctypes.byref(p)) == OK
-    assert p.lanes == 16 and p.chunks == 1
+    assert p.lanes == 16 and p.chunks == 6  # 2048 channels x 16 lanes x 6 chunks = 3 waves per SIMD
+    d = desc(B=8, T=2048, D=768, DS=16)
+    assert lib.sscan_plan_select(ctypes.byref(d), 1, ctypes.byref(p)) == OK
+    assert p.lanes == 16 and p.chunks == 2  # 1.5 -> 3 waves per SIMD
     # backward partial buffers: one (gb, gc) pair per channel tile, step and state, plus gA per batch row
     d = desc(B=8, T=2048, D=768, DS=16)
     n = ctypes.c_size_t()

@@ -116,6 +116,36 @@ def test_backward_small_shapes(gpu, B, T, D, DS, io, h0, dhT, lanes):
         assert_close(name, a, r, TOL_F32)
 
 
+CHUNKED_BWD = [
+    # B, T, D, DS, io, h0, dhT, lanes, chunks
+    (2, 300, 40, 16, "f32", True, True, 16, 2),
+    (2, 300, 40, 16, "f32", True, False, 16, 3),
+    (1, 1000, 33, 16, "f32", False, True, 16, 5),
+    (2, 257, 70, 8, "f32", True, True, 8, 2),
+    (2, 513, 20, 4, "bf16", True, True, 4, 4),
+    (1, 128, 16, 16, "f32", True, True, 16, 4),
+]
+
+
+@pytest.mark.parametrize("B,T,D,DS,io,h0,dhT,lanes,chunks", CHUNKED_BWD)
+def test_backward_chunked_sweep(gpu, B, T, D, DS, io, h0, dhT, lanes, chunks):
+    announce(f"chunked bwd B={B} T={T} D={D} DS={DS} io={io} h0={h0} dhT={dhT} plan=({lanes},{chunks})")
+    w = workloads.custom(B, T, D, DS, io=io, seed=11 + T + D, h0_std=0.3 if h0 else 0.0, delta_mu=-1.0,
+                         with_dy=True, with_dhT=dhT)
+    inp = workloads.make_inputs(w)
+    g = to_dev(inp, gpu)
+    y, hT, H = run_fwd(g, return_H=True)
+    grads = sscan_bwd(g["dy"], g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"], H, g["dhT"],
+                      plan=Plan(lanes, chunks))
+    ref = oracle.bwd(inp["dy"], inp["x"], inp["delta"], inp["A"], inp["b"], inp["c"], inp["h0"], inp["dhT"])
+    for name, a, r in zip(["gx", "gdelta", "gb", "gc", "gA", "gh0"], grads, ref):
+        assert_close(name, a, r, TOL_F32)
+    single = sscan_bwd(g["dy"], g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"], H, g["dhT"],
+                       plan=Plan(lanes, 1))
+    for name, a, r in zip(["gx", "gdelta", "gb", "gc", "gA", "gh0"], grads, single):
+        assert rel_err(a, r) < 1e-5, name
+
+
 def test_zero_delta_keeps_state_bitwise(gpu):
     announce("delta=0: hT == h0 bitwise")
     w = workloads.custom(2, 50, 40, 16, seed=3, h0_std=0.5)
@@ -165,6 +195,41 @@ def test_split_calls_carry_the_state(gpu):
     # and against the GPU's own single call: identical up to fp32 rounding of the state
     y1, h1 = run_fwd(g, plan=Plan(0, 1))
     assert rel_err(h, h1) < 1e-6
+
+
+def test_split_calls_backward_chains_dhT(gpu):
+    """A sequence split over three forward calls is back-propagated call by call, last
+    call first, each call's gh0 becoming the previous call's dhT; the result equals the
+    backward of one unsplit call."""
+    announce("split-call backward: gh0 -> dhT across 3 calls, 2x300x40x16 fp32")
+    w = workloads.custom(2, 300, 40, 16, seed=13, h0_std=0.2, with_dy=True, with_dhT=True)
+    inp = workloads.make_inputs(w)
+    g = to_dev(inp, gpu)
+    bounds = [(0, 90), (90, 91), (91, 300)]
+    hs, Hs = [g["h0"]], []
+    for t0, t1 in bounds:
+        sl = slice(t0, t1)
+        _, hT, H = sscan_fwd(g["x"][:, sl], g["delta"][:, sl], g["A"], g["b"][:, sl], g["c"][:, sl], hs[-1],
+                             return_H=True)
+        hs.append(hT)
+        Hs.append(H)
+    dhT = g["dhT"]
+    gx = torch.empty_like(g["x"])
+    gd = torch.empty_like(g["x"])
+    gb = torch.empty_like(g["b"])
+    gc = torch.empty_like(g["c"])
+    gA = torch.zeros_like(g["A"])
+    for k in reversed(range(len(bounds))):
+        t0, t1 = bounds[k]
+        sl = slice(t0, t1)
+        r = sscan_bwd(g["dy"][:, sl], g["x"][:, sl], g["delta"][:, sl], g["A"], g["b"][:, sl], g["c"][:, sl],
+                      hs[k], Hs[k], dhT)
+        gx[:, sl], gd[:, sl], gb[:, sl], gc[:, sl] = r[0], r[1], r[2], r[3]
+        gA += r[4]
+        dhT = r[5]
+    ref = oracle.bwd(inp["dy"], inp["x"], inp["delta"], inp["A"], inp["b"], inp["c"], inp["h0"], inp["dhT"])
+    for name, a, r in zip(["gx", "gdelta", "gb", "gc", "gA", "gh0"], [gx, gd, gb, gc, gA, dhT], ref):
+        assert_close(name, a, r, TOL_F32)
 
 
 def test_backward_is_bitwise_reproducible(gpu):
