@@ -55,6 +55,39 @@ __device__ __forceinline__ float rows_reduce_scatter(float b0, float c0, float b
   return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
+// DPP pattern that pairs each lane with one whose lane-index bit M differs and whose
+// higher bits agree (M = 1, 2, 4, 8).
+template <int M>
+__host__ __device__ constexpr int pair_ctrl() {
+  return M == 8 ? kDppRowMirror : (M == 4 ? kDppRowHalfMirror : (M == 2 ? kDppQuadXor2 : kDppQuadXor1));
+}
+
+// Reduce-scatter over a group of 2M lanes (group index j): on entry every lane holds C
+// live values v[0..C); each stage halves the live values, keeping the half selected by
+// bit M of j and adding the partner's copy of it.  On exit lane j holds group totals of
+// max(1, C/2M) consecutive items starting at idx0; once a single value is left the
+// remaining stages are plain all-reduce steps.  Every stage's adds are independent.
+template <int M, int C, int V>
+__device__ __forceinline__ void reduce_scatter(float (&v)[V], int j, int& idx0) {
+  if constexpr (M >= 1) {
+    if constexpr (C >= 2) {
+      constexpr int H = C / 2;
+      const bool up = (j & M) != 0;
+#pragma unroll
+      for (int q = 0; q < H; ++q) {
+        const float keep = up ? v[q + H] : v[q];
+        const float send = up ? v[q] : v[q + H];
+        v[q] = keep + dpp<pair_ctrl<M>()>(send);
+      }
+      if (up) idx0 += H;
+      reduce_scatter<M / 2, H, V>(v, j, idx0);
+    } else {
+      v[0] += dpp<pair_ctrl<M>()>(v[0]);
+      reduce_scatter<M / 2, 1, V>(v, j, idx0);
+    }
+  }
+}
+
 template <typename IO, int DS, int L>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 16 && L == 16 ? 3 : (DS / L >= 8 ? 1 : 2)))) void bwd_kernel(const BwdParams p) {
   constexpr int K = DS / L;
@@ -147,8 +180,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
     bcoff[e] = idx < BC ? static_cast<uint32_t>(idx) * ES : kOutOfRange;
   }
   float rx[PER], rd[PER], ry[PER], rb[PER_BC], rc[PER_BC];
+  // Every prefetch below is issued unconditionally, with an empty resource (all loads
+  // return 0) where there is nothing to fetch: a load issued on one path only makes the
+  // compiler's wait for older loads path-dependent, and it then waits for everything.
   auto load_tile = [&](int ts) {
-    const int rows = min(TB, t_hi - ts);
+    const int rows = ts >= t_lo ? tile_rows(t_hi, ts, TB) : 0;
     const rsrc_t rX = make_rsrc(xrow + (int64_t)ts * D, static_cast<uint32_t>(rows * D) * ES);
     const rsrc_t rD = make_rsrc(drow + (int64_t)ts * D, static_cast<uint32_t>(rows * D) * ES);
     const rsrc_t rY = make_rsrc(yrow + (int64_t)ts * D, static_cast<uint32_t>(rows * D) * ES);
@@ -167,6 +203,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
     }
   };
   auto store_tile = [&]() {
+    // keep the scheduler from hoisting the delta*x products (and with them the wait for
+    // the loads) into the step code that runs while the loads are still in flight
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int e = 0; e < PER; ++e) s_in[tid + e * kThreads] = make_float4(rd[e], rx[e], ry[e], rd[e] * rx[e]);
 #pragma unroll
@@ -180,44 +219,52 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
   };
 
   // ---- H_{t-1} for a block of HB steps starting at step tf, prefetched a block ahead ----
-  // Entry r holds H_{tf+r-1}: h0 for step 0, and 0 for steps outside [1, T].
+  // Entry r holds H_{tf+r-1}, and 0 for steps outside [1, T] or when the block is not
+  // valid; step 0 takes h0 from registers instead (loaded once, below).  The loaded
+  // registers are used as they are, so that nothing waits for a prefetch before the
+  // block it belongs to is reached.
   float hbuf[2][HB][K];
-  auto load_hblock = [&](float (&dst)[HB][K], int tf) {
+  float hzero[K];
+#pragma unroll
+  for (int i = 0; i < K; ++i) hzero[i] = 0.f;
+  if (chunk == 0 && p.h0 != nullptr && dvalid) load_k<K>(p.h0 + soff, hzero);
+  auto load_hblock = [&](float (&dst)[HB][K], int tf, bool valid) {
     const int h_lo = max(tf - 1, 0);
     const int h_hi = min(tf - 1 + HB, T);  // exclusive
-    const rsrc_t rH = make_rsrc(Hrow + (int64_t)h_lo * D * DS, static_cast<uint32_t>(max(h_hi - h_lo, 0)) * hstep);
+    const uint32_t nrow = valid ? static_cast<uint32_t>(max(h_hi - h_lo, 0)) : 0u;
+    const rsrc_t rH = make_rsrc(Hrow + (int64_t)h_lo * D * DS, nrow * hstep);
 #pragma unroll
     for (int r = 0; r < HB; ++r) {
       const int tp = tf - 1 + r;
       const uint32_t off = (tp >= 0) ? hlane + static_cast<uint32_t>(tp - h_lo) * hstep : kOutOfRange;
       buf_load_vec<K>(rH, off, dst[r]);
     }
-    if (tf == 0 && p.h0 != nullptr && dvalid) load_k<K>(p.h0 + soff, dst[0]);
   };
 
   if (ntiles > 0) {
     const int ts_last = t_lo + (ntiles - 1) * TB;
     load_tile(ts_last);
-    load_hblock(hbuf[0], ts_last + (NSUB - 1) * HB);
+    load_hblock(hbuf[0], ts_last + (NSUB - 1) * HB, true);
+    store_tile();
   }
 
+  // As in the forward, each tile issues the loads of the tile before it first and parks
+  // them in LDS only after its own steps, so that no loaded tile register is live across
+  // the loop back-edge (the wait for it would otherwise cover every later load).
   for (int it = ntiles - 1; it >= 0; --it) {
     const int ts = t_lo + it * TB;
-    __syncthreads();  // previous tile's LDS users are done
-    store_tile();
-    __syncthreads();
-    if (it > 0) load_tile(ts - TB);
+    __syncthreads();  // this tile's inputs are in LDS; the previous tile's output reads are done
+    load_tile(ts - TB);
 
 #pragma unroll
     for (int sb = NSUB - 1; sb >= 0; --sb) {
       // An even number of H blocks precede each tile, so buffer roles depend only on sb.
       float (&cur)[HB][K] = hbuf[(NSUB - 1 - sb) & 1];
       float (&nxt)[HB][K] = hbuf[((NSUB - 1 - sb) & 1) ^ 1];
-      if (sb > 0) {
-        load_hblock(nxt, ts + (sb - 1) * HB);
-      } else if (it > 0) {
-        load_hblock(nxt, ts - TB + (NSUB - 1) * HB);
-      }
+      if (sb > 0)
+        load_hblock(nxt, ts + (sb - 1) * HB, true);
+      else
+        load_hblock(nxt, ts - TB + (NSUB - 1) * HB, it > 0);
 
 #pragma unroll
       for (int bt = NBAT - 1; bt >= 0; --bt) {
@@ -248,7 +295,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
         for (int s = 0; s < S; ++s) {
           float bv[K];
           lds_load_vec<K>(&s_b[(tt0 + s) * DS + j * K], bv);
-          const float(&hp)[K] = cur[bt * S + s];                          // H_{t-1}
+          float hp[K];                                                     // H_{t-1}
+#pragma unroll
+          for (int i = 0; i < K; ++i) hp[i] = cur[bt * S + s][i];
+          if (bt == 0 && s == 0) {
+            const bool first = ts + sb * HB == 0;  // step 0 of the sequence: H_{-1} = h0
+#pragma unroll
+            for (int i = 0; i < K; ++i) hp[i] = first ? hzero[i] : hp[i];
+          }
           const float(&ht)[K] = (s == S - 1) ? hcur : cur[bt * S + s + 1];  // H_t
           float sl = 0.f, gd = 0.f;
 #pragma unroll
@@ -265,12 +319,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
         }
 #pragma unroll
         for (int i = 0; i < K; ++i) hcur[i] = cur[bt * S][i];
-        // phase D: sums over each channel's states -> gx, gdelta
+        // phase D: sums over each channel's states -> gx, gdelta.  The (Sl, gdl) pairs of
+        // the whole batch are reduce-scattered over the channel's lanes, so that the
+        // stages carry independent adds instead of one dependent chain per step.
+        {
+          constexpr int V = 2 * S;
+          constexpr int CF = V / L > 1 ? V / L : 1;  // items each lane finishes
+          float red[V];
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-          const float st = group_sum<L>(Sl[s]);
-          const float gt = group_sum<L>(gdl[s]);
-          s_gxd[(tt0 + s) * CPW + ch] = make_float2(in[s].x * st, fmaf(in[s].y, st, gt));
+          for (int s = 0; s < S; ++s) { red[2 * s] = Sl[s]; red[2 * s + 1] = gdl[s]; }
+          int idx0 = 0;
+          if constexpr (L > 1) reduce_scatter<L / 2, V, V>(red, j, idx0);
+          if constexpr (CF == 1) {
+            // lanes that differ only in the bits below MP hold the same item; the lane
+            // across bit MP holds the other half of the step's pair
+            constexpr int MP = L / V;
+            const float other = dpp<pair_ctrl<MP>()>(red[0]);
+            const bool second = (idx0 & 1) != 0;
+            if (!second && (j & (MP - 1)) == 0) {
+              const int tr = (tt0 + (idx0 >> 1)) * CPW + ch;
+              const float4 v = s_in[tr];
+              s_gxd[tr] = make_float2(v.x * red[0], fmaf(v.y, red[0], other));
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < CF / 2; ++r) {
+              const int tr = (tt0 + (idx0 >> 1) + r) * CPW + ch;
+              const float4 v = s_in[tr];
+              s_gxd[tr] = make_float2(v.x * red[2 * r], fmaf(v.y, red[2 * r], red[2 * r + 1]));
+            }
+          }
         }
         // phase E: sums over the channels of the wave -> one (gb, gc) slot per wave
 #pragma unroll
@@ -306,21 +384,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v.x), rGX, off, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v.y), rGD, off, 0, 0);
       }
-      float2* __restrict__ part = p.part_bc + ((int64_t)dtile * p.B + bb) * T * DS + (int64_t)ts * DS;
+      const rsrc_t rP = make_rsrc(p.part_bc + ((int64_t)dtile * p.B + bb) * T * DS + (int64_t)ts * DS,
+                                  static_cast<uint32_t>(rows * DS) * 8u);
 #pragma unroll
       for (int e = 0; e < PER_BC; ++e) {
         const int idx = tid + e * kThreads;
-        if (idx < BC && ts + idx / DS < t_hi) {
-          float sb = s_red[idx], sc = s_red[NWAVE * BC + idx];
+        const int ridx = (BC % kThreads == 0 || idx < BC) ? idx : 0;
+        float sb = s_red[ridx], sc = s_red[NWAVE * BC + ridx];
 #pragma unroll
-          for (int w = 1; w < NWAVE; ++w) {
-            sb += s_red[w * BC + idx];
-            sc += s_red[NWAVE * BC + w * BC + idx];
-          }
-          part[idx] = make_float2(sb, sc);
+        for (int w = 1; w < NWAVE; ++w) {
+          sb += s_red[w * BC + ridx];
+          sc += s_red[NWAVE * BC + w * BC + ridx];
         }
+        const uint32_t off = (BC % kThreads == 0 || idx < BC) ? static_cast<uint32_t>(idx) * 8u : kOutOfRange;
+        float v2[2] = {sb, sc};
+        buf_store_vec<2>(rP, off, v2);
       }
     }
+    store_tile();  // the inputs of the tile before this one (zeros before the chunk start)
   }
 
   if (!dvalid) return;

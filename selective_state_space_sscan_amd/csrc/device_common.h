@@ -115,6 +115,14 @@ __device__ __forceinline__ void lds_load_vec(const float* p, float (&v)[K]) {
   }
 }
 
+// Rows of a tile that lie in [.., hi): clamp(hi - ts, 0, tb).  The value is uniform, but
+// the compiler lowers this clamp to a vector med3; reading it back into a scalar register
+// keeps the buffer resources built from it scalar (a vector resource would force a
+// loop around every load that uses it).
+__device__ __forceinline__ int tile_rows(int hi, int ts, int tb) {
+  return __builtin_amdgcn_readfirstlane(max(0, min(tb, hi - ts)));
+}
+
 // ---- XCD-aware workgroup order -------------------------------------------------------
 // Workgroups are dispatched to the 8 XCDs round-robin by linear id, and each XCD has its
 // own L2.  Remap linear ids so that G consecutive logical tiles (which share 128-byte

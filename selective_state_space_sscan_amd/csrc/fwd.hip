@@ -50,8 +50,14 @@ __host__ __device__ constexpr int fwd_batch_steps() {
   return (32 / K) < 16 ? ((32 / K) < TB ? (32 / K) : TB) : (16 < TB ? 16 : TB);
 }
 
-template <typename IO, int DS, int L, bool LOCAL>
+// MODE: kLocal (local pass of the two-level scan: no outputs but the chunk pair),
+// kFull (y and hT), kFullH (y, hT and H).  Whether H is stored is a compile-time
+// choice so that the stores are unconditional in the step code.
+constexpr int kLocal = 0, kFull = 1, kFullH = 2;
+
+template <typename IO, int DS, int L, int MODE>
 __global__ __launch_bounds__(kThreads) void fwd_kernel(const FwdParams p) {
+  constexpr bool LOCAL = MODE == kLocal;
   constexpr int K = DS / L;
   constexpr int CPW = kThreads / L;
   constexpr int TB = fwd_tile_steps(L);
@@ -132,8 +138,11 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(const FwdParams p) {
   const uint32_t hlane = dvalid ? static_cast<uint32_t>(d * DS + j * K) * 4u : kOutOfRange;
 
   float rx[PER], rd[PER], rb[PER_BC], rc[PER_BC];
+  // Past the end of the chunk the resource is empty and every load returns 0: the
+  // prefetch is issued unconditionally, so that the wait for it never has to cover the
+  // H and y stores issued after it (a conditional load makes the wait count path-dependent).
   auto load_tile = [&](int ts) {
-    const int rows = min(TB, t_end - ts);
+    const int rows = tile_rows(t_end, ts, TB);
     const rsrc_t rX = make_rsrc(xrow + (int64_t)ts * D, static_cast<uint32_t>(rows * D) * ES);
     const rsrc_t rD = make_rsrc(drow + (int64_t)ts * D, static_cast<uint32_t>(rows * D) * ES);
     const rsrc_t rB = make_rsrc(brow + (int64_t)ts * DS, static_cast<uint32_t>(rows * DS) * ES);
@@ -150,6 +159,9 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(const FwdParams p) {
     }
   };
   auto store_tile = [&]() {
+    // keep the scheduler from hoisting the delta*x products (and with them the wait for
+    // the loads) into the step code that runs while the loads are still in flight
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int e = 0; e < PER; ++e) s_dw[tid + e * kThreads] = make_float2(rd[e], rd[e] * rx[e]);
 #pragma unroll
@@ -164,18 +176,22 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(const FwdParams p) {
 
   const int nsteps_total = t_end - t_begin;
   const int ntiles = nsteps_total > 0 ? (nsteps_total + TB - 1) / TB : 0;
-  if (ntiles > 0) load_tile(t_begin);
+  if (ntiles > 0) {
+    load_tile(t_begin);
+    store_tile();
+  }
 
+  // Each tile issues the next tile's loads before its own steps and parks them in LDS
+  // only after them, so no loaded register is live across the loop back-edge and the
+  // wait for those loads never has to cover the H stores issued in between.
   for (int it = 0; it < ntiles; ++it) {
     const int ts = t_begin + it * TB;
     const int rows = min(TB, t_end - ts);
-    __syncthreads();  // the previous tile's LDS reads are complete
-    store_tile();
-    __syncthreads();
-    if (it + 1 < ntiles) load_tile(ts + TB);
+    __syncthreads();  // this tile's inputs are in LDS; the previous tile's y reads are done
+    load_tile(ts + TB);
 
     const rsrc_t rH = make_rsrc(Hrow + (int64_t)ts * D * DS, static_cast<uint32_t>(rows) * hstep);
-#pragma unroll 1
+#pragma unroll
     for (int s0 = 0; s0 < TB; s0 += S) {
       // decays and injections of S steps: independent of the state, issued together
       float a[S][K], u[S][K];
@@ -215,19 +231,20 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(const FwdParams p) {
           for (int i = 0; i < K; ++i) yp = fmaf(a[s][i], cv[i], yp);
           s_y[(s0 + s) * CPW + ch] = group_sum<L>(yp);  // every lane of the channel holds the sum
         }
-        if (p.H != nullptr) {
+        if constexpr (MODE == kFullH) {
 #pragma unroll
           for (int s = 0; s < S; ++s) buf_store_vec<K>(rH, hlane + static_cast<uint32_t>(s0 + s) * hstep, a[s]);
         }
       }
     }
 
+    __syncthreads();  // every lane is done with this tile's inputs and has written its y
     if constexpr (!LOCAL) {
-      __syncthreads();
       const rsrc_t rY = make_rsrc(yrow + (int64_t)ts * D, static_cast<uint32_t>(rows * D) * ES);
 #pragma unroll
       for (int e = 0; e < PER; ++e) buf_store_io<IO>(rY, xoff[e], s_y[tid + e * kThreads]);
     }
+    store_tile();  // the next tile's inputs (zeros past the end of the chunk)
   }
 
   if (!dvalid) return;
@@ -260,9 +277,11 @@ __global__ __launch_bounds__(kThreads) void fill_kernel(float* __restrict__ dst,
 template <typename IO, int DS, int L>
 hipError_t launch_fwd_t(bool local_pass, const FwdParams& p, unsigned blocks, hipStream_t s) {
   if (local_pass)
-    hipLaunchKernelGGL((fwd_kernel<IO, DS, L, true>), dim3(blocks), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((fwd_kernel<IO, DS, L, kLocal>), dim3(blocks), dim3(kThreads), 0, s, p);
+  else if (p.H != nullptr)
+    hipLaunchKernelGGL((fwd_kernel<IO, DS, L, kFullH>), dim3(blocks), dim3(kThreads), 0, s, p);
   else
-    hipLaunchKernelGGL((fwd_kernel<IO, DS, L, false>), dim3(blocks), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((fwd_kernel<IO, DS, L, kFull>), dim3(blocks), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
