@@ -17,9 +17,11 @@
 // and CPW = 256/L channels, L lanes per channel, K = DS/L states per lane.  The
 // workgroup walks tiles of TB steps from the end of the sequence to the start; the
 // x / delta / dy tiles and the b / c rows are loaded cooperatively one tile ahead and
-// parked in LDS as fp32.  Each lane reads its own states H_{t-1} straight from HBM
-// (coalesced: the lanes of a wave cover consecutive (channel, state) addresses) a
-// sub-block ahead, and keeps H_t from the previous step.  Sums over a channel's states
+// parked in LDS as fp32.  The states H_{t-1} of a wave's channels are fetched a
+// sub-block ahead with 16-byte loads per lane (a wave's channels cover consecutive
+// addresses of each step row), parked in a per-wave LDS block when their sub-block
+// starts, and read back by each lane for its own states; H_t is kept from the step
+// before.  Sums over a channel's states
 // use DPP; sums over channels use DPP row rotations, the gfx950 row-swap permutes and
 // one LDS slot per wave, and each workgroup writes one (gb, gc) partial per (step,
 // state) and one gA partial per (batch row, channel, state).  A second kernel adds the
@@ -105,7 +107,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
   constexpr int NITEM = S * K;
   constexpr uint32_t ES = sizeof(IO);
   static_assert(TILE % kThreads == 0 && TB % HB == 0 && HB % S == 0, "tile shape");
-  static_assert(NSUB % 2 == 0, "H blocks per tile must be even");
   static_assert(NITEM % 2 == 0, "items per batch must pair up");
 
   __shared__ float4 s_in[TILE];              // (delta, x, dy, delta*x) at [step*CPW + channel]
@@ -145,7 +146,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
   const float* Hrow = p.H + (int64_t)bb * T * D * DS;
   const int64_t soff = ((int64_t)bb * D + d) * DS + j * K;
   const uint32_t hstep = static_cast<uint32_t>(D) * DS * 4u;
-  const uint32_t hlane = dvalid ? static_cast<uint32_t>(d * DS + j * K) * 4u : kOutOfRange;
 
   float Av[K], A2[K], G[K], gA[K], hcur[K];
 #pragma unroll
@@ -219,32 +219,58 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
   };
 
   // ---- H_{t-1} for a block of HB steps starting at step tf, prefetched a block ahead ----
-  // Entry r holds H_{tf+r-1}, and 0 for steps outside [1, T] or when the block is not
-  // valid; step 0 takes h0 from registers instead (loaded once, below).  The loaded
-  // registers are used as they are, so that nothing waits for a prefetch before the
-  // block it belongs to is reached.
-  float hbuf[2][HB][K];
+  // Per step, the lanes of a wave need 64*K consecutive floats of H (its channels' rows).
+  // A block is fetched with 16-byte loads per lane (a quarter of the vector-memory
+  // instructions and address work of one dword per lane and step) into registers, and
+  // parked in a per-wave LDS block at the start of the sub-block that reads it, where
+  // each lane picks up its own states.  Row r of a block holds H_{tf+r-1}, and 0 for
+  // steps outside [1, T], for channels past D, or when the block is not valid; step 0
+  // takes h0 from registers.
+  constexpr int WROW = 64 * K;                                  // floats per step and wave
+  constexpr int HBLK = HB * WROW;                               // floats per block and wave
+  constexpr int DB = (HBLK * 4) % (64 * 16) == 0 ? 16 : 4;      // bytes per lane and load
+  constexpr int NQ = HBLK * 4 / (64 * DB);                      // loads per block
+  static_assert(NQ * 64 * DB == HBLK * 4, "an H block is a whole number of loads");
+  __shared__ float s_h[NWAVE * HBLK];
+  const int wd0 = d0 + wave * (64 / L);                         // first channel of this wave
+  const uint32_t wbytes = static_cast<uint32_t>(max(0, min(64 / L, D - wd0)) * DS * 4);
+  const uint32_t whoff = static_cast<uint32_t>(wd0) * DS * 4u;
+  float* const hblk = s_h + wave * HBLK;
+  float hq[NQ][DB / 4];
   float hzero[K];
 #pragma unroll
   for (int i = 0; i < K; ++i) hzero[i] = 0.f;
   if (chunk == 0 && p.h0 != nullptr && dvalid) load_k<K>(p.h0 + soff, hzero);
-  auto load_hblock = [&](float (&dst)[HB][K], int tf, bool valid) {
+  auto load_hblock = [&](float (&dst)[NQ][DB / 4], int tf, bool valid) {
     const int h_lo = max(tf - 1, 0);
     const int h_hi = min(tf - 1 + HB, T);  // exclusive
     const uint32_t nrow = valid ? static_cast<uint32_t>(max(h_hi - h_lo, 0)) : 0u;
     const rsrc_t rH = make_rsrc(Hrow + (int64_t)h_lo * D * DS, nrow * hstep);
 #pragma unroll
-    for (int r = 0; r < HB; ++r) {
+    for (int q = 0; q < NQ; ++q) {
+      const int pos = q * 64 * DB + lane * DB;  // byte within the wave's block
+      const int r = pos / (WROW * 4);
+      const uint32_t b = static_cast<uint32_t>(pos % (WROW * 4));
       const int tp = tf - 1 + r;
-      const uint32_t off = (tp >= 0) ? hlane + static_cast<uint32_t>(tp - h_lo) * hstep : kOutOfRange;
-      buf_load_vec<K>(rH, off, dst[r]);
+      const uint32_t off = (tp >= 0 && b < wbytes) ? static_cast<uint32_t>(tp - h_lo) * hstep + whoff + b : kOutOfRange;
+      buf_load_vec<DB / 4>(rH, off, dst[q]);
+    }
+  };
+  auto park_hblock = [&](const float (&src)[NQ][DB / 4]) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      float* dst = hblk + q * 16 * DB + lane * (DB / 4);
+      if constexpr (DB == 16)
+        *reinterpret_cast<float4*>(dst) = make_float4(src[q][0], src[q][1], src[q][2], src[q][3]);
+      else
+        dst[0] = src[q][0];
     }
   };
 
   if (ntiles > 0) {
     const int ts_last = t_lo + (ntiles - 1) * TB;
     load_tile(ts_last);
-    load_hblock(hbuf[0], ts_last + (NSUB - 1) * HB, true);
+    load_hblock(hq, ts_last + (NSUB - 1) * HB, true);
     store_tile();
   }
 
@@ -258,13 +284,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
 
 #pragma unroll
     for (int sb = NSUB - 1; sb >= 0; --sb) {
-      // An even number of H blocks precede each tile, so buffer roles depend only on sb.
-      float (&cur)[HB][K] = hbuf[(NSUB - 1 - sb) & 1];
-      float (&nxt)[HB][K] = hbuf[((NSUB - 1 - sb) & 1) ^ 1];
+      park_hblock(hq);  // this sub-block's H rows, loaded during the previous one
       if (sb > 0)
-        load_hblock(nxt, ts + (sb - 1) * HB, true);
+        load_hblock(hq, ts + (sb - 1) * HB, true);
       else
-        load_hblock(nxt, ts - TB + (NSUB - 1) * HB, it > 0);
+        load_hblock(hq, ts - TB + (NSUB - 1) * HB, it > 0);
 
 #pragma unroll
       for (int bt = NBAT - 1; bt >= 0; --bt) {
@@ -291,19 +315,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
         }
         // phase C: gradient terms of each step
         float Sl[S], gdl[S], gbv[S][K], gcv[S][K];
+        float hrow[S][K];  // H_{t-1} of the batch's steps
+#pragma unroll
+        for (int s = 0; s < S; ++s) lds_load_vec<K>(&hblk[(bt * S + s) * WROW + lane * K], hrow[s]);
+        if (bt == 0) {
+          const bool first = ts + sb * HB == 0;  // step 0 of the sequence: H_{-1} = h0
+#pragma unroll
+          for (int i = 0; i < K; ++i) hrow[0][i] = first ? hzero[i] : hrow[0][i];
+        }
 #pragma unroll
         for (int s = 0; s < S; ++s) {
           float bv[K];
           lds_load_vec<K>(&s_b[(tt0 + s) * DS + j * K], bv);
-          float hp[K];                                                     // H_{t-1}
-#pragma unroll
-          for (int i = 0; i < K; ++i) hp[i] = cur[bt * S + s][i];
-          if (bt == 0 && s == 0) {
-            const bool first = ts + sb * HB == 0;  // step 0 of the sequence: H_{-1} = h0
-#pragma unroll
-            for (int i = 0; i < K; ++i) hp[i] = first ? hzero[i] : hp[i];
-          }
-          const float(&ht)[K] = (s == S - 1) ? hcur : cur[bt * S + s + 1];  // H_t
+          const float(&hp)[K] = hrow[s];                                     // H_{t-1}
+          const float(&ht)[K] = (s == S - 1) ? hcur : hrow[s + 1];           // H_t
           float sl = 0.f, gd = 0.f;
 #pragma unroll
           for (int i = 0; i < K; ++i) {
@@ -318,7 +343,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
           gdl[s] = gd;
         }
 #pragma unroll
-        for (int i = 0; i < K; ++i) hcur[i] = cur[bt * S][i];
+        for (int i = 0; i < K; ++i) hcur[i] = hrow[0][i];
         // phase D: sums over each channel's states -> gx, gdelta.  The (Sl, gdl) pairs of
         // the whole batch are reduce-scattered over the channel's lanes, so that the
         // stages carry independent adds instead of one dependent chain per step.
@@ -381,8 +406,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
       for (int e = 0; e < PER; ++e) {
         const float2 v = s_gxd[tid + e * kThreads];
         const uint32_t off = xoff[e] == kOutOfRange ? kOutOfRange : xoff[e] / ES * 4u;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v.x), rGX, off, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v.y), rGD, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v.x), rGX, off, 0, kNonTemporal);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v.y), rGD, off, 0, kNonTemporal);
       }
       const rsrc_t rP = make_rsrc(p.part_bc + ((int64_t)dtile * p.B + bb) * T * DS + (int64_t)ts * DS,
                                   static_cast<uint32_t>(rows * DS) * 8u);

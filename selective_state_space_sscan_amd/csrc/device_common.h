@@ -61,25 +61,31 @@ __device__ __forceinline__ void buf_store_io(rsrc_t r, uint32_t off, float v) {
   buf_store_elem(r, off, v, static_cast<IO*>(nullptr));
 }
 
-// K consecutive fp32 values at byte offset off.
-template <int K>
+// Cache-policy operand of a buffer instruction with the non-temporal bit set: the data
+// is streamed out and not kept in the caches.  For the materialised states, written once
+// and read back only by the backward, this raises the sustained HBM write rate markedly.
+constexpr int kNonTemporal = 2;
+
+// K consecutive fp32 values at byte offset off.  AUX is the instruction's cache-policy
+// operand (0: default).
+template <int K, int AUX = 0>
 __device__ __forceinline__ void buf_load_vec(rsrc_t r, uint32_t off, float (&v)[K]) {
   if constexpr (K % 4 == 0) {
 #pragma unroll
     for (int q = 0; q < K / 4; ++q) {
-      const auto t = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * q, 0, 0);
+      const auto t = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * q, 0, AUX);
       v[4 * q] = __uint_as_float(t[0]); v[4 * q + 1] = __uint_as_float(t[1]);
       v[4 * q + 2] = __uint_as_float(t[2]); v[4 * q + 3] = __uint_as_float(t[3]);
     }
   } else if constexpr (K == 2) {
-    const auto t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    const auto t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX);
     v[0] = __uint_as_float(t[0]); v[1] = __uint_as_float(t[1]);
   } else {
-    v[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+    v[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX));
   }
 }
 
-template <int K>
+template <int K, int AUX = 0>
 __device__ __forceinline__ void buf_store_vec(rsrc_t r, uint32_t off, const float (&v)[K]) {
   if constexpr (K % 4 == 0) {
 #pragma unroll
@@ -87,14 +93,14 @@ __device__ __forceinline__ void buf_store_vec(rsrc_t r, uint32_t off, const floa
       __attribute__((ext_vector_type(4))) uint32_t t;
       t[0] = __float_as_uint(v[4 * q]); t[1] = __float_as_uint(v[4 * q + 1]);
       t[2] = __float_as_uint(v[4 * q + 2]); t[3] = __float_as_uint(v[4 * q + 3]);
-      __builtin_amdgcn_raw_buffer_store_b128(t, r, off + 16 * q, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(t, r, off + 16 * q, 0, AUX);
     }
   } else if constexpr (K == 2) {
     __attribute__((ext_vector_type(2))) uint32_t t;
     t[0] = __float_as_uint(v[0]); t[1] = __float_as_uint(v[1]);
-    __builtin_amdgcn_raw_buffer_store_b64(t, r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(t, r, off, 0, AUX);
   } else {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[0]), r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[0]), r, off, 0, AUX);
   }
 }
 

@@ -233,7 +233,8 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(const FwdParams p) {
         }
         if constexpr (MODE == kFullH) {
 #pragma unroll
-          for (int s = 0; s < S; ++s) buf_store_vec<K>(rH, hlane + static_cast<uint32_t>(s0 + s) * hstep, a[s]);
+          for (int s = 0; s < S; ++s)
+            buf_store_vec<K, kNonTemporal>(rH, hlane + static_cast<uint32_t>(s0 + s) * hstep, a[s]);
         }
       }
     }
