@@ -202,6 +202,7 @@ def main() -> int:
     print(f"bench: step {step_ms:.4f} ms (fwd {f_avg:.4f}, bwd {b_avg:.4f})", file=sys.stderr, flush=True)
 
     fwd_only = None if args.no_fwd_only else bench_fwd_only(dev, args.warmup, max(5, K // 5))
+    decode = None if args.no_fwd_only else bench_decode(dev, args.warmup, max(5, K // 5))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -214,10 +215,68 @@ def main() -> int:
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "fwd+bwd B=8 T=2048 D=768 DS=16 fp32, H materialised, 6 gradients",
                    "B": B, "T": T, "D": D, "DS": DS, "io": "f32"},
-        "roofline": roofline, "cpu_baseline": cpu, "detail": detail, "fwd_only": fwd_only,
+        "roofline": roofline, "cpu_baseline": cpu, "detail": detail, "fwd_only": fwd_only, "decode": decode,
     }
     print(json.dumps(line))
     return 0
+
+
+def bench_decode(dev, warmup, reps):
+    """One-token decode steps on a resident state.  A run of consecutive in-place steps is
+    captured once in a HIP graph and replayed, so the time per step is the GPU's (eager
+    calls from Python are host-bound at this size); the eager per-call time is reported
+    beside it."""
+    import torch
+
+    import workloads
+    from selective_state_space_sscan_amd import sscan_decode
+
+    out = {}
+    B, D, DS = 16, 1024, 16
+    for io in ("f32", "bf16"):
+        w = workloads.custom(B, 1, D, DS, io=io, seed=9, h0_std=0.1)
+        g = {k: (None if v is None else v.to(dev)) for k, v in workloads.make_inputs(w).items()}
+        x, dl, b, c = g["x"][:, 0], g["delta"][:, 0], g["b"][:, 0], g["c"][:, 0]
+        state = g["h0"].clone()
+        y = torch.empty((B, D), dtype=x.dtype, device=dev)
+        for _ in range(max(warmup, 3)):
+            sscan_decode(x, dl, g["A"], b, c, state, y=y, inplace=True)
+        torch.cuda.synchronize()
+        n = max(50, reps * 10)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            sscan_decode(x, dl, g["A"], b, c, state, y=y, inplace=True)
+        e1.record()
+        torch.cuda.synchronize()
+        us_eager = e0.elapsed_time(e1) * 1e3 / n
+        steps = 32
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream(device=dev)
+        cap.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                for _ in range(steps):
+                    sscan_decode(x, dl, g["A"], b, c, state, y=y, inplace=True)
+        torch.cuda.current_stream(dev).wait_stream(cap)
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        reps_g = max(10, reps)
+        e0.record()
+        for _ in range(reps_g):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps_g * steps)
+        s = 2 if io == "bf16" else 4
+        nbytes = B * D * DS * 8 + B * D * 3 * s + B * DS * 2 * s + D * DS * 4
+        out[io] = {"workload": f"decode step B={B} D={D} DS={DS} {io} I/O, state fp32 in place",
+                   "us_per_step": us, "us_per_step_eager_python": us_eager,
+                   "tokens_per_s": B / (us * 1e-6), "gb_per_s": nbytes / (us * 1e-6) / 1e9}
+        print(f"bench: decode {io}: {us:.2f} us/step in a graph, {us_eager:.2f} us/step eager",
+              file=sys.stderr, flush=True)
+    return out
 
 
 def bench_fwd_only(dev, warmup, reps):

@@ -123,6 +123,21 @@ int sscan_bwd(const sscan_desc* desc, const sscan_plan* plan, const void* dy, co
 /* Bytes of workspace sscan_bwd needs for (desc, plan) -> *bytes. */
 int sscan_bwd_workspace(const sscan_desc* desc, const sscan_plan* plan, size_t* bytes);
 
+/* One decode step (T = 1) on a state kept in device memory between calls: the recurrence
+ * of the forward applied to a single token ("ruDNN KDA chunk.rs" page, chunk_kda: one
+ * token goes through a fused recurrent kernel on the resident state, and inputs are
+ * never mutated).  For each b, d, n:
+ *     state_out[b,d,n] = exp(delta[b,d] A[d,n]) state_in[b,d,n] + delta[b,d] b[b,n] x[b,d]
+ *     y[b,d]           = sum_n state_out[b,d,n] c[b,n]
+ *   desc->T must be 1 (SSCAN_ERR_SHAPE otherwise); layouts, strides and dtypes are the
+ *   forward's with T = 1: x, delta, y (B,1,D) io; b, c (B,1,DS) io; A (D,DS) fp32.
+ *   state_in, state_out (B,D,DS) fp32, 16-byte aligned.  state_out may be state_in itself
+ *   (the update is then in place); any other overlap is SSCAN_ERR_SHAPE.
+ *   Same result as sscan_fwd with T = 1, h0 = state_in, hT = state_out, up to the order of
+ *   the sum over states.  B == 0 or D == 0: nothing to do.  Needs no workspace. */
+int sscan_decode(const sscan_desc* desc, const void* x, const void* delta, const float* A, const void* b,
+                 const void* c, const float* state_in, float* state_out, void* y, hipStream_t stream);
+
 /* The plan the library picks for desc (backward != 0: for sscan_bwd) -> *plan.  Uses no GPU. */
 int sscan_plan_select(const sscan_desc* desc, int backward, sscan_plan* plan);
 

@@ -15,8 +15,8 @@ import torch
 from . import _lib
 from ._lib import SScanError, sscan_desc, sscan_plan
 
-__all__ = ["sscan_fwd", "sscan_bwd", "sscan_fwd_workspace", "sscan_bwd_workspace", "sscan_plan_select",
-           "sscan_version", "SelectiveScan", "selective_scan", "SScanError", "Plan"]
+__all__ = ["sscan_fwd", "sscan_bwd", "sscan_decode", "sscan_fwd_workspace", "sscan_bwd_workspace",
+           "sscan_plan_select", "sscan_version", "SelectiveScan", "selective_scan", "SScanError", "Plan"]
 
 _IO = {torch.float32: _lib.SSCAN_F32, torch.bfloat16: _lib.SSCAN_BF16}
 
@@ -268,6 +268,61 @@ def sscan_bwd(dy: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: torch.T
                            _ptr(ws), ctypes.c_size_t(wsn), _stream(device))
     _lib.check(st)
     return gx, gdelta, gb, gc, gA, gh0
+
+
+def sscan_decode(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, b: torch.Tensor, c: torch.Tensor,
+                 state: torch.Tensor, *, y: Optional[torch.Tensor] = None, state_out: Optional[torch.Tensor] = None,
+                 inplace: bool = False):
+    """One decode step on a resident state.  Returns (y, state_out).
+
+    x, delta: (B,D) or (B,1,D) fp32 or bf16; A: (D,DS) fp32; b, c: (B,DS) or (B,1,DS) of x's
+    dtype; state: (B,D,DS) contiguous fp32.  With ``inplace`` the new state overwrites
+    ``state`` (and is returned); otherwise it goes to ``state_out`` (allocated if None).
+    y has x's dtype and shape.
+    """
+    lib = _lib.load()
+    if x.dtype not in _IO:
+        raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
+    for n_, t in (("delta", delta), ("b", b), ("c", c)):
+        if t.dtype != x.dtype:
+            raise TypeError(f"{n_} must have x's dtype {x.dtype}, got {t.dtype}")
+    device = x.device
+    if device.type != "cuda":
+        raise ValueError("sscan_decode runs on a GPU: move the tensors to a HIP device")
+    squeeze = x.dim() == 2
+    x3, d3 = (x.unsqueeze(1), delta.unsqueeze(1)) if squeeze else (x, delta)
+    b3 = b.unsqueeze(1) if b.dim() == 2 else b
+    c3 = c.unsqueeze(1) if c.dim() == 2 else c
+    if x3.dim() != 3 or x3.shape[1] != 1:
+        raise ValueError(f"x must be (B,D) or (B,1,D), got {tuple(x.shape)}")
+    B, _, D = x3.shape
+    if A.dim() != 2 or A.shape[0] != D:
+        raise ValueError(f"A must have shape (D, DS) with D={D}, got {tuple(A.shape)}")
+    DS = A.shape[1]
+    if tuple(d3.shape) != (B, 1, D) or tuple(b3.shape) != (B, 1, DS) or tuple(c3.shape) != (B, 1, DS):
+        raise ValueError("shape mismatch among x, delta (B,D) and b, c (B,DS)")
+    _check_device(device, delta=delta, A=A, b=b, c=c, state=state, y=y, state_out=state_out)
+    (x3, d3), x_bs = _same_stride([x3, d3], ["x", "delta"])
+    (b3, c3), bc_bs = _same_stride([b3, c3], ["b", "c"])
+    A = _f32_contig(A, (D, DS), "A")
+    if state.dtype != torch.float32 or tuple(state.shape) != (B, D, DS) or not state.is_contiguous():
+        raise ValueError(f"state must be a contiguous float32 tensor of shape {(B, D, DS)}")
+    if inplace:
+        state_out = state
+    elif state_out is None:
+        state_out = torch.empty_like(state)
+    elif state_out.dtype != torch.float32 or tuple(state_out.shape) != (B, D, DS) or not state_out.is_contiguous():
+        raise ValueError(f"state_out must be a contiguous float32 tensor of shape {(B, D, DS)}")
+    y3 = torch.empty((B, 1, D), dtype=x.dtype, device=device) if y is None else (y.unsqueeze(1) if y.dim() == 2 else y)
+    if y3.dtype != x.dtype or tuple(y3.shape) != (B, 1, D):
+        raise ValueError("y must have x's dtype and shape")
+    y_bs = _batch_stride(y3, "y")
+    d = _desc(B, 1, D, DS, _IO[x.dtype], x_bs, bc_bs, y_bs)
+    with torch.cuda.device(device):
+        st = lib.sscan_decode(ctypes.byref(d), _ptr(x3), _ptr(d3), _ptr(A), _ptr(b3), _ptr(c3), _ptr(state),
+                              _ptr(state_out), _ptr(y3), _stream(device))
+    _lib.check(st)
+    return (y3.squeeze(1) if squeeze else y3), state_out
 
 
 class SelectiveScan(torch.autograd.Function):

@@ -392,4 +392,35 @@ int sscan_bwd(const sscan_desc* desc, const sscan_plan* plan, const void* dy, co
   return ok();
 }
 
+int sscan_decode(const sscan_desc* desc, const void* x, const void* delta, const float* A, const void* b,
+                 const void* c, const float* state_in, float* state_out, void* y, hipStream_t stream) {
+  Resolved r;
+  int st = resolve_desc(desc, &r);
+  if (st != SSCAN_OK) return st;
+  if (r.T != 1) return fail(SSCAN_ERR_SHAPE, "decode takes one step: desc.T must be 1, got %lld", (long long)r.T);
+  if (r.B == 0 || r.D == 0) return ok();
+  if (x == nullptr || delta == nullptr || A == nullptr || b == nullptr || c == nullptr || state_in == nullptr ||
+      state_out == nullptr || y == nullptr)
+    return fail(SSCAN_ERR_NULL, "x, delta, A, b, c, state_in, state_out and y are required");
+  const size_t es = r.io_size;
+  if (misaligned(x, es) || misaligned(delta, es) || misaligned(b, es) || misaligned(c, es) || misaligned(y, es))
+    return fail(SSCAN_ERR_ALIGN, "io tensors must be aligned to their element size");
+  if (misaligned(A, 16) || misaligned(state_in, 16) || misaligned(state_out, 16))
+    return fail(SSCAN_ERR_ALIGN, "A, state_in and state_out must be 16-byte aligned");
+  const int64_t nstate = r.B * r.D * r.DS;
+  const char* si = reinterpret_cast<const char*>(state_in);
+  const char* so = reinterpret_cast<const char*>(state_out);
+  const int64_t sbytes = nstate * 4;
+  if (si != so && si < so + sbytes && so < si + sbytes)
+    return fail(SSCAN_ERR_SHAPE, "state_out must be state_in itself or not overlap it");
+  if ((nstate + kThreads - 1) / kThreads > std::numeric_limits<int32_t>::max())
+    return fail(SSCAN_ERR_UNSUPPORTED, "too many workgroups");
+  sscan::DecodeParams p{};
+  p.x = x; p.delta = delta; p.A = A; p.b = b; p.c = c; p.state_in = state_in; p.state_out = state_out; p.y = y;
+  p.x_bs = r.x_bs; p.bc_bs = r.bc_bs; p.y_bs = r.y_bs;
+  p.B = (int32_t)r.B; p.D = (int32_t)r.D;
+  const hipError_t e = sscan::launch_decode(r.io, (int)r.DS, p, stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "decode step");
+}
+
 }  // extern "C"

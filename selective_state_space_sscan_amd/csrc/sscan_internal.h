@@ -99,12 +99,26 @@ struct ReduceParams {
   int32_t chunks;
 };
 
+struct DecodeParams {
+  const void* x;          // (B, D) rows at b*x_bs
+  const void* delta;
+  const float* A;         // (D, DS)
+  const void* b;          // (B, DS) rows at b*bc_bs
+  const void* c;
+  const float* state_in;  // (B, D, DS)
+  float* state_out;       // (B, D, DS); may be state_in itself
+  void* y;                // (B, D) rows at b*y_bs
+  int64_t x_bs, bc_bs, y_bs;
+  int32_t B, D;
+};
+
 // Launchers (defined in the .hip translation units).  Each returns a hipError_t.
 hipError_t launch_fwd(int io, int DS, int lanes, bool local_pass, const FwdParams& p, unsigned blocks, hipStream_t s);
 hipError_t launch_carry(const CarryParams& p, hipStream_t s);
 hipError_t launch_bwd(int io, int DS, int lanes, bool local_pass, const BwdParams& p, unsigned blocks, hipStream_t s);
 hipError_t launch_bwd_carry(const BwdCarryParams& p, hipStream_t s);
 hipError_t launch_bwd_reduce(const ReduceParams& p, hipStream_t s);
+hipError_t launch_decode(int io, int DS, const DecodeParams& p, hipStream_t s);
 hipError_t launch_fill(float* dst, int64_t n, hipStream_t s);                         // dst[i] = 0
 hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t s);  // src ? copy : zero
 

@@ -186,3 +186,22 @@ def test_plan_select_and_workspace_sizes(lib):
     assert lib.sscan_bwd_workspace(ctypes.byref(d), None, ctypes.byref(n)) == OK
     tiles = (768 + 15) // 16
     assert n.value >= tiles * 8 * 2048 * 16 * 8 + 8 * 768 * 16 * 4
+
+
+def dec(lib, d, x=FAKE, delta=FAKE, A=FAKE, b=FAKE, c=FAKE, si=FAKE, so=FAKE + 0x10000, y=FAKE):
+    v = lambda p: None if p is None else ctypes.c_void_p(p)
+    return lib.sscan_decode(ctypes.byref(d), v(x), v(delta), v(A), v(b), v(c), v(si), v(so), v(y), None)
+
+
+def test_decode_validation(lib):
+    assert dec(lib, desc(T=2)) == E_SHAPE           # one step only
+    assert dec(lib, desc(T=0)) == E_SHAPE
+    assert dec(lib, desc(T=1), si=None) == E_NULL
+    assert dec(lib, desc(T=1), y=None) == E_NULL
+    assert dec(lib, desc(T=1), si=FAKE + 4) == E_ALIGN
+    assert dec(lib, desc(T=1, io=1), x=FAKE + 1) == E_ALIGN
+    # B=2, D=16, DS=4: the state is 512 bytes; a partial overlap is refused, identity is not
+    assert dec(lib, desc(T=1), si=FAKE, so=FAKE + 256) == E_SHAPE
+    assert dec(lib, desc(T=1, DS=3)) == E_UNSUP
+    # nothing to do: no pointer is looked at
+    assert dec(lib, desc(B=0, T=1), x=None, delta=None, A=None, b=None, c=None, si=None, so=None, y=None) == OK
