@@ -33,7 +33,7 @@ _LIB = os.path.join(_HERE, "libsscan_oracle.so")
 _lock = threading.Lock()
 _lib = None
 
-__all__ = ["build", "fwd", "bwd", "default_threads"]
+__all__ = ["build", "fwd", "bwd", "default_threads", "mamba_fwd", "mamba_bwd", "softplus", "softplus_grad"]
 
 
 def build(force: bool = False) -> str:
@@ -139,3 +139,6 @@ def bwd(dy, x, delta, A, b, c, h0=None, dhT=None, *, nthreads=None):
     if rc != 0:
         raise RuntimeError(f"sscan_oracle_bwd failed ({rc})")
     return gx, gdelta, gb, gc, gA, gh0
+
+
+from .mamba import mamba_bwd, mamba_fwd, softplus, softplus_grad  # noqa: E402  (uses fwd/bwd above)

@@ -79,9 +79,12 @@ def _round_bf16(t: torch.Tensor) -> torch.Tensor:
 def make_inputs(w: Workload) -> Dict[str, Optional[torch.Tensor]]:
     """Draw the inputs of workload ``w`` on the CPU.
 
-    Returns a dict with keys x, delta, A, b, c, h0, dy, dhT.  x, delta, b, c
-    (and dy) are fp32 for f32 workloads and bf16 for bf16 workloads; A, h0 and
-    dhT are always fp32.  h0 / dy / dhT are None when the workload has none.
+    Returns a dict with keys x, delta, A, b, c, h0, dy, dhT, and for the
+    Mamba-style wrapper delta_raw (delta = softplus(delta_raw)), A_log
+    (A = -exp(A_log)) and Dskip (D,) ~ 1 + 0.5 N(0, 1).  x, delta, delta_raw, b,
+    c (and dy) are fp32 for f32 workloads and bf16 for bf16 workloads; A, A_log,
+    Dskip, h0 and dhT are always fp32.  h0 / dy / dhT are None when the workload
+    has none.
     """
     g = torch.Generator().manual_seed(int(w.seed))
     B, T, D, DS = w.B, w.T, w.D, w.DS
@@ -96,6 +99,7 @@ def make_inputs(w: Workload) -> Dict[str, Optional[torch.Tensor]]:
     h0_raw = torch.randn(B, D, DS, generator=g)
     dy = torch.randn(B, T, D, generator=g) if w.with_dy else None
     dhT = torch.randn(B, D, DS, generator=g) if w.with_dhT else None
+    Dskip = 1.0 + 0.5 * torch.randn(D, generator=g)  # drawn last: the draws above are unchanged
 
     delta = torch.nn.functional.softplus(delta_raw)
     ladder = -torch.arange(1, DS + 1, dtype=torch.float32).expand(D, DS)
@@ -110,14 +114,17 @@ def make_inputs(w: Workload) -> Dict[str, Optional[torch.Tensor]]:
     A = A.contiguous()
     h0 = (h0_raw * w.h0_std).contiguous() if w.h0_std > 0 else None
 
+    A_log = torch.log(-A).contiguous()  # the Mamba-style parameterisation A = -exp(A_log)
+
     if w.io == "bf16":
-        x, delta, b, c = (_round_bf16(t) for t in (x, delta, b, c))
+        x, delta, delta_raw, b, c = (_round_bf16(t) for t in (x, delta, delta_raw, b, c))
         if dy is not None:
             dy = _round_bf16(dy)
     elif w.io != "f32":
         raise ValueError(f"unknown io dtype {w.io!r}")
     return {"x": x.contiguous(), "delta": delta.contiguous(), "A": A, "b": b.contiguous(),
-            "c": c.contiguous(), "h0": h0, "dy": None if dy is None else dy.contiguous(), "dhT": dhT}
+            "c": c.contiguous(), "h0": h0, "dy": None if dy is None else dy.contiguous(), "dhT": dhT,
+            "delta_raw": delta_raw.contiguous(), "A_log": A_log, "Dskip": Dskip.contiguous()}
 
 
 def chunk_bounds(T: int, chunks: int):
