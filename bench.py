@@ -47,7 +47,8 @@ def alu_peak_states_per_s() -> float:
 
 
 PROFILE = os.path.join(ROOT, "profiles", "fwd_bwd_f32_B8_T2048_D768_DS16.md")
-KERNEL_SOURCES = ("fwd.hip", "bwd.hip", "device_common.h", "sscan_internal.h", "sscan_api.cpp")
+KERNEL_SOURCES = ("fwd_kernel.h", "fwd.hip", "bwd_kernel.h", "bwd.hip", "device_common.h", "sscan_internal.h",
+                  "sscan_api.cpp")
 
 
 def kernel_source_hash() -> str:
@@ -201,6 +202,7 @@ def main() -> int:
     }
     print(f"bench: step {step_ms:.4f} ms (fwd {f_avg:.4f}, bwd {b_avg:.4f})", file=sys.stderr, flush=True)
 
+    mamba = None if args.no_fwd_only else bench_mamba(g, y, hT, H, outs, B, T, D, args.warmup, max(10, K // 2))
     fwd_only = None if args.no_fwd_only else bench_fwd_only(dev, args.warmup, max(5, K // 5))
     decode = None if args.no_fwd_only else bench_decode(dev, args.warmup, max(5, K // 5))
 
@@ -215,10 +217,53 @@ def main() -> int:
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "fwd+bwd B=8 T=2048 D=768 DS=16 fp32, H materialised, 6 gradients",
                    "B": B, "T": T, "D": D, "DS": DS, "io": "f32"},
-        "roofline": roofline, "cpu_baseline": cpu, "detail": detail, "fwd_only": fwd_only, "decode": decode,
+        "roofline": roofline, "cpu_baseline": cpu, "detail": detail, "mamba": mamba, "fwd_only": fwd_only,
+        "decode": decode,
     }
     print(json.dumps(line))
     return 0
+
+
+def bench_mamba(g, y, hT, H, outs, B, T, D, warmup, reps):
+    """The Mamba-style wrapper (softplus step, A = -exp(A_log), skip term fused into the
+    scan kernels) on the same workload and buffers: forward with H and backward."""
+    import torch
+
+    from selective_state_space_sscan_amd import sscan_mamba_bwd, sscan_mamba_bwd_workspace, sscan_mamba_fwd
+
+    dev = g["x"].device
+    ws_b = torch.empty(max(1, sscan_mamba_bwd_workspace(B, T, D, H.shape[-1])), dtype=torch.uint8, device=dev)
+    gD = torch.empty((D,), dtype=torch.float32, device=dev)
+    mouts = tuple(outs) + (gD,)
+
+    def fwd():
+        sscan_mamba_fwd(g["x"], g["delta_raw"], g["A_log"], g["b"], g["c"], g["Dskip"], g["h0"], y=y, hT=hT, H=H)
+
+    def bwd():
+        sscan_mamba_bwd(g["dy"], g["x"], g["delta_raw"], g["A_log"], g["b"], g["c"], g["Dskip"], g["h0"], H, None,
+                        workspace=ws_b, out=mouts)
+
+    for _ in range(warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    f_ms = b_ms = 0.0
+    for _ in range(reps):
+        ev[0].record()
+        fwd()
+        ev[1].record()
+        bwd()
+        ev[2].record()
+        torch.cuda.synchronize()
+        f_ms += ev[0].elapsed_time(ev[1])
+        b_ms += ev[1].elapsed_time(ev[2])
+    f_ms /= reps
+    b_ms /= reps
+    print(f"bench: mamba wrapper fwd {f_ms:.4f} ms, bwd {b_ms:.4f} ms", file=sys.stderr, flush=True)
+    return {"workload": f"Mamba-style wrapper on B={B} T={T} D={D}: softplus(delta_raw), -exp(A_log), Dskip*x; "
+                        "fwd writes H, bwd returns 7 gradients",
+            "fwd_ms": f_ms, "bwd_ms": b_ms, "elems_per_s": B * T * D / ((f_ms + b_ms) * 1e-3)}
 
 
 def bench_decode(dev, warmup, reps):

@@ -123,6 +123,37 @@ int sscan_bwd(const sscan_desc* desc, const sscan_plan* plan, const void* dy, co
 /* Bytes of workspace sscan_bwd needs for (desc, plan) -> *bytes. */
 int sscan_bwd_workspace(const sscan_desc* desc, const sscan_plan* plan, size_t* bytes);
 
+/* Mamba-style wrapper around the scan (POPCORNBENCH page: the module's forward, steps
+ * 1, 4 and 9, and its numerically stable softplus that returns its argument above 20):
+ *     delta = softplus(delta_raw)    softplus(r) = r if r > 20 else log(1 + e^r)
+ *     A     = -exp(A_log)
+ *     y     = scan(x, delta, A, b, c, h0) + Dskip * x
+ * The prologue is applied as the inputs are staged and the skip term before y is
+ * rounded, inside the scan kernels: nothing extra is read or written.
+ *   Arguments, layouts, workspace (sscan_fwd_workspace) and errors as in sscan_fwd, with
+ *   delta_raw (B,T,D) io in place of delta, A_log (D,DS) fp32 in place of A, and
+ *   Dskip (D,) fp32, 4-byte aligned, or NULL (no skip term).  H holds the states of the
+ *   scan (what sscan_mamba_bwd takes). */
+int sscan_mamba_fwd(const sscan_desc* desc, const sscan_plan* plan, const void* x, const void* delta_raw,
+                    const float* A_log, const void* b, const void* c, const float* Dskip, const float* h0, void* y,
+                    float* hT, float* H, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Backward of sscan_mamba_fwd: gradients of L = sum(dy*y) + sum(dhT*hT) by the chain rule
+ * through the three maps (d delta/d delta_raw = 1 above 20, else e^r/(1+e^r); dA/dA_log = A;
+ * the skip term adds dy * Dskip to gx).
+ *   Arguments as in sscan_bwd, with delta_raw, A_log and Dskip as in sscan_mamba_fwd, and
+ *   gdelta_raw (B,T,D), gA_log (D,DS) fp32 in place of gdelta, gA.  gDskip (D,) fp32 or
+ *   NULL (not written) receives sum over b, t of dy * x -- the gradient for Dskip, also
+ *   when Dskip is NULL (that is, at Dskip = 0).  T == 0: gA_log = 0, gDskip = 0, gh0 = dhT.
+ *   ws/ws_bytes: at least what sscan_mamba_bwd_workspace reports. */
+int sscan_mamba_bwd(const sscan_desc* desc, const sscan_plan* plan, const void* dy, const float* dhT, const void* x,
+                    const void* delta_raw, const float* A_log, const void* b, const void* c, const float* Dskip,
+                    const float* h0, const float* H, float* gx, float* gdelta_raw, float* gA_log, float* gb,
+                    float* gc, float* gDskip, float* gh0, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Bytes of workspace sscan_mamba_bwd needs for (desc, plan) -> *bytes. */
+int sscan_mamba_bwd_workspace(const sscan_desc* desc, const sscan_plan* plan, size_t* bytes);
+
 /* One decode step (T = 1) on a state kept in device memory between calls: the recurrence
  * of the forward applied to a single token ("ruDNN KDA chunk.rs" page, chunk_kda: one
  * token goes through a fused recurrent kernel on the resident state, and inputs are

@@ -7,8 +7,10 @@ libsscan.so, hand-written HIP kernels behind a C ABI (include/sscan.h); this
 package is its Python binding.  Build it with
 ``python -m selective_state_space_sscan_amd.build``.
 """
-from .api import (Plan, SelectiveScan, SScanError, selective_scan, sscan_bwd, sscan_bwd_workspace, sscan_decode,
-                  sscan_fwd, sscan_fwd_workspace, sscan_plan_select, sscan_version)
+from .api import (MambaScan, Plan, SelectiveScan, SScanError, mamba_scan, selective_scan, sscan_bwd,
+                  sscan_bwd_workspace, sscan_decode, sscan_fwd, sscan_fwd_workspace, sscan_mamba_bwd,
+                  sscan_mamba_bwd_workspace, sscan_mamba_fwd, sscan_plan_select, sscan_version)
 
-__all__ = ["Plan", "SelectiveScan", "SScanError", "selective_scan", "sscan_bwd", "sscan_bwd_workspace",
-           "sscan_decode", "sscan_fwd", "sscan_fwd_workspace", "sscan_plan_select", "sscan_version"]
+__all__ = ["MambaScan", "Plan", "SelectiveScan", "SScanError", "mamba_scan", "selective_scan", "sscan_bwd",
+           "sscan_bwd_workspace", "sscan_decode", "sscan_fwd", "sscan_fwd_workspace", "sscan_mamba_bwd",
+           "sscan_mamba_bwd_workspace", "sscan_mamba_fwd", "sscan_plan_select", "sscan_version"]

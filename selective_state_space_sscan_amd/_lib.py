@@ -27,8 +27,9 @@ STATUS_NAMES = {
 }
 
 # Every function include/sscan.h declares.
-EXPORTED = ("sscan_fwd", "sscan_fwd_workspace", "sscan_bwd", "sscan_bwd_workspace", "sscan_decode",
-            "sscan_plan_select", "sscan_status_str", "sscan_last_error", "sscan_version")
+EXPORTED = ("sscan_fwd", "sscan_fwd_workspace", "sscan_bwd", "sscan_bwd_workspace", "sscan_mamba_fwd",
+            "sscan_mamba_bwd", "sscan_mamba_bwd_workspace", "sscan_decode", "sscan_plan_select",
+            "sscan_status_str", "sscan_last_error", "sscan_version")
 
 
 class sscan_desc(ctypes.Structure):
@@ -71,6 +72,12 @@ def load() -> ctypes.CDLL:
         lib.sscan_bwd.restype = i32
         lib.sscan_bwd_workspace.argtypes = [pdesc, pplan, ctypes.POINTER(sz)]
         lib.sscan_bwd_workspace.restype = i32
+        lib.sscan_mamba_fwd.argtypes = [pdesc, pplan] + [vp] * 10 + [vp, sz, vp]
+        lib.sscan_mamba_fwd.restype = i32
+        lib.sscan_mamba_bwd.argtypes = [pdesc, pplan] + [vp] * 17 + [vp, sz, vp]
+        lib.sscan_mamba_bwd.restype = i32
+        lib.sscan_mamba_bwd_workspace.argtypes = [pdesc, pplan, ctypes.POINTER(sz)]
+        lib.sscan_mamba_bwd_workspace.restype = i32
         lib.sscan_decode.argtypes = [pdesc] + [vp] * 8 + [vp]
         lib.sscan_decode.restype = i32
         lib.sscan_plan_select.argtypes = [pdesc, i32, pplan]

@@ -15,8 +15,9 @@ import torch
 from . import _lib
 from ._lib import SScanError, sscan_desc, sscan_plan
 
-__all__ = ["sscan_fwd", "sscan_bwd", "sscan_decode", "sscan_fwd_workspace", "sscan_bwd_workspace",
-           "sscan_plan_select", "sscan_version", "SelectiveScan", "selective_scan", "SScanError", "Plan"]
+__all__ = ["sscan_fwd", "sscan_bwd", "sscan_mamba_fwd", "sscan_mamba_bwd", "sscan_decode", "sscan_fwd_workspace",
+           "sscan_bwd_workspace", "sscan_mamba_bwd_workspace", "sscan_plan_select", "sscan_version",
+           "SelectiveScan", "selective_scan", "MambaScan", "mamba_scan", "SScanError", "Plan"]
 
 _IO = {torch.float32: _lib.SSCAN_F32, torch.bfloat16: _lib.SSCAN_BF16}
 
@@ -142,6 +143,16 @@ def sscan_bwd_workspace(B: int, T: int, D: int, DS: int, io: torch.dtype = torch
     return int(n.value)
 
 
+def sscan_mamba_bwd_workspace(B: int, T: int, D: int, DS: int, io: torch.dtype = torch.float32,
+                              plan: Optional[Plan] = None) -> int:
+    lib = _lib.load()
+    d = _desc(B, T, D, DS, _IO[io])
+    _, pp = _plan_ptr(plan)
+    n = ctypes.c_size_t(0)
+    _lib.check(lib.sscan_mamba_bwd_workspace(ctypes.byref(d), pp, ctypes.byref(n)))
+    return int(n.value)
+
+
 def _workspace(nbytes: int, device, given: Optional[torch.Tensor]):
     if nbytes == 0:
         return None, 0
@@ -163,6 +174,20 @@ def sscan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, b: torch.Te
     y (optional out): (B,T,D) of x's dtype; hT (optional out): (B,D,DS) fp32;
     H (optional out): (B,T,D,DS) fp32 per-step states.
     """
+    return _fwd_call(False, x, delta, A, b, c, None, h0, y, hT, H, return_H, plan, workspace)
+
+
+def sscan_mamba_fwd(x: torch.Tensor, delta_raw: torch.Tensor, A_log: torch.Tensor, b: torch.Tensor,
+                    c: torch.Tensor, Dskip: Optional[torch.Tensor] = None, h0: Optional[torch.Tensor] = None, *,
+                    y: Optional[torch.Tensor] = None, hT: Optional[torch.Tensor] = None,
+                    H: Optional[torch.Tensor] = None, return_H: bool = False, plan: Optional[Plan] = None,
+                    workspace: Optional[torch.Tensor] = None):
+    """Mamba-style wrapper: delta = softplus(delta_raw) (identity above 20), A = -exp(A_log),
+    y = scan + Dskip * x.  Same shapes and returns as ``sscan_fwd``; Dskip: (D,) fp32 or None."""
+    return _fwd_call(True, x, delta_raw, A_log, b, c, Dskip, h0, y, hT, H, return_H, plan, workspace)
+
+
+def _fwd_call(mamba, x, delta, A, b, c, Dskip, h0, y, hT, H, return_H, plan, workspace):
     lib = _lib.load()
     if x.dtype not in _IO:
         raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
@@ -178,11 +203,12 @@ def sscan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, b: torch.Te
     DS = A.shape[1]
     if tuple(delta.shape) != (B, T, D) or tuple(b.shape) != (B, T, DS) or tuple(c.shape) != (B, T, DS):
         raise ValueError("shape mismatch among x (B,T,D), delta (B,T,D), b and c (B,T,DS)")
-    _check_device(device, delta=delta, A=A, b=b, c=c, h0=h0, y=y, hT=hT, H=H)
+    _check_device(device, delta=delta, A=A, b=b, c=c, h0=h0, y=y, hT=hT, H=H, Dskip=Dskip)
     (x, delta), x_bs = _same_stride([x, delta], ["x", "delta"])
     (b, c), bc_bs = _same_stride([b, c], ["b", "c"])
     A = _f32_contig(A, (D, DS), "A")
     h0 = _f32_contig(h0, (B, D, DS), "h0")
+    Dskip = _f32_contig(Dskip, (D,), "Dskip")
     if y is None:
         y = torch.empty((B, T, D), dtype=x.dtype, device=device)
     elif y.dtype != x.dtype or tuple(y.shape) != (B, T, D):
@@ -202,8 +228,13 @@ def sscan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, b: torch.Te
     _lib.check(lib.sscan_fwd_workspace(ctypes.byref(d), pp, ctypes.byref(nws)))
     ws, wsn = _workspace(int(nws.value), device, workspace)
     with torch.cuda.device(device):
-        st = lib.sscan_fwd(ctypes.byref(d), pp, _ptr(x), _ptr(delta), _ptr(A), _ptr(b), _ptr(c), _ptr(h0), _ptr(y),
-                           _ptr(hT), _ptr(H), _ptr(ws), ctypes.c_size_t(wsn), _stream(device))
+        if mamba:
+            st = lib.sscan_mamba_fwd(ctypes.byref(d), pp, _ptr(x), _ptr(delta), _ptr(A), _ptr(b), _ptr(c),
+                                     _ptr(Dskip), _ptr(h0), _ptr(y), _ptr(hT), _ptr(H), _ptr(ws),
+                                     ctypes.c_size_t(wsn), _stream(device))
+        else:
+            st = lib.sscan_fwd(ctypes.byref(d), pp, _ptr(x), _ptr(delta), _ptr(A), _ptr(b), _ptr(c), _ptr(h0),
+                               _ptr(y), _ptr(hT), _ptr(H), _ptr(ws), ctypes.c_size_t(wsn), _stream(device))
     _lib.check(st)
     return (y, hT, H) if (return_H or H is not None) else (y, hT)
 
@@ -218,6 +249,24 @@ def sscan_bwd(dy: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: torch.T
     batch rows and steps.  H is the (B,T,D,DS) state tensor the forward materialised.
     ``out`` may supply the six contiguous float32 output tensors (gh0 may be None).
     """
+    return _bwd_call(False, dy, x, delta, A, b, c, None, h0, H, dhT, need_gh0, False, plan, workspace, out)
+
+
+def sscan_mamba_bwd(dy: torch.Tensor, x: torch.Tensor, delta_raw: torch.Tensor, A_log: torch.Tensor,
+                    b: torch.Tensor, c: torch.Tensor, Dskip: Optional[torch.Tensor], h0: Optional[torch.Tensor],
+                    H: torch.Tensor, dhT: Optional[torch.Tensor] = None, *, need_gh0: bool = True,
+                    need_gDskip: bool = True, plan: Optional[Plan] = None,
+                    workspace: Optional[torch.Tensor] = None, out: Optional[Tuple[torch.Tensor, ...]] = None):
+    """Backward of ``sscan_mamba_fwd``.  Returns (gx, gdelta_raw, gb, gc, gA_log, gh0, gDskip).
+
+    gDskip (D,) is the gradient for Dskip (sum over b, t of dy*x), also when Dskip is None;
+    None if not needed.  ``out`` may supply the seven outputs in that order.
+    """
+    return _bwd_call(True, dy, x, delta_raw, A_log, b, c, Dskip, h0, H, dhT, need_gh0, need_gDskip, plan,
+                     workspace, out)
+
+
+def _bwd_call(mamba, dy, x, delta, A, b, c, Dskip, h0, H, dhT, need_gh0, need_gD, plan, workspace, out):
     lib = _lib.load()
     if x.dtype not in _IO:
         raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
@@ -233,7 +282,8 @@ def sscan_bwd(dy: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: torch.T
         raise ValueError("dy and delta must have x's shape")
     if tuple(b.shape) != (B, T, DS) or tuple(c.shape) != (B, T, DS):
         raise ValueError("b and c must have shape (B,T,DS)")
-    _check_device(device, dy=dy, delta=delta, A=A, b=b, c=c, h0=h0, H=H, dhT=dhT)
+    _check_device(device, dy=dy, delta=delta, A=A, b=b, c=c, h0=h0, H=H, dhT=dhT, Dskip=Dskip)
+    Dskip = _f32_contig(Dskip, (D,), "Dskip")
     (x, delta, dy), x_bs = _same_stride([x, delta, dy], ["x", "delta", "dy"])
     (b, c), bc_bs = _same_stride([b, c], ["b", "c"])
     A = _f32_contig(A, (D, DS), "A")
@@ -241,11 +291,15 @@ def sscan_bwd(dy: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: torch.T
     dhT = _f32_contig(dhT, (B, D, DS), "dhT")
     H = _f32_contig(H, (B, T, D, DS), "H")
     f32 = dict(dtype=torch.float32, device=device)
+    gD = None
     if out is not None:
-        gx, gdelta, gb, gc, gA, gh0 = out
-        shapes = [(B, T, D), (B, T, D), (B, T, DS), (B, T, DS), (D, DS), (B, D, DS)]
-        for name, t, shp in zip(["gx", "gdelta", "gb", "gc", "gA", "gh0"], out, shapes):
-            if t is None and name == "gh0":
+        if mamba:
+            gx, gdelta, gb, gc, gA, gh0, gD = out
+        else:
+            gx, gdelta, gb, gc, gA, gh0 = out
+        shapes = [(B, T, D), (B, T, D), (B, T, DS), (B, T, DS), (D, DS), (B, D, DS), (D,)]
+        for name, t, shp in zip(["gx", "gdelta", "gb", "gc", "gA", "gh0", "gDskip"], out, shapes):
+            if t is None and name in ("gh0", "gDskip"):
                 continue
             if t is None or t.dtype != torch.float32 or tuple(t.shape) != shp or not t.is_contiguous() \
                     or t.device != device:
@@ -257,16 +311,26 @@ def sscan_bwd(dy: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: torch.T
         gc = torch.empty((B, T, DS), **f32)
         gA = torch.empty((D, DS), **f32)
         gh0 = torch.empty((B, D, DS), **f32) if need_gh0 else None
+        gD = torch.empty((D,), **f32) if (mamba and need_gD) else None
     d = _desc(B, T, D, DS, _IO[x.dtype], x_bs, bc_bs, 0)
     pc, pp = _plan_ptr(plan)
     nws = ctypes.c_size_t(0)
-    _lib.check(lib.sscan_bwd_workspace(ctypes.byref(d), pp, ctypes.byref(nws)))
+    query = lib.sscan_mamba_bwd_workspace if mamba else lib.sscan_bwd_workspace
+    _lib.check(query(ctypes.byref(d), pp, ctypes.byref(nws)))
     ws, wsn = _workspace(int(nws.value), device, workspace)
     with torch.cuda.device(device):
-        st = lib.sscan_bwd(ctypes.byref(d), pp, _ptr(dy), _ptr(dhT), _ptr(x), _ptr(delta), _ptr(A), _ptr(b), _ptr(c),
-                           _ptr(h0), _ptr(H), _ptr(gx), _ptr(gdelta), _ptr(gb), _ptr(gc), _ptr(gA), _ptr(gh0),
-                           _ptr(ws), ctypes.c_size_t(wsn), _stream(device))
+        if mamba:
+            st = lib.sscan_mamba_bwd(ctypes.byref(d), pp, _ptr(dy), _ptr(dhT), _ptr(x), _ptr(delta), _ptr(A),
+                                     _ptr(b), _ptr(c), _ptr(Dskip), _ptr(h0), _ptr(H), _ptr(gx), _ptr(gdelta),
+                                     _ptr(gA), _ptr(gb), _ptr(gc), _ptr(gD), _ptr(gh0), _ptr(ws),
+                                     ctypes.c_size_t(wsn), _stream(device))
+        else:
+            st = lib.sscan_bwd(ctypes.byref(d), pp, _ptr(dy), _ptr(dhT), _ptr(x), _ptr(delta), _ptr(A), _ptr(b),
+                               _ptr(c), _ptr(h0), _ptr(H), _ptr(gx), _ptr(gdelta), _ptr(gb), _ptr(gc), _ptr(gA),
+                               _ptr(gh0), _ptr(ws), ctypes.c_size_t(wsn), _stream(device))
     _lib.check(st)
+    if mamba:
+        return gx, gdelta, gb, gc, gA, gh0, gD
     return gx, gdelta, gb, gc, gA, gh0
 
 
@@ -354,3 +418,32 @@ class SelectiveScan(torch.autograd.Function):
 def selective_scan(x, delta, A, b, c, h0=None):
     """Autograd-aware forward: returns (y, hT)."""
     return SelectiveScan.apply(x, delta, A, b, c, h0)
+
+
+class MambaScan(torch.autograd.Function):
+    """Differentiable Mamba-style wrapper: (x, delta_raw, A_log, b, c, Dskip, h0) -> (y, hT)."""
+
+    @staticmethod
+    def forward(ctx, x, delta_raw, A_log, b, c, Dskip=None, h0=None):
+        y, hT, H = sscan_mamba_fwd(x, delta_raw, A_log, b, c, Dskip, h0, return_H=True)
+        ctx.save_for_backward(x, delta_raw, A_log, b, c, Dskip, h0, H)
+        ctx.has_h0 = h0 is not None
+        ctx.has_D = Dskip is not None
+        return y, hT
+
+    @staticmethod
+    def backward(ctx, dy, dhT):
+        x, delta_raw, A_log, b, c, Dskip, h0, H = ctx.saved_tensors
+        if dy is None:
+            dy = torch.zeros_like(x)
+        dy = dy.to(x.dtype)
+        gx, gdr, gb, gc, gAl, gh0, gD = sscan_mamba_bwd(dy, x, delta_raw, A_log, b, c, Dskip, h0, H,
+                                                        None if dhT is None else dhT.float().contiguous(),
+                                                        need_gh0=ctx.has_h0, need_gDskip=ctx.has_D)
+        return (gx.to(x.dtype), gdr.to(delta_raw.dtype), gAl, gb.to(b.dtype), gc.to(c.dtype),
+                gD if ctx.has_D else None, gh0 if ctx.has_h0 else None)
+
+
+def mamba_scan(x, delta_raw, A_log, b, c, Dskip=None, h0=None):
+    """Autograd-aware Mamba-style wrapper: returns (y, hT)."""
+    return MambaScan.apply(x, delta_raw, A_log, b, c, Dskip, h0)

@@ -61,6 +61,25 @@ __device__ __forceinline__ void buf_store_io(rsrc_t r, uint32_t off, float v) {
   buf_store_elem(r, off, v, static_cast<IO*>(nullptr));
 }
 
+// Mamba-style step size: the softplus of a raw value in the thresholded form of the
+// POPCORNBENCH page (the argument itself above 20, else log(1 + e^v)), and its
+// derivative (1 above the threshold, else the logistic 1 / (1 + e^-v)).  Both use the
+// hardware exp2 / log2 / reciprocal (about an ulp each): log(1 + e^v) is evaluated as
+// max(v, 0) + log1p(e^-|v|), with log1p(u) = u log(w) / (w - 1), w = 1 + u (Kahan's
+// formula: w - 1 is exact, and the ratio cancels the rounding of w), so the result stays
+// within a few ulps for every v, including far below 0 where log(1 + e^v) ~ e^v.
+constexpr float kSoftplusThreshold = 20.f;
+constexpr float kLn2 = 0.6931471805599453f;
+__device__ __forceinline__ float softplus_th(float v) {
+  const float u = __builtin_amdgcn_exp2f(-fabsf(v) * kLog2e);  // e^-|v| in (0, 1]
+  const float w = 1.f + u;
+  const float l = (w == 1.f) ? u : __builtin_amdgcn_logf(w) * kLn2 * u * __builtin_amdgcn_rcpf(w - 1.f);
+  return v > kSoftplusThreshold ? v : fmaxf(v, 0.f) + l;
+}
+__device__ __forceinline__ float softplus_th_grad(float v) {
+  return v > kSoftplusThreshold ? 1.f : __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-v * kLog2e));
+}
+
 // Cache-policy operand of a buffer instruction with the non-temporal bit set: the data
 // is streamed out and not kept in the caches.  For the materialised states, written once
 // and read back only by the backward, this raises the sustained HBM write rate markedly.

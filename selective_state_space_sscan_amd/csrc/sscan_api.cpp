@@ -153,12 +153,13 @@ FwdLayout fwd_layout(const Resolved& r, int chunks) {
 }
 
 struct BwdLayout {
-  size_t bc_off, a_off, pairs_off, gin_off, total;
+  size_t bc_off, a_off, pairs_off, gin_off, d_off, total;
   int64_t ntiles_d, chunk_len, chunks;
 };
 
 // Chunks of the reverse sweep are whole tiles long; the last one takes the remainder.
-BwdLayout bwd_layout(const Resolved& r, int lanes, int chunks) {
+// with_D: room for the Mamba wrapper's per-(chunk, batch row) partial sums of dy * x.
+BwdLayout bwd_layout(const Resolved& r, int lanes, int chunks, bool with_D) {
   BwdLayout L{};
   const int64_t cpw = kThreads / lanes;
   const int64_t tb = sscan::bwd_tile_steps(lanes);
@@ -170,7 +171,8 @@ BwdLayout bwd_layout(const Resolved& r, int lanes, int chunks) {
   L.a_off = align_up((size_t)(L.ntiles_d * r.B * r.T * r.DS) * sizeof(float2), 256);
   L.pairs_off = align_up(L.a_off + (size_t)L.chunks * nstate * sizeof(float), 256);
   L.gin_off = align_up(L.pairs_off + (size_t)(L.chunks - 1) * nstate * sizeof(float2), 256);
-  L.total = align_up(L.gin_off + (size_t)(L.chunks - 1) * nstate * sizeof(float), 256);
+  L.d_off = align_up(L.gin_off + (size_t)(L.chunks - 1) * nstate * sizeof(float), 256);
+  L.total = with_D ? align_up(L.d_off + (size_t)(L.chunks * r.B * r.D) * sizeof(float), 256) : L.d_off;
   return L;
 }
 
@@ -185,6 +187,166 @@ bool misaligned(const void* p, size_t a) { return p != nullptr && (reinterpret_c
 
 int hip_fail(hipError_t e, const char* what) {
   return fail(SSCAN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// The forward, plain (mamba = false) or wrapped: delta holds delta_raw, A holds A_log and
+// Dskip (may be null) adds the skip term.
+int fwd_impl(bool mamba, const sscan_desc* desc, const sscan_plan* plan, const void* x, const void* delta,
+             const float* A, const void* b, const void* c, const float* Dskip, const float* h0, void* y, float* hT,
+             float* H, void* ws, size_t ws_bytes, hipStream_t stream) {
+  Resolved r;
+  int st = resolve_desc(desc, &r);
+  if (st != SSCAN_OK) return st;
+  int lanes, chunks;
+  st = resolve_plan(r, plan, false, &lanes, &chunks);
+  if (st != SSCAN_OK) return st;
+  if (r.B == 0 || r.D == 0) return ok();
+  const bool steps = r.T > 0;
+  if (steps && (x == nullptr || delta == nullptr || A == nullptr || b == nullptr || c == nullptr || y == nullptr))
+    return fail(SSCAN_ERR_NULL, "x, delta, A, b, c and y are required when T > 0");
+  const size_t es = r.io_size;
+  if (misaligned(x, es) || misaligned(delta, es) || misaligned(b, es) || misaligned(c, es) || misaligned(y, es))
+    return fail(SSCAN_ERR_ALIGN, "io tensors must be aligned to their element size");
+  if (misaligned(A, 16) || misaligned(h0, 16) || misaligned(hT, 16) || misaligned(H, 16))
+    return fail(SSCAN_ERR_ALIGN, "A, h0, hT and H must be 16-byte aligned");
+  if (misaligned(Dskip, 4)) return fail(SSCAN_ERR_ALIGN, "Dskip must be 4-byte aligned");
+  if (!steps) {
+    if (hT == nullptr) return ok();
+    const hipError_t e = sscan::launch_copy_or_zero(hT, h0, r.B * r.D * r.DS, stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "hT <- h0");
+  }
+  const FwdLayout lay = fwd_layout(r, chunks);
+  if (lay.total > 0) {
+    if (ws == nullptr || ws_bytes < lay.total)
+      return fail(SSCAN_ERR_WORKSPACE, "forward needs %zu workspace bytes, got %zu", lay.total, ws_bytes);
+    if (misaligned(ws, 16)) return fail(SSCAN_ERR_ALIGN, "workspace must be 16-byte aligned");
+  }
+
+  sscan::FwdParams p{};
+  p.x = x; p.delta = delta; p.A = A; p.b = b; p.c = c; p.h0 = h0; p.y = y; p.hT = hT; p.H = H;
+  p.Dskip = mamba ? Dskip : nullptr;
+  p.x_bs = r.x_bs; p.bc_bs = r.bc_bs; p.y_bs = r.y_bs;
+  p.B = (int32_t)r.B; p.T = (int32_t)r.T; p.D = (int32_t)r.D;
+  p.chunks = chunks;
+  p.chunk_len = (int32_t)ceil_div(r.T, chunks);
+  const int64_t cpw = kThreads / lanes;
+  const int64_t ntiles_d = ceil_div(r.D, cpw);
+  p.ntiles_d = (int32_t)ntiles_d;
+  p.xcd_group = xcd_group(lanes, r.io_size);
+  if (ntiles_d * r.B * chunks > std::numeric_limits<int32_t>::max())
+    return fail(SSCAN_ERR_UNSUPPORTED, "too many workgroups");
+  hipError_t e;
+  if (chunks > 1) {
+    char* wsb = static_cast<char*>(ws);
+    p.pairs = reinterpret_cast<float2*>(wsb + lay.pairs_off);
+    p.hin = reinterpret_cast<const float*>(wsb + lay.hin_off);
+    e = sscan::launch_fwd(r.io, (int)r.DS, lanes, true, mamba, p, (unsigned)(ntiles_d * r.B * (chunks - 1)), stream);
+    if (e != hipSuccess) return hip_fail(e, "forward local pass");
+    sscan::CarryParams cp{};
+    cp.pairs = p.pairs;
+    cp.h0 = h0;
+    cp.hin = reinterpret_cast<float*>(wsb + lay.hin_off);
+    cp.n = r.B * r.D * r.DS;
+    cp.chunks = chunks;
+    e = sscan::launch_carry(cp, stream);
+    if (e != hipSuccess) return hip_fail(e, "chunk carry");
+  }
+  e = sscan::launch_fwd(r.io, (int)r.DS, lanes, false, mamba, p, (unsigned)(ntiles_d * r.B * chunks), stream);
+  if (e != hipSuccess) return hip_fail(e, "forward pass");
+  return ok();
+}
+
+// The backward, plain or wrapped (then gdelta is for delta_raw, gA for A_log, gx includes
+// dy * Dskip, and gD, if not null, receives the gradient for Dskip).
+int bwd_impl(bool mamba, const sscan_desc* desc, const sscan_plan* plan, const void* dy, const float* dhT,
+             const void* x, const void* delta, const float* A, const void* b, const void* c, const float* Dskip,
+             const float* h0, const float* H, float* gx, float* gdelta, float* gb, float* gc, float* gA, float* gD,
+             float* gh0, void* ws, size_t ws_bytes, hipStream_t stream) {
+  Resolved r;
+  int st = resolve_desc(desc, &r);
+  if (st != SSCAN_OK) return st;
+  int lanes, chunks;
+  st = resolve_plan(r, plan, true, &lanes, &chunks);
+  if (st != SSCAN_OK) return st;
+  const bool steps = r.T > 0 && r.B > 0;
+  if (r.D > 0 && gA == nullptr) return fail(SSCAN_ERR_NULL, "gA is required");
+  if (steps && r.D > 0 &&
+      (dy == nullptr || x == nullptr || delta == nullptr || A == nullptr || b == nullptr || c == nullptr ||
+       H == nullptr || gx == nullptr || gdelta == nullptr || gb == nullptr || gc == nullptr))
+    return fail(SSCAN_ERR_NULL, "dy, x, delta, A, b, c, H, gx, gdelta, gb and gc are required when T > 0");
+  if (steps && r.D == 0 && (gb == nullptr || gc == nullptr))
+    return fail(SSCAN_ERR_NULL, "gb and gc are required when T > 0");
+  const size_t es = r.io_size;
+  if (misaligned(dy, es) || misaligned(x, es) || misaligned(delta, es) || misaligned(b, es) || misaligned(c, es))
+    return fail(SSCAN_ERR_ALIGN, "io tensors must be aligned to their element size");
+  if (misaligned(gx, 4) || misaligned(gdelta, 4) || misaligned(gb, 4) || misaligned(gc, 4) || misaligned(gD, 4) ||
+      misaligned(Dskip, 4))
+    return fail(SSCAN_ERR_ALIGN, "gradient tensors and Dskip must be 4-byte aligned");
+  if (!mamba) gD = nullptr;
+  if (misaligned(A, 16) || misaligned(h0, 16) || misaligned(H, 16) || misaligned(dhT, 16) || misaligned(gA, 16) ||
+      misaligned(gh0, 16))
+    return fail(SSCAN_ERR_ALIGN, "A, h0, H, dhT, gA and gh0 must be 16-byte aligned");
+
+  if (!steps || r.D == 0) {
+    // No step to sweep: gA = 0, gh0 = dhT (zeros if absent); gb, gc over D = 0 channels are 0.
+    hipError_t e = sscan::launch_fill(gA, r.D * r.DS, stream);
+    if (e == hipSuccess && gD != nullptr) e = sscan::launch_fill(gD, r.D, stream);  // no step: sum of nothing
+    if (e == hipSuccess && gh0 != nullptr) e = sscan::launch_copy_or_zero(gh0, dhT, r.B * r.D * r.DS, stream);
+    if (e == hipSuccess && steps && r.D == 0) {
+      e = sscan::launch_fill(gb, r.B * r.T * r.DS, stream);
+      if (e == hipSuccess) e = sscan::launch_fill(gc, r.B * r.T * r.DS, stream);
+    }
+    return e == hipSuccess ? ok() : hip_fail(e, "backward without steps");
+  }
+
+  const BwdLayout lay = bwd_layout(r, lanes, chunks, mamba);
+  if (ws == nullptr || ws_bytes < lay.total)
+    return fail(SSCAN_ERR_WORKSPACE, "backward needs %zu workspace bytes, got %zu", lay.total, ws_bytes);
+  if (misaligned(ws, 16)) return fail(SSCAN_ERR_ALIGN, "workspace must be 16-byte aligned");
+
+  char* wsb = static_cast<char*>(ws);
+  sscan::BwdParams p{};
+  p.dy = dy; p.dhT = dhT; p.x = x; p.delta = delta; p.A = A; p.b = b; p.c = c; p.h0 = h0; p.H = H;
+  p.gx = gx; p.gdelta = gdelta; p.gh0 = gh0;
+  p.part_bc = reinterpret_cast<float2*>(wsb + lay.bc_off);
+  p.part_A = reinterpret_cast<float*>(wsb + lay.a_off);
+  p.pairs = reinterpret_cast<float2*>(wsb + lay.pairs_off);
+  p.gin = reinterpret_cast<const float*>(wsb + lay.gin_off);
+  p.Dskip = mamba ? Dskip : nullptr;
+  p.part_D = gD != nullptr ? reinterpret_cast<float*>(wsb + lay.d_off) : nullptr;
+  p.chunk_len = (int32_t)lay.chunk_len;
+  p.chunks = (int32_t)lay.chunks;
+  p.x_bs = r.x_bs; p.bc_bs = r.bc_bs; p.y_bs = r.y_bs;
+  p.B = (int32_t)r.B; p.T = (int32_t)r.T; p.D = (int32_t)r.D;
+  p.ntiles_d = (int32_t)lay.ntiles_d;
+  p.xcd_group = xcd_group(lanes, r.io_size);
+  if (lay.ntiles_d * r.B * lay.chunks > std::numeric_limits<int32_t>::max())
+    return fail(SSCAN_ERR_UNSUPPORTED, "too many workgroups");
+  hipError_t e;
+  if (lay.chunks > 1) {
+    e = sscan::launch_bwd(r.io, (int)r.DS, lanes, true, mamba, p, (unsigned)(lay.ntiles_d * r.B * (lay.chunks - 1)),
+                          stream);
+    if (e != hipSuccess) return hip_fail(e, "backward local pass");
+    sscan::BwdCarryParams cp{};
+    cp.pairs = p.pairs;
+    cp.dhT = dhT;
+    cp.gin = reinterpret_cast<float*>(wsb + lay.gin_off);
+    cp.n = r.B * r.D * r.DS;
+    cp.chunks = (int32_t)lay.chunks;
+    e = sscan::launch_bwd_carry(cp, stream);
+    if (e != hipSuccess) return hip_fail(e, "backward chunk carry");
+  }
+  e = sscan::launch_bwd(r.io, (int)r.DS, lanes, false, mamba, p, (unsigned)(lay.ntiles_d * r.B * lay.chunks), stream);
+  if (e != hipSuccess) return hip_fail(e, "backward sweep");
+  sscan::ReduceParams q{};
+  q.part_bc = p.part_bc; q.part_A = p.part_A; q.gb = gb; q.gc = gc; q.gA = gA;
+  q.A_log = mamba ? A : nullptr;
+  q.part_D = p.part_D;
+  q.gD = gD;
+  q.B = p.B; q.T = p.T; q.D = p.D; q.DS = (int32_t)r.DS; q.ntiles_d = p.ntiles_d; q.chunks = p.chunks;
+  e = sscan::launch_bwd_reduce(q, stream);
+  if (e != hipSuccess) return hip_fail(e, "backward reduce");
+  return ok();
 }
 
 }  // namespace
@@ -243,153 +405,48 @@ int sscan_bwd_workspace(const sscan_desc* desc, const sscan_plan* plan, size_t* 
   int lanes, chunks;
   st = resolve_plan(r, plan, true, &lanes, &chunks);
   if (st != SSCAN_OK) return st;
-  *bytes = (r.B == 0 || r.D == 0 || r.T == 0) ? 0 : bwd_layout(r, lanes, chunks).total;
+  *bytes = (r.B == 0 || r.D == 0 || r.T == 0) ? 0 : bwd_layout(r, lanes, chunks, false).total;
+  return ok();
+}
+
+int sscan_mamba_bwd_workspace(const sscan_desc* desc, const sscan_plan* plan, size_t* bytes) {
+  Resolved r;
+  int st = resolve_desc(desc, &r);
+  if (st != SSCAN_OK) return st;
+  if (bytes == nullptr) return fail(SSCAN_ERR_NULL, "bytes is NULL");
+  int lanes, chunks;
+  st = resolve_plan(r, plan, true, &lanes, &chunks);
+  if (st != SSCAN_OK) return st;
+  *bytes = (r.B == 0 || r.D == 0 || r.T == 0) ? 0 : bwd_layout(r, lanes, chunks, true).total;
   return ok();
 }
 
 int sscan_fwd(const sscan_desc* desc, const sscan_plan* plan, const void* x, const void* delta, const float* A,
               const void* b, const void* c, const float* h0, void* y, float* hT, float* H, void* ws, size_t ws_bytes,
               hipStream_t stream) {
-  Resolved r;
-  int st = resolve_desc(desc, &r);
-  if (st != SSCAN_OK) return st;
-  int lanes, chunks;
-  st = resolve_plan(r, plan, false, &lanes, &chunks);
-  if (st != SSCAN_OK) return st;
-  if (r.B == 0 || r.D == 0) return ok();
-  const bool steps = r.T > 0;
-  if (steps && (x == nullptr || delta == nullptr || A == nullptr || b == nullptr || c == nullptr || y == nullptr))
-    return fail(SSCAN_ERR_NULL, "x, delta, A, b, c and y are required when T > 0");
-  const size_t es = r.io_size;
-  if (misaligned(x, es) || misaligned(delta, es) || misaligned(b, es) || misaligned(c, es) || misaligned(y, es))
-    return fail(SSCAN_ERR_ALIGN, "io tensors must be aligned to their element size");
-  if (misaligned(A, 16) || misaligned(h0, 16) || misaligned(hT, 16) || misaligned(H, 16))
-    return fail(SSCAN_ERR_ALIGN, "A, h0, hT and H must be 16-byte aligned");
-  if (!steps) {
-    if (hT == nullptr) return ok();
-    const hipError_t e = sscan::launch_copy_or_zero(hT, h0, r.B * r.D * r.DS, stream);
-    return e == hipSuccess ? ok() : hip_fail(e, "hT <- h0");
-  }
-  const FwdLayout lay = fwd_layout(r, chunks);
-  if (lay.total > 0) {
-    if (ws == nullptr || ws_bytes < lay.total)
-      return fail(SSCAN_ERR_WORKSPACE, "forward needs %zu workspace bytes, got %zu", lay.total, ws_bytes);
-    if (misaligned(ws, 16)) return fail(SSCAN_ERR_ALIGN, "workspace must be 16-byte aligned");
-  }
+  return fwd_impl(false, desc, plan, x, delta, A, b, c, nullptr, h0, y, hT, H, ws, ws_bytes, stream);
+}
 
-  sscan::FwdParams p{};
-  p.x = x; p.delta = delta; p.A = A; p.b = b; p.c = c; p.h0 = h0; p.y = y; p.hT = hT; p.H = H;
-  p.x_bs = r.x_bs; p.bc_bs = r.bc_bs; p.y_bs = r.y_bs;
-  p.B = (int32_t)r.B; p.T = (int32_t)r.T; p.D = (int32_t)r.D;
-  p.chunks = chunks;
-  p.chunk_len = (int32_t)ceil_div(r.T, chunks);
-  const int64_t cpw = kThreads / lanes;
-  const int64_t ntiles_d = ceil_div(r.D, cpw);
-  p.ntiles_d = (int32_t)ntiles_d;
-  p.xcd_group = xcd_group(lanes, r.io_size);
-  if (ntiles_d * r.B * chunks > std::numeric_limits<int32_t>::max())
-    return fail(SSCAN_ERR_UNSUPPORTED, "too many workgroups");
-  hipError_t e;
-  if (chunks > 1) {
-    char* wsb = static_cast<char*>(ws);
-    p.pairs = reinterpret_cast<float2*>(wsb + lay.pairs_off);
-    p.hin = reinterpret_cast<const float*>(wsb + lay.hin_off);
-    e = sscan::launch_fwd(r.io, (int)r.DS, lanes, true, p, (unsigned)(ntiles_d * r.B * (chunks - 1)), stream);
-    if (e != hipSuccess) return hip_fail(e, "forward local pass");
-    sscan::CarryParams cp{};
-    cp.pairs = p.pairs;
-    cp.h0 = h0;
-    cp.hin = reinterpret_cast<float*>(wsb + lay.hin_off);
-    cp.n = r.B * r.D * r.DS;
-    cp.chunks = chunks;
-    e = sscan::launch_carry(cp, stream);
-    if (e != hipSuccess) return hip_fail(e, "chunk carry");
-  }
-  e = sscan::launch_fwd(r.io, (int)r.DS, lanes, false, p, (unsigned)(ntiles_d * r.B * chunks), stream);
-  if (e != hipSuccess) return hip_fail(e, "forward pass");
-  return ok();
+int sscan_mamba_fwd(const sscan_desc* desc, const sscan_plan* plan, const void* x, const void* delta_raw,
+                    const float* A_log, const void* b, const void* c, const float* Dskip, const float* h0, void* y,
+                    float* hT, float* H, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return fwd_impl(true, desc, plan, x, delta_raw, A_log, b, c, Dskip, h0, y, hT, H, ws, ws_bytes, stream);
 }
 
 int sscan_bwd(const sscan_desc* desc, const sscan_plan* plan, const void* dy, const float* dhT, const void* x,
               const void* delta, const float* A, const void* b, const void* c, const float* h0, const float* H,
               float* gx, float* gdelta, float* gb, float* gc, float* gA, float* gh0, void* ws, size_t ws_bytes,
               hipStream_t stream) {
-  Resolved r;
-  int st = resolve_desc(desc, &r);
-  if (st != SSCAN_OK) return st;
-  int lanes, chunks;
-  st = resolve_plan(r, plan, true, &lanes, &chunks);
-  if (st != SSCAN_OK) return st;
-  const bool steps = r.T > 0 && r.B > 0;
-  if (r.D > 0 && gA == nullptr) return fail(SSCAN_ERR_NULL, "gA is required");
-  if (steps && r.D > 0 &&
-      (dy == nullptr || x == nullptr || delta == nullptr || A == nullptr || b == nullptr || c == nullptr ||
-       H == nullptr || gx == nullptr || gdelta == nullptr || gb == nullptr || gc == nullptr))
-    return fail(SSCAN_ERR_NULL, "dy, x, delta, A, b, c, H, gx, gdelta, gb and gc are required when T > 0");
-  if (steps && r.D == 0 && (gb == nullptr || gc == nullptr))
-    return fail(SSCAN_ERR_NULL, "gb and gc are required when T > 0");
-  const size_t es = r.io_size;
-  if (misaligned(dy, es) || misaligned(x, es) || misaligned(delta, es) || misaligned(b, es) || misaligned(c, es))
-    return fail(SSCAN_ERR_ALIGN, "io tensors must be aligned to their element size");
-  if (misaligned(gx, 4) || misaligned(gdelta, 4) || misaligned(gb, 4) || misaligned(gc, 4))
-    return fail(SSCAN_ERR_ALIGN, "gradient tensors must be 4-byte aligned");
-  if (misaligned(A, 16) || misaligned(h0, 16) || misaligned(H, 16) || misaligned(dhT, 16) || misaligned(gA, 16) ||
-      misaligned(gh0, 16))
-    return fail(SSCAN_ERR_ALIGN, "A, h0, H, dhT, gA and gh0 must be 16-byte aligned");
+  return bwd_impl(false, desc, plan, dy, dhT, x, delta, A, b, c, nullptr, h0, H, gx, gdelta, gb, gc, gA, nullptr,
+                  gh0, ws, ws_bytes, stream);
+}
 
-  if (!steps || r.D == 0) {
-    // No step to sweep: gA = 0, gh0 = dhT (zeros if absent); gb, gc over D = 0 channels are 0.
-    hipError_t e = sscan::launch_fill(gA, r.D * r.DS, stream);
-    if (e == hipSuccess && gh0 != nullptr) e = sscan::launch_copy_or_zero(gh0, dhT, r.B * r.D * r.DS, stream);
-    if (e == hipSuccess && steps && r.D == 0) {
-      e = sscan::launch_fill(gb, r.B * r.T * r.DS, stream);
-      if (e == hipSuccess) e = sscan::launch_fill(gc, r.B * r.T * r.DS, stream);
-    }
-    return e == hipSuccess ? ok() : hip_fail(e, "backward without steps");
-  }
-
-  const BwdLayout lay = bwd_layout(r, lanes, chunks);
-  if (ws == nullptr || ws_bytes < lay.total)
-    return fail(SSCAN_ERR_WORKSPACE, "backward needs %zu workspace bytes, got %zu", lay.total, ws_bytes);
-  if (misaligned(ws, 16)) return fail(SSCAN_ERR_ALIGN, "workspace must be 16-byte aligned");
-
-  char* wsb = static_cast<char*>(ws);
-  sscan::BwdParams p{};
-  p.dy = dy; p.dhT = dhT; p.x = x; p.delta = delta; p.A = A; p.b = b; p.c = c; p.h0 = h0; p.H = H;
-  p.gx = gx; p.gdelta = gdelta; p.gh0 = gh0;
-  p.part_bc = reinterpret_cast<float2*>(wsb + lay.bc_off);
-  p.part_A = reinterpret_cast<float*>(wsb + lay.a_off);
-  p.pairs = reinterpret_cast<float2*>(wsb + lay.pairs_off);
-  p.gin = reinterpret_cast<const float*>(wsb + lay.gin_off);
-  p.chunk_len = (int32_t)lay.chunk_len;
-  p.chunks = (int32_t)lay.chunks;
-  p.x_bs = r.x_bs; p.bc_bs = r.bc_bs; p.y_bs = r.y_bs;
-  p.B = (int32_t)r.B; p.T = (int32_t)r.T; p.D = (int32_t)r.D;
-  p.ntiles_d = (int32_t)lay.ntiles_d;
-  p.xcd_group = xcd_group(lanes, r.io_size);
-  if (lay.ntiles_d * r.B * lay.chunks > std::numeric_limits<int32_t>::max())
-    return fail(SSCAN_ERR_UNSUPPORTED, "too many workgroups");
-  hipError_t e;
-  if (lay.chunks > 1) {
-    e = sscan::launch_bwd(r.io, (int)r.DS, lanes, true, p, (unsigned)(lay.ntiles_d * r.B * (lay.chunks - 1)), stream);
-    if (e != hipSuccess) return hip_fail(e, "backward local pass");
-    sscan::BwdCarryParams cp{};
-    cp.pairs = p.pairs;
-    cp.dhT = dhT;
-    cp.gin = reinterpret_cast<float*>(wsb + lay.gin_off);
-    cp.n = r.B * r.D * r.DS;
-    cp.chunks = (int32_t)lay.chunks;
-    e = sscan::launch_bwd_carry(cp, stream);
-    if (e != hipSuccess) return hip_fail(e, "backward chunk carry");
-  }
-  e = sscan::launch_bwd(r.io, (int)r.DS, lanes, false, p, (unsigned)(lay.ntiles_d * r.B * lay.chunks), stream);
-  if (e != hipSuccess) return hip_fail(e, "backward sweep");
-  sscan::ReduceParams q{};
-  q.part_bc = p.part_bc; q.part_A = p.part_A; q.gb = gb; q.gc = gc; q.gA = gA;
-  q.B = p.B; q.T = p.T; q.D = p.D; q.DS = (int32_t)r.DS; q.ntiles_d = p.ntiles_d; q.chunks = p.chunks;
-  e = sscan::launch_bwd_reduce(q, stream);
-  if (e != hipSuccess) return hip_fail(e, "backward reduce");
-  return ok();
+int sscan_mamba_bwd(const sscan_desc* desc, const sscan_plan* plan, const void* dy, const float* dhT, const void* x,
+                    const void* delta_raw, const float* A_log, const void* b, const void* c, const float* Dskip,
+                    const float* h0, const float* H, float* gx, float* gdelta_raw, float* gA_log, float* gb,
+                    float* gc, float* gDskip, float* gh0, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return bwd_impl(true, desc, plan, dy, dhT, x, delta_raw, A_log, b, c, Dskip, h0, H, gx, gdelta_raw, gb, gc, gA_log,
+                  gDskip, gh0, ws, ws_bytes, stream);
 }
 
 int sscan_decode(const sscan_desc* desc, const void* x, const void* delta, const float* A, const void* b,

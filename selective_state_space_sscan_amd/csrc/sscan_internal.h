@@ -35,6 +35,7 @@ struct FwdParams {
   float* H;            // may be null
   float2* pairs;       // two-level scan: (decay product, local end state) per chunk, (C-1,B,D,DS)
   const float* hin;    // two-level scan: start state of chunks 1..C-1, (C-1,B,D,DS)
+  const float* Dskip;  // Mamba wrapper: per-channel skip weight (D,), may be null (no skip)
   int64_t x_bs;        // batch stride of x, delta (elements)
   int64_t bc_bs;       // batch stride of b, c (elements)
   int64_t y_bs;        // batch stride of y (elements)
@@ -70,6 +71,8 @@ struct BwdParams {
   float* part_A;       // (chunks, B, D, DS): per-(chunk, batch row) gA partial sums
   float2* pairs;       // two-level sweep: (decay product, local carry) of chunks 1..C-1, (C-1,B,D,DS)
   const float* gin;    // two-level sweep: carry entering chunks 0..C-2 from the right, (C-1,B,D,DS)
+  const float* Dskip;  // Mamba wrapper: per-channel skip weight (D,), may be null (zero)
+  float* part_D;       // Mamba wrapper: per-(chunk, batch row) partial sums of dy*x, (chunks,B,D), or null
   int64_t x_bs;        // x, delta, dy
   int64_t bc_bs;       // b, c
   int64_t y_bs;        // gx, gdelta
@@ -94,6 +97,9 @@ struct ReduceParams {
   float* gb;
   float* gc;
   float* gA;
+  const float* A_log;   // Mamba wrapper: gA is scaled by A = -exp(A_log) (gradient for A_log); null otherwise
+  const float* part_D;  // Mamba wrapper: (chunks, B, D) partials of dy*x, or null
+  float* gD;            // Mamba wrapper: gradient for Dskip (D,), or null
   int32_t B, T, D, DS;
   int32_t ntiles_d;
   int32_t chunks;
@@ -113,9 +119,21 @@ struct DecodeParams {
 };
 
 // Launchers (defined in the .hip translation units).  Each returns a hipError_t.
-hipError_t launch_fwd(int io, int DS, int lanes, bool local_pass, const FwdParams& p, unsigned blocks, hipStream_t s);
+// mamba: delta holds delta_raw (delta = softplus), A holds A_log (A = -exp(A_log)), and
+// the skip term Dskip * x is added to y (forward) or its gradients formed (backward).
+hipError_t launch_fwd(int io, int DS, int lanes, bool local_pass, bool mamba, const FwdParams& p, unsigned blocks,
+                      hipStream_t s);
+hipError_t launch_fwd_plain(int io, int DS, int lanes, bool local_pass, const FwdParams& p, unsigned blocks,
+                            hipStream_t s);
+hipError_t launch_fwd_mamba(int io, int DS, int lanes, bool local_pass, const FwdParams& p, unsigned blocks,
+                            hipStream_t s);
 hipError_t launch_carry(const CarryParams& p, hipStream_t s);
-hipError_t launch_bwd(int io, int DS, int lanes, bool local_pass, const BwdParams& p, unsigned blocks, hipStream_t s);
+hipError_t launch_bwd(int io, int DS, int lanes, bool local_pass, bool mamba, const BwdParams& p, unsigned blocks,
+                      hipStream_t s);
+hipError_t launch_bwd_plain(int io, int DS, int lanes, bool local_pass, const BwdParams& p, unsigned blocks,
+                            hipStream_t s);
+hipError_t launch_bwd_mamba(int io, int DS, int lanes, bool local_pass, const BwdParams& p, unsigned blocks,
+                            hipStream_t s);
 hipError_t launch_bwd_carry(const BwdCarryParams& p, hipStream_t s);
 hipError_t launch_bwd_reduce(const ReduceParams& p, hipStream_t s);
 hipError_t launch_decode(int io, int DS, const DecodeParams& p, hipStream_t s);
