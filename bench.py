@@ -203,6 +203,7 @@ def main() -> int:
     print(f"bench: step {step_ms:.4f} ms (fwd {f_avg:.4f}, bwd {b_avg:.4f})", file=sys.stderr, flush=True)
 
     mamba = None if args.no_fwd_only else bench_mamba(g, y, hT, H, outs, B, T, D, args.warmup, max(10, K // 2))
+    hfree = None if args.no_fwd_only else bench_hfree(g, y, hT, outs, B, T, D, DS, args.warmup, max(10, K // 2))
     fwd_only = None if args.no_fwd_only else bench_fwd_only(dev, args.warmup, max(5, K // 5))
     decode = None if args.no_fwd_only else bench_decode(dev, args.warmup, max(5, K // 5))
 
@@ -217,11 +218,53 @@ def main() -> int:
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "fwd+bwd B=8 T=2048 D=768 DS=16 fp32, H materialised, 6 gradients",
                    "B": B, "T": T, "D": D, "DS": DS, "io": "f32"},
-        "roofline": roofline, "cpu_baseline": cpu, "detail": detail, "mamba": mamba, "fwd_only": fwd_only,
+        "roofline": roofline, "cpu_baseline": cpu, "detail": detail, "hfree": hfree, "mamba": mamba,
+        "fwd_only": fwd_only,
         "decode": decode,
     }
     print(json.dumps(line))
     return 0
+
+
+def bench_hfree(g, y, hT, outs, B, T, D, DS, warmup, reps):
+    """The H-free path on the same workload: the forward keeps the state entering every
+    32-step block instead of H, the backward recomputes each tile's states from them."""
+    import torch
+
+    from selective_state_space_sscan_amd import sscan_bwd_ckpt, sscan_fwd_ckpt
+
+    dev = g["x"].device
+    hck = torch.empty((B, (T + 31) // 32, D, DS), dtype=torch.float32, device=dev)
+
+    def fwd():
+        sscan_fwd_ckpt(g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"], y=y, hT=hT, hck=hck)
+
+    def bwd():
+        sscan_bwd_ckpt(g["dy"], g["x"], g["delta"], g["A"], g["b"], g["c"], hck, None, out=outs)
+
+    for _ in range(warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    f_ms = b_ms = 0.0
+    for _ in range(reps):
+        ev[0].record()
+        fwd()
+        ev[1].record()
+        bwd()
+        ev[2].record()
+        torch.cuda.synchronize()
+        f_ms += ev[0].elapsed_time(ev[1])
+        b_ms += ev[1].elapsed_time(ev[2])
+    f_ms /= reps
+    b_ms /= reps
+    print(f"bench: H-free fwd {f_ms:.4f} ms, bwd {b_ms:.4f} ms", file=sys.stderr, flush=True)
+    return {"workload": f"fwd+bwd B={B} T={T} D={D} DS={DS} fp32 with boundary states every 32 steps instead of H "
+                        "(1/32 of its memory); the backward recomputes each tile's states",
+            "fwd_ms": f_ms, "bwd_ms": b_ms, "ms_per_step": f_ms + b_ms,
+            "elems_per_s": B * T * D / ((f_ms + b_ms) * 1e-3),
+            "state_bytes": hck.numel() * 4, "H_bytes": B * T * D * DS * 4}
 
 
 def bench_mamba(g, y, hT, H, outs, B, T, D, warmup, reps):

@@ -61,6 +61,13 @@ extern "C" {
 
 #define SSCAN_VERSION 1
 
+/* Steps between the boundary states kept by the H-free path (sscan_fwd_ckpt). */
+#define SSCAN_CKPT_STEPS 32
+
+/* Which inputs the checkpointed entry points take: the plain scan's (delta, A), or the
+ * Mamba-style wrapper's (delta_raw, A_log, Dskip) as in sscan_mamba_fwd. */
+typedef enum sscan_wrapper { SSCAN_WRAP_NONE = 0, SSCAN_WRAP_MAMBA = 1 } sscan_wrapper;
+
 /* Element type of x, delta, b, c, y, dy. */
 typedef enum sscan_dtype { SSCAN_F32 = 0, SSCAN_BF16 = 1 } sscan_dtype;
 
@@ -153,6 +160,36 @@ int sscan_mamba_bwd(const sscan_desc* desc, const sscan_plan* plan, const void* 
 
 /* Bytes of workspace sscan_mamba_bwd needs for (desc, plan) -> *bytes. */
 int sscan_mamba_bwd_workspace(const sscan_desc* desc, const sscan_plan* plan, size_t* bytes);
+
+/* H-free path, forward: the forward of sscan_fwd (wrapper SSCAN_WRAP_NONE) or of
+ * sscan_mamba_fwd (SSCAN_WRAP_MAMBA; then delta is delta_raw, A is A_log and Dskip is used)
+ * that keeps, instead of every state H, only the state entering each block of
+ * SSCAN_CKPT_STEPS steps, as the "ruDNN KDA chunk.rs" page keeps chunk boundary states
+ * (retain_boundaries) rather than a state history:
+ *     hck[b, k, d, n] = h[b, k*SSCAN_CKPT_STEPS - 1, d, n]   (h0, or zeros, for k = 0)
+ *   hck (B, ceil(T/SSCAN_CKPT_STEPS), D, DS) fp32, 16-byte aligned, required when there are
+ *   steps; 1/SSCAN_CKPT_STEPS of the memory and HBM writes of H.  Everything else as in
+ *   sscan_fwd / sscan_mamba_fwd, including the workspace query (sscan_fwd_workspace).
+ *   SSCAN_ERR_UNSUPPORTED for an unknown wrapper. */
+int sscan_fwd_ckpt(const sscan_desc* desc, const sscan_plan* plan, int wrapper, const void* x, const void* delta,
+                   const float* A, const void* b, const void* c, const float* Dskip, const float* h0, void* y,
+                   float* hT, float* hck, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* H-free path, backward: the gradients of sscan_bwd / sscan_mamba_bwd from the boundary
+ * states of sscan_fwd_ckpt instead of H.  Each SSCAN_CKPT_STEPS-step tile of the reverse
+ * sweep first recomputes its states from the boundary state at its start with the
+ * forward's own arithmetic (so they equal the forward's states bit for bit), then sweeps.
+ *   No h0 argument: hck[:, 0] is h0.  gDskip is used with SSCAN_WRAP_MAMBA only (NULL or
+ *   the gradient for Dskip, as in sscan_mamba_bwd).  Runs 8 or 16 lanes per channel, so it
+ *   needs DS >= 8 (SSCAN_ERR_UNSUPPORTED otherwise, or for plan.lanes < 8).
+ *   ws/ws_bytes: at least what sscan_bwd_ckpt_workspace reports for the same wrapper. */
+int sscan_bwd_ckpt(const sscan_desc* desc, const sscan_plan* plan, int wrapper, const void* dy, const float* dhT,
+                   const void* x, const void* delta, const float* A, const void* b, const void* c, const float* Dskip,
+                   const float* hck, float* gx, float* gdelta, float* gb, float* gc, float* gA, float* gDskip,
+                   float* gh0, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Bytes of workspace sscan_bwd_ckpt needs for (desc, plan, wrapper) -> *bytes. */
+int sscan_bwd_ckpt_workspace(const sscan_desc* desc, const sscan_plan* plan, int wrapper, size_t* bytes);
 
 /* One decode step (T = 1) on a state kept in device memory between calls: the recurrence
  * of the forward applied to a single token ("ruDNN KDA chunk.rs" page, chunk_kda: one

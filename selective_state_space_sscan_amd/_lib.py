@@ -28,8 +28,12 @@ STATUS_NAMES = {
 
 # Every function include/sscan.h declares.
 EXPORTED = ("sscan_fwd", "sscan_fwd_workspace", "sscan_bwd", "sscan_bwd_workspace", "sscan_mamba_fwd",
-            "sscan_mamba_bwd", "sscan_mamba_bwd_workspace", "sscan_decode", "sscan_plan_select",
-            "sscan_status_str", "sscan_last_error", "sscan_version")
+            "sscan_mamba_bwd", "sscan_mamba_bwd_workspace", "sscan_fwd_ckpt", "sscan_bwd_ckpt",
+            "sscan_bwd_ckpt_workspace", "sscan_decode", "sscan_plan_select", "sscan_status_str",
+            "sscan_last_error", "sscan_version")
+SSCAN_CKPT_STEPS = 32
+SSCAN_WRAP_NONE = 0
+SSCAN_WRAP_MAMBA = 1
 
 
 class sscan_desc(ctypes.Structure):
@@ -78,6 +82,12 @@ def load() -> ctypes.CDLL:
         lib.sscan_mamba_bwd.restype = i32
         lib.sscan_mamba_bwd_workspace.argtypes = [pdesc, pplan, ctypes.POINTER(sz)]
         lib.sscan_mamba_bwd_workspace.restype = i32
+        lib.sscan_fwd_ckpt.argtypes = [pdesc, pplan, i32] + [vp] * 10 + [vp, sz, vp]
+        lib.sscan_fwd_ckpt.restype = i32
+        lib.sscan_bwd_ckpt.argtypes = [pdesc, pplan, i32] + [vp] * 16 + [vp, sz, vp]
+        lib.sscan_bwd_ckpt.restype = i32
+        lib.sscan_bwd_ckpt_workspace.argtypes = [pdesc, pplan, i32, ctypes.POINTER(sz)]
+        lib.sscan_bwd_ckpt_workspace.restype = i32
         lib.sscan_decode.argtypes = [pdesc] + [vp] * 8 + [vp]
         lib.sscan_decode.restype = i32
         lib.sscan_plan_select.argtypes = [pdesc, i32, pplan]

@@ -15,7 +15,8 @@ import torch
 from . import _lib
 from ._lib import SScanError, sscan_desc, sscan_plan
 
-__all__ = ["sscan_fwd", "sscan_bwd", "sscan_mamba_fwd", "sscan_mamba_bwd", "sscan_decode", "sscan_fwd_workspace",
+__all__ = ["sscan_fwd", "sscan_bwd", "sscan_mamba_fwd", "sscan_mamba_bwd", "sscan_fwd_ckpt", "sscan_bwd_ckpt",
+           "sscan_decode", "sscan_fwd_workspace",
            "sscan_bwd_workspace", "sscan_mamba_bwd_workspace", "sscan_plan_select", "sscan_version",
            "SelectiveScan", "selective_scan", "MambaScan", "mamba_scan", "SScanError", "Plan"]
 
@@ -187,7 +188,20 @@ def sscan_mamba_fwd(x: torch.Tensor, delta_raw: torch.Tensor, A_log: torch.Tenso
     return _fwd_call(True, x, delta_raw, A_log, b, c, Dskip, h0, y, hT, H, return_H, plan, workspace)
 
 
-def _fwd_call(mamba, x, delta, A, b, c, Dskip, h0, y, hT, H, return_H, plan, workspace):
+def sscan_fwd_ckpt(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, b: torch.Tensor, c: torch.Tensor,
+                   h0: Optional[torch.Tensor] = None, *, mamba: bool = False, Dskip: Optional[torch.Tensor] = None,
+                   y: Optional[torch.Tensor] = None, hT: Optional[torch.Tensor] = None,
+                   hck: Optional[torch.Tensor] = None, plan: Optional[Plan] = None,
+                   workspace: Optional[torch.Tensor] = None):
+    """Forward keeping boundary states instead of H.  Returns (y, hT, hck).
+
+    hck: (B, ceil(T/32), D, DS) fp32, the state entering every 32-step block (hck[:, 0] = h0).
+    With ``mamba`` the inputs are the wrapper's (delta_raw, A_log, Dskip) as in sscan_mamba_fwd.
+    """
+    return _fwd_call(mamba, x, delta, A, b, c, Dskip, h0, y, hT, None, False, plan, workspace, ckpt=True, hck=hck)
+
+
+def _fwd_call(mamba, x, delta, A, b, c, Dskip, h0, y, hT, H, return_H, plan, workspace, ckpt=False, hck=None):
     lib = _lib.load()
     if x.dtype not in _IO:
         raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
@@ -222,13 +236,23 @@ def _fwd_call(mamba, x, delta, A, b, c, Dskip, h0, y, hT, H, return_H, plan, wor
         H = torch.empty((B, T, D, DS), dtype=torch.float32, device=device)
     if H is not None and (not H.is_contiguous() or tuple(H.shape) != (B, T, D, DS) or H.dtype != torch.float32):
         raise ValueError("H must be a contiguous (B,T,D,DS) float32 tensor")
+    if ckpt:
+        nck = (T + _lib.SSCAN_CKPT_STEPS - 1) // _lib.SSCAN_CKPT_STEPS
+        if hck is None:
+            hck = torch.empty((B, nck, D, DS), dtype=torch.float32, device=device)
+        elif not hck.is_contiguous() or tuple(hck.shape) != (B, nck, D, DS) or hck.dtype != torch.float32:
+            raise ValueError(f"hck must be a contiguous {(B, nck, D, DS)} float32 tensor")
     d = _desc(B, T, D, DS, _IO[x.dtype], x_bs, bc_bs, y_bs)
     pc, pp = _plan_ptr(plan)
     nws = ctypes.c_size_t(0)
     _lib.check(lib.sscan_fwd_workspace(ctypes.byref(d), pp, ctypes.byref(nws)))
     ws, wsn = _workspace(int(nws.value), device, workspace)
     with torch.cuda.device(device):
-        if mamba:
+        if ckpt:
+            st = lib.sscan_fwd_ckpt(ctypes.byref(d), pp, int(bool(mamba)), _ptr(x), _ptr(delta), _ptr(A), _ptr(b),
+                                    _ptr(c), _ptr(Dskip), _ptr(h0), _ptr(y), _ptr(hT), _ptr(hck), _ptr(ws),
+                                    ctypes.c_size_t(wsn), _stream(device))
+        elif mamba:
             st = lib.sscan_mamba_fwd(ctypes.byref(d), pp, _ptr(x), _ptr(delta), _ptr(A), _ptr(b), _ptr(c),
                                      _ptr(Dskip), _ptr(h0), _ptr(y), _ptr(hT), _ptr(H), _ptr(ws),
                                      ctypes.c_size_t(wsn), _stream(device))
@@ -236,6 +260,8 @@ def _fwd_call(mamba, x, delta, A, b, c, Dskip, h0, y, hT, H, return_H, plan, wor
             st = lib.sscan_fwd(ctypes.byref(d), pp, _ptr(x), _ptr(delta), _ptr(A), _ptr(b), _ptr(c), _ptr(h0),
                                _ptr(y), _ptr(hT), _ptr(H), _ptr(ws), ctypes.c_size_t(wsn), _stream(device))
     _lib.check(st)
+    if ckpt:
+        return y, hT, hck
     return (y, hT, H) if (return_H or H is not None) else (y, hT)
 
 
@@ -266,7 +292,20 @@ def sscan_mamba_bwd(dy: torch.Tensor, x: torch.Tensor, delta_raw: torch.Tensor, 
                      workspace, out)
 
 
-def _bwd_call(mamba, dy, x, delta, A, b, c, Dskip, h0, H, dhT, need_gh0, need_gD, plan, workspace, out):
+def sscan_bwd_ckpt(dy: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, b: torch.Tensor,
+                   c: torch.Tensor, hck: torch.Tensor, dhT: Optional[torch.Tensor] = None, *, mamba: bool = False,
+                   Dskip: Optional[torch.Tensor] = None, need_gh0: bool = True, need_gDskip: bool = True,
+                   plan: Optional[Plan] = None, workspace: Optional[torch.Tensor] = None,
+                   out: Optional[Tuple[torch.Tensor, ...]] = None):
+    """Backward from the boundary states of ``sscan_fwd_ckpt`` (no H).
+
+    Returns what ``sscan_bwd`` returns, or with ``mamba`` what ``sscan_mamba_bwd`` returns.
+    """
+    return _bwd_call(mamba, dy, x, delta, A, b, c, Dskip, None, None, dhT, need_gh0, need_gDskip and mamba, plan,
+                     workspace, out, hck=hck)
+
+
+def _bwd_call(mamba, dy, x, delta, A, b, c, Dskip, h0, H, dhT, need_gh0, need_gD, plan, workspace, out, hck=None):
     lib = _lib.load()
     if x.dtype not in _IO:
         raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
@@ -289,7 +328,14 @@ def _bwd_call(mamba, dy, x, delta, A, b, c, Dskip, h0, H, dhT, need_gh0, need_gD
     A = _f32_contig(A, (D, DS), "A")
     h0 = _f32_contig(h0, (B, D, DS), "h0")
     dhT = _f32_contig(dhT, (B, D, DS), "dhT")
-    H = _f32_contig(H, (B, T, D, DS), "H")
+    ckpt = hck is not None
+    if ckpt:
+        nck = (T + _lib.SSCAN_CKPT_STEPS - 1) // _lib.SSCAN_CKPT_STEPS
+        hck = _f32_contig(hck, (B, nck, D, DS), "hck")
+        if H is not None:
+            raise ValueError("H and hck are alternatives")
+    else:
+        H = _f32_contig(H, (B, T, D, DS), "H")
     f32 = dict(dtype=torch.float32, device=device)
     gD = None
     if out is not None:
@@ -315,11 +361,19 @@ def _bwd_call(mamba, dy, x, delta, A, b, c, Dskip, h0, H, dhT, need_gh0, need_gD
     d = _desc(B, T, D, DS, _IO[x.dtype], x_bs, bc_bs, 0)
     pc, pp = _plan_ptr(plan)
     nws = ctypes.c_size_t(0)
-    query = lib.sscan_mamba_bwd_workspace if mamba else lib.sscan_bwd_workspace
-    _lib.check(query(ctypes.byref(d), pp, ctypes.byref(nws)))
+    if ckpt:
+        _lib.check(lib.sscan_bwd_ckpt_workspace(ctypes.byref(d), pp, int(bool(mamba)), ctypes.byref(nws)))
+    else:
+        query = lib.sscan_mamba_bwd_workspace if mamba else lib.sscan_bwd_workspace
+        _lib.check(query(ctypes.byref(d), pp, ctypes.byref(nws)))
     ws, wsn = _workspace(int(nws.value), device, workspace)
     with torch.cuda.device(device):
-        if mamba:
+        if ckpt:
+            st = lib.sscan_bwd_ckpt(ctypes.byref(d), pp, int(bool(mamba)), _ptr(dy), _ptr(dhT), _ptr(x), _ptr(delta),
+                                    _ptr(A), _ptr(b), _ptr(c), _ptr(Dskip), _ptr(hck), _ptr(gx), _ptr(gdelta),
+                                    _ptr(gb), _ptr(gc), _ptr(gA), _ptr(gD), _ptr(gh0), _ptr(ws),
+                                    ctypes.c_size_t(wsn), _stream(device))
+        elif mamba:
             st = lib.sscan_mamba_bwd(ctypes.byref(d), pp, _ptr(dy), _ptr(dhT), _ptr(x), _ptr(delta), _ptr(A),
                                      _ptr(b), _ptr(c), _ptr(Dskip), _ptr(h0), _ptr(H), _ptr(gx), _ptr(gdelta),
                                      _ptr(gA), _ptr(gb), _ptr(gc), _ptr(gD), _ptr(gh0), _ptr(ws),
@@ -396,54 +450,70 @@ class SelectiveScan(torch.autograd.Function):
     """
 
     @staticmethod
-    def forward(ctx, x, delta, A, b, c, h0=None):
-        y, hT, H = sscan_fwd(x, delta, A, b, c, h0, return_H=True)
-        ctx.save_for_backward(x, delta, A, b, c, h0, H)
+    def forward(ctx, x, delta, A, b, c, h0=None, ckpt=False):
+        if ckpt:
+            y, hT, S = sscan_fwd_ckpt(x, delta, A, b, c, h0)
+        else:
+            y, hT, S = sscan_fwd(x, delta, A, b, c, h0, return_H=True)
+        ctx.save_for_backward(x, delta, A, b, c, h0, S)
         ctx.has_h0 = h0 is not None
+        ctx.ckpt = ckpt
         return y, hT
 
     @staticmethod
     def backward(ctx, dy, dhT):
-        x, delta, A, b, c, h0, H = ctx.saved_tensors
+        x, delta, A, b, c, h0, S = ctx.saved_tensors
         if dy is None:
             dy = torch.zeros_like(x)
         dy = dy.to(x.dtype)
-        gx, gdelta, gb, gc, gA, gh0 = sscan_bwd(dy, x, delta, A, b, c, h0, H,
-                                                None if dhT is None else dhT.float().contiguous(),
-                                                need_gh0=ctx.has_h0)
+        dhT = None if dhT is None else dhT.float().contiguous()
+        if ctx.ckpt:
+            gx, gdelta, gb, gc, gA, gh0 = sscan_bwd_ckpt(dy, x, delta, A, b, c, S, dhT, need_gh0=ctx.has_h0)
+        else:
+            gx, gdelta, gb, gc, gA, gh0 = sscan_bwd(dy, x, delta, A, b, c, h0, S, dhT, need_gh0=ctx.has_h0)
         return (gx.to(x.dtype), gdelta.to(delta.dtype), gA, gb.to(b.dtype), gc.to(c.dtype),
-                gh0 if ctx.has_h0 else None)
+                gh0 if ctx.has_h0 else None, None)
 
 
-def selective_scan(x, delta, A, b, c, h0=None):
-    """Autograd-aware forward: returns (y, hT)."""
-    return SelectiveScan.apply(x, delta, A, b, c, h0)
+def selective_scan(x, delta, A, b, c, h0=None, ckpt=False):
+    """Autograd-aware forward: returns (y, hT).  ``ckpt`` keeps boundary states instead of H
+    (1/32 of the memory; the backward recomputes the states)."""
+    return SelectiveScan.apply(x, delta, A, b, c, h0, ckpt)
 
 
 class MambaScan(torch.autograd.Function):
     """Differentiable Mamba-style wrapper: (x, delta_raw, A_log, b, c, Dskip, h0) -> (y, hT)."""
 
     @staticmethod
-    def forward(ctx, x, delta_raw, A_log, b, c, Dskip=None, h0=None):
-        y, hT, H = sscan_mamba_fwd(x, delta_raw, A_log, b, c, Dskip, h0, return_H=True)
-        ctx.save_for_backward(x, delta_raw, A_log, b, c, Dskip, h0, H)
+    def forward(ctx, x, delta_raw, A_log, b, c, Dskip=None, h0=None, ckpt=False):
+        if ckpt:
+            y, hT, S = sscan_fwd_ckpt(x, delta_raw, A_log, b, c, h0, mamba=True, Dskip=Dskip)
+        else:
+            y, hT, S = sscan_mamba_fwd(x, delta_raw, A_log, b, c, Dskip, h0, return_H=True)
+        ctx.save_for_backward(x, delta_raw, A_log, b, c, Dskip, h0, S)
         ctx.has_h0 = h0 is not None
         ctx.has_D = Dskip is not None
+        ctx.ckpt = ckpt
         return y, hT
 
     @staticmethod
     def backward(ctx, dy, dhT):
-        x, delta_raw, A_log, b, c, Dskip, h0, H = ctx.saved_tensors
+        x, delta_raw, A_log, b, c, Dskip, h0, S = ctx.saved_tensors
         if dy is None:
             dy = torch.zeros_like(x)
         dy = dy.to(x.dtype)
-        gx, gdr, gb, gc, gAl, gh0, gD = sscan_mamba_bwd(dy, x, delta_raw, A_log, b, c, Dskip, h0, H,
-                                                        None if dhT is None else dhT.float().contiguous(),
-                                                        need_gh0=ctx.has_h0, need_gDskip=ctx.has_D)
+        dhT = None if dhT is None else dhT.float().contiguous()
+        if ctx.ckpt:
+            gx, gdr, gb, gc, gAl, gh0, gD = sscan_bwd_ckpt(dy, x, delta_raw, A_log, b, c, S, dhT, mamba=True,
+                                                           Dskip=Dskip, need_gh0=ctx.has_h0,
+                                                           need_gDskip=ctx.has_D)
+        else:
+            gx, gdr, gb, gc, gAl, gh0, gD = sscan_mamba_bwd(dy, x, delta_raw, A_log, b, c, Dskip, h0, S, dhT,
+                                                            need_gh0=ctx.has_h0, need_gDskip=ctx.has_D)
         return (gx.to(x.dtype), gdr.to(delta_raw.dtype), gAl, gb.to(b.dtype), gc.to(c.dtype),
-                gD if ctx.has_D else None, gh0 if ctx.has_h0 else None)
+                gD if ctx.has_D else None, gh0 if ctx.has_h0 else None, None)
 
 
-def mamba_scan(x, delta_raw, A_log, b, c, Dskip=None, h0=None):
-    """Autograd-aware Mamba-style wrapper: returns (y, hT)."""
-    return MambaScan.apply(x, delta_raw, A_log, b, c, Dskip, h0)
+def mamba_scan(x, delta_raw, A_log, b, c, Dskip=None, h0=None, ckpt=False):
+    """Autograd-aware Mamba-style wrapper: returns (y, hT); ``ckpt`` as in selective_scan."""
+    return MambaScan.apply(x, delta_raw, A_log, b, c, Dskip, h0, ckpt)

@@ -55,8 +55,8 @@ __global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(const ReduceParams
 
 hipError_t launch_bwd_plain(int io, int DS, int lanes, bool local_pass, const BwdParams& p, unsigned grid,
                             hipStream_t s) {
-  if (io == 0) return launch_bwd_io<float, false>(DS, lanes, local_pass, p, grid, s);
-  return launch_bwd_io<bf16_t, false>(DS, lanes, local_pass, p, grid, s);
+  if (io == 0) return launch_bwd_io<float, false, false>(DS, lanes, local_pass, p, grid, s);
+  return launch_bwd_io<bf16_t, false, false>(DS, lanes, local_pass, p, grid, s);
 }
 
 hipError_t launch_bwd(int io, int DS, int lanes, bool local_pass, bool mamba, const BwdParams& p, unsigned grid,

@@ -95,8 +95,12 @@ __device__ __forceinline__ void reduce_scatter(float (&v)[V], int j, int& idx0) 
 // MAMBA: the Mamba-style wrapper -- delta is read as delta_raw (delta = softplus, whose
 // derivative scales gdelta), A as A_log (A = -exp(A_log)), the skip term adds dy * Dskip
 // to gx, and each workgroup leaves a partial sum of dy * x per channel for gDskip.
-template <typename IO, int DS, int L, bool MAMBA>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 16 && L == 16 ? 3 : (DS / L >= 8 ? 1 : 2)))) void bwd_kernel(const BwdParams p) {
+// HF: the H-free sweep -- instead of reading H, each tile recomputes its states from the
+// boundary state saved by the forward at the tile's first step (tiles and checkpoint
+// blocks are both kCkptSteps long), with the forward's own arithmetic, so the states
+// are the forward's bit for bit.  They go to a per-wave LDS block that the sweep reads.
+template <typename IO, int DS, int L, bool MAMBA, bool HF>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 16 && L == 16 ? (HF ? 2 : 3) : (DS / L >= 8 ? 1 : 2)))) void bwd_kernel(const BwdParams p) {
   constexpr int K = DS / L;
   constexpr int CPW = kThreads / L;
   constexpr int TB = bwd_tile_steps(L);
@@ -113,6 +117,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
   constexpr uint32_t ES = sizeof(IO);
   static_assert(TILE % kThreads == 0 && TB % HB == 0 && HB % S == 0, "tile shape");
   static_assert(NITEM % 2 == 0, "items per batch must pair up");
+  static_assert(!HF || TB == kCkptSteps, "the H-free sweep takes one boundary block per tile");
 
   __shared__ float4 s_in[TILE];              // (delta, x, dy, delta*x) at [step*CPW + channel]
   __shared__ float s_b[BC];
@@ -150,7 +155,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
   const IO* crow = static_cast<const IO*>(p.c) + (int64_t)bb * p.bc_bs;
   float* gxrow = p.gx + (int64_t)bb * p.y_bs;
   float* gdrow = p.gdelta + (int64_t)bb * p.y_bs;
-  const float* Hrow = p.H + (int64_t)bb * T * D * DS;
+  const float* Hrow = HF ? nullptr : p.H + (int64_t)bb * T * D * DS;
   const int64_t soff = ((int64_t)bb * D + d) * DS + j * K;
   const uint32_t hstep = static_cast<uint32_t>(D) * DS * 4u;
 
@@ -165,7 +170,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
       load_k<K>(p.gin + (int64_t)chunk * nstate + soff, G);
     else if (p.dhT != nullptr)
       load_k<K>(p.dhT + soff, G);
-    if (t_hi > t_lo) load_k<K>(Hrow + (int64_t)(t_hi - 1) * D * DS + d * DS + j * K, hcur);
+    if (!HF && t_hi > t_lo) load_k<K>(Hrow + (int64_t)(t_hi - 1) * D * DS + d * DS + j * K, hcur);
   }
 #pragma unroll
   for (int i = 0; i < K; ++i) {
@@ -257,11 +262,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
   constexpr int DB = (HBLK * 4) % (64 * 16) == 0 ? 16 : 4;      // bytes per lane and load
   constexpr int NQ = HBLK * 4 / (64 * DB);                      // loads per block
   static_assert(NQ * 64 * DB == HBLK * 4, "an H block is a whole number of loads");
-  __shared__ float s_h[NWAVE * HBLK];
+  __shared__ float s_h[HF ? 1 : NWAVE * HBLK];
+  // H-free: rows 0..TB of a wave's block hold H_{ts-1} .. H_{ts+TB-1} of the current tile
+  __shared__ float s_hs[HF ? NWAVE * (TB + 1) * WROW : 1];
+  float* const hsw = s_hs + (HF ? wave * (TB + 1) * WROW : 0);
+  // boundary state of the next tile to sweep, loaded one tile ahead
+  float hck_next[K];
+  const float* ckrow = HF ? p.hck + (int64_t)bb * p.nck * D * DS : nullptr;
+  auto load_ckpt = [&](int ts, bool valid) {
+    const rsrc_t rK = make_rsrc(ckrow, valid ? static_cast<uint32_t>(p.nck) * D * DS * 4u : 0u);
+    const uint32_t off = dvalid ? static_cast<uint32_t>(((ts / kCkptSteps) * D + d) * DS + j * K) * 4u : kOutOfRange;
+    buf_load_vec<K>(rK, off, hck_next);
+  };
   const int wd0 = d0 + wave * (64 / L);                         // first channel of this wave
   const uint32_t wbytes = static_cast<uint32_t>(max(0, min(64 / L, D - wd0)) * DS * 4);
   const uint32_t whoff = static_cast<uint32_t>(wd0) * DS * 4u;
-  float* const hblk = s_h + wave * HBLK;
+  float* const hblk = s_h + (HF ? 0 : wave * HBLK);
   float hq[NQ][DB / 4];
   float hzero[K];
 #pragma unroll
@@ -296,7 +312,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
   if (ntiles > 0) {
     const int ts_last = t_lo + (ntiles - 1) * TB;
     load_tile(ts_last);
-    load_hblock(hq, ts_last + (NSUB - 1) * HB, true);
+    if constexpr (HF)
+      load_ckpt(ts_last, true);
+    else
+      load_hblock(hq, ts_last + (NSUB - 1) * HB, true);
     store_tile();
   }
 
@@ -308,13 +327,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
     __syncthreads();  // this tile's inputs are in LDS; the previous tile's output reads are done
     load_tile(ts - TB);
 
+    if constexpr (HF) {
+      // recompute the tile's states from its boundary state, as the forward formed them:
+      // a = exp2(delta * A log2 e), h = fma(a, h, (delta x) b); padded steps leave h as is
+      float hs[K];
+#pragma unroll
+      for (int i = 0; i < K; ++i) hs[i] = hck_next[i];
+      load_ckpt(ts - TB, it > 0);
+      store_state<K>(hsw + lane * K, hs);
+#pragma unroll
+      for (int t = 0; t < TB; ++t) {
+        const float4 in4 = s_in[t * CPW + ch];
+        float bv[K];
+        lds_load_vec<K>(&s_b[t * DS + j * K], bv);
+#pragma unroll
+        for (int i = 0; i < K; ++i) hs[i] = fmaf(exp2_hw(in4.x * A2[i]), hs[i], in4.w * bv[i]);
+        store_state<K>(hsw + (t + 1) * WROW + lane * K, hs);
+      }
+#pragma unroll
+      for (int i = 0; i < K; ++i) hcur[i] = hs[i];  // H_t of the tile's last step
+    }
+
 #pragma unroll
     for (int sb = NSUB - 1; sb >= 0; --sb) {
-      park_hblock(hq);  // this sub-block's H rows, loaded during the previous one
-      if (sb > 0)
-        load_hblock(hq, ts + (sb - 1) * HB, true);
-      else
-        load_hblock(hq, ts - TB + (NSUB - 1) * HB, it > 0);
+      if constexpr (!HF) {
+        park_hblock(hq);  // this sub-block's H rows, loaded during the previous one
+        if (sb > 0)
+          load_hblock(hq, ts + (sb - 1) * HB, true);
+        else
+          load_hblock(hq, ts - TB + (NSUB - 1) * HB, it > 0);
+      }
 
 #pragma unroll
       for (int bt = NBAT - 1; bt >= 0; --bt) {
@@ -343,8 +385,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
         float Sl[S], gdl[S], gbv[S][K], gcv[S][K];
         float hrow[S][K];  // H_{t-1} of the batch's steps
 #pragma unroll
-        for (int s = 0; s < S; ++s) lds_load_vec<K>(&hblk[(bt * S + s) * WROW + lane * K], hrow[s]);
-        if (bt == 0) {
+        for (int s = 0; s < S; ++s) {
+          if constexpr (HF)
+            lds_load_vec<K>(&hsw[(tt0 + s) * WROW + lane * K], hrow[s]);
+          else
+            lds_load_vec<K>(&hblk[(bt * S + s) * WROW + lane * K], hrow[s]);
+        }
+        if (!HF && bt == 0) {
           const bool first = ts + sb * HB == 0;  // step 0 of the sequence: H_{-1} = h0
 #pragma unroll
           for (int i = 0; i < K; ++i) hrow[0][i] = first ? hzero[i] : hrow[0][i];
@@ -620,36 +667,43 @@ __global__ __launch_bounds__(kThreads) void bwd_local_kernel(const BwdParams p) 
     pr[i] = make_float2(exp2_hw(static_cast<float>(static_cast<double>(A2[i]) * dsum)), G[i]);
 }
 
-template <typename IO, int DS, int L, bool MAMBA>
+// HF picks the H-free sweep; it exists only where the tile is one boundary block long.
+// The local pass of the two-level sweep reads no states and is the same for both.
+template <typename IO, int DS, int L, bool MAMBA, bool HF>
 hipError_t launch_bwd_t(bool local_pass, const BwdParams& p, unsigned blocks, hipStream_t s) {
-  if (local_pass)
+  if (local_pass) {
     hipLaunchKernelGGL((bwd_local_kernel<IO, DS, L, MAMBA>), dim3(blocks), dim3(kThreads), 0, s, p);
-  else
-    hipLaunchKernelGGL((bwd_kernel<IO, DS, L, MAMBA>), dim3(blocks), dim3(kThreads), 0, s, p);
-  return hipGetLastError();
+    return hipGetLastError();
+  }
+  if constexpr (HF && bwd_tile_steps(L) != kCkptSteps) {
+    return hipErrorInvalidValue;
+  } else {
+    hipLaunchKernelGGL((bwd_kernel<IO, DS, L, MAMBA, HF>), dim3(blocks), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+  }
 }
 
-template <typename IO, int DS, bool MAMBA>
+template <typename IO, int DS, bool MAMBA, bool HF>
 hipError_t launch_bwd_ds(int lanes, bool local_pass, const BwdParams& p, unsigned grid, hipStream_t s) {
   switch (lanes) {
-    case 1: return launch_bwd_t<IO, DS, 1, MAMBA>(local_pass, p, grid, s);
-    case 2: if constexpr (DS >= 2) return launch_bwd_t<IO, DS, 2, MAMBA>(local_pass, p, grid, s); break;
-    case 4: if constexpr (DS >= 4) return launch_bwd_t<IO, DS, 4, MAMBA>(local_pass, p, grid, s); break;
-    case 8: if constexpr (DS >= 8) return launch_bwd_t<IO, DS, 8, MAMBA>(local_pass, p, grid, s); break;
-    case 16: if constexpr (DS >= 16) return launch_bwd_t<IO, DS, 16, MAMBA>(local_pass, p, grid, s); break;
+    case 1: return launch_bwd_t<IO, DS, 1, MAMBA, HF>(local_pass, p, grid, s);
+    case 2: if constexpr (DS >= 2) return launch_bwd_t<IO, DS, 2, MAMBA, HF>(local_pass, p, grid, s); break;
+    case 4: if constexpr (DS >= 4) return launch_bwd_t<IO, DS, 4, MAMBA, HF>(local_pass, p, grid, s); break;
+    case 8: if constexpr (DS >= 8) return launch_bwd_t<IO, DS, 8, MAMBA, HF>(local_pass, p, grid, s); break;
+    case 16: if constexpr (DS >= 16) return launch_bwd_t<IO, DS, 16, MAMBA, HF>(local_pass, p, grid, s); break;
     default: break;
   }
   return hipErrorInvalidValue;
 }
 
-template <typename IO, bool MAMBA>
+template <typename IO, bool MAMBA, bool HF>
 hipError_t launch_bwd_io(int DS, int lanes, bool local_pass, const BwdParams& p, unsigned grid, hipStream_t s) {
   switch (DS) {
-    case 1: return launch_bwd_ds<IO, 1, MAMBA>(lanes, local_pass, p, grid, s);
-    case 2: return launch_bwd_ds<IO, 2, MAMBA>(lanes, local_pass, p, grid, s);
-    case 4: return launch_bwd_ds<IO, 4, MAMBA>(lanes, local_pass, p, grid, s);
-    case 8: return launch_bwd_ds<IO, 8, MAMBA>(lanes, local_pass, p, grid, s);
-    case 16: return launch_bwd_ds<IO, 16, MAMBA>(lanes, local_pass, p, grid, s);
+    case 1: return launch_bwd_ds<IO, 1, MAMBA, HF>(lanes, local_pass, p, grid, s);
+    case 2: return launch_bwd_ds<IO, 2, MAMBA, HF>(lanes, local_pass, p, grid, s);
+    case 4: return launch_bwd_ds<IO, 4, MAMBA, HF>(lanes, local_pass, p, grid, s);
+    case 8: return launch_bwd_ds<IO, 8, MAMBA, HF>(lanes, local_pass, p, grid, s);
+    case 16: return launch_bwd_ds<IO, 16, MAMBA, HF>(lanes, local_pass, p, grid, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -80,6 +80,20 @@ __device__ __forceinline__ float softplus_th_grad(float v) {
   return v > kSoftplusThreshold ? 1.f : __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-v * kLog2e));
 }
 
+// K consecutive floats to global memory or LDS (16-byte stores when K is a multiple of 4).
+template <int K>
+__device__ __forceinline__ void store_state(float* __restrict__ p, const float (&v)[K]) {
+  if constexpr (K % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < K / 4; ++q)
+      reinterpret_cast<float4*>(p)[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+  } else if constexpr (K == 2) {
+    *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+  } else {
+    p[0] = v[0];
+  }
+}
+
 // Cache-policy operand of a buffer instruction with the non-temporal bit set: the data
 // is streamed out and not kept in the caches.  For the materialised states, written once
 // and read back only by the backward, this raises the sustained HBM write rate markedly.

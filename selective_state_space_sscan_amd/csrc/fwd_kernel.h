@@ -32,19 +32,6 @@ __device__ __forceinline__ void load_state(const float* __restrict__ p, float (&
   lds_load_vec<K>(p, v);  // plain vector load; also valid for global memory
 }
 
-template <int K>
-__device__ __forceinline__ void store_state(float* __restrict__ p, const float (&v)[K]) {
-  if constexpr (K % 4 == 0) {
-#pragma unroll
-    for (int q = 0; q < K / 4; ++q)
-      reinterpret_cast<float4*>(p)[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
-  } else if constexpr (K == 2) {
-    *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
-  } else {
-    p[0] = v[0];
-  }
-}
-
 // Steps whose decays and injections are formed together before the serial update:
 // at most 32 floats per array per lane, at most 16 steps.
 template <int K, int TB>
@@ -212,6 +199,13 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(const FwdParams p) {
     const rsrc_t rH = make_rsrc(Hrow + (int64_t)ts * D * DS, static_cast<uint32_t>(rows) * hstep);
 #pragma unroll
     for (int s0 = 0; s0 < TB; s0 += S) {
+      if constexpr (MODE == kFull) {
+        // H-free path: the state entering every block of kCkptSteps steps (S divides it and
+        // every tile starts on a multiple of S, so each block start begins a batch).  Batches
+        // past the end of the chunk are padding: their block indices lie beyond the array.
+        if (p.hck != nullptr && dvalid && ts + s0 < t_end && ((ts + s0) % kCkptSteps) == 0)
+          store_state<K>(p.hck + (((int64_t)bb * p.nck + (ts + s0) / kCkptSteps) * D + d) * DS + j * K, h);
+      }
       // decays and injections of S steps: independent of the state, issued together
       float a[S][K], u[S][K];
       float dl[S];

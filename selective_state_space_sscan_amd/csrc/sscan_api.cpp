@@ -191,9 +191,32 @@ int hip_fail(hipError_t e, const char* what) {
 
 // The forward, plain (mamba = false) or wrapped: delta holds delta_raw, A holds A_log and
 // Dskip (may be null) adds the skip term.
+// The H-free sweep takes one boundary block per tile: lanes with kCkptSteps-step tiles
+// (8 or 16 lanes per channel, so DS >= 8).  Its LDS holds a tile of states, which allows
+// two workgroups per CU, and it measured fastest with more T-chunks than the sweep over H
+// (8x2048x768x16: 287 us with 4 chunks, 323 us with 2): the default aims at six waves'
+// worth of lanes per SIMD.
+int resolve_hf_plan(const Resolved& r, const sscan_plan* plan, int* lanes, int* chunks) {
+  if (r.DS < 8) return fail(SSCAN_ERR_UNSUPPORTED, "the H-free backward needs DS >= 8, got DS=%lld", (long long)r.DS);
+  if (plan != nullptr && plan->lanes != 0 && plan->lanes < 8)
+    return fail(SSCAN_ERR_UNSUPPORTED, "the H-free backward runs 8 or 16 lanes per channel, plan.lanes=%d",
+                plan->lanes);
+  if (*lanes < 8) *lanes = (int)(r.DS < 16 ? r.DS : 16);
+  if (plan == nullptr || plan->chunks == 0) {
+    const int64_t lanes_total = r.B * r.D * *lanes;
+    int64_t c = lanes_total > 0 ? ceil_div(6 * kLanesOneWavePerSimd, lanes_total) : 1;
+    const int64_t cap = r.T / (4 * sscan::kCkptSteps);
+    if (c > cap) c = cap;
+    if (c > 16) c = 16;
+    *chunks = c > 1 ? (int)c : 1;
+  }
+  return SSCAN_OK;
+}
+
+// hck (not null): instead of H, keep the state entering every kCkptSteps-step block.
 int fwd_impl(bool mamba, const sscan_desc* desc, const sscan_plan* plan, const void* x, const void* delta,
              const float* A, const void* b, const void* c, const float* Dskip, const float* h0, void* y, float* hT,
-             float* H, void* ws, size_t ws_bytes, hipStream_t stream) {
+             float* H, float* hck, void* ws, size_t ws_bytes, hipStream_t stream) {
   Resolved r;
   int st = resolve_desc(desc, &r);
   if (st != SSCAN_OK) return st;
@@ -210,6 +233,8 @@ int fwd_impl(bool mamba, const sscan_desc* desc, const sscan_plan* plan, const v
   if (misaligned(A, 16) || misaligned(h0, 16) || misaligned(hT, 16) || misaligned(H, 16))
     return fail(SSCAN_ERR_ALIGN, "A, h0, hT and H must be 16-byte aligned");
   if (misaligned(Dskip, 4)) return fail(SSCAN_ERR_ALIGN, "Dskip must be 4-byte aligned");
+  if (misaligned(hck, 16)) return fail(SSCAN_ERR_ALIGN, "hck must be 16-byte aligned");
+  if (hck != nullptr && H != nullptr) return fail(SSCAN_ERR_UNSUPPORTED, "H and boundary states are alternatives");
   if (!steps) {
     if (hT == nullptr) return ok();
     const hipError_t e = sscan::launch_copy_or_zero(hT, h0, r.B * r.D * r.DS, stream);
@@ -225,10 +250,19 @@ int fwd_impl(bool mamba, const sscan_desc* desc, const sscan_plan* plan, const v
   sscan::FwdParams p{};
   p.x = x; p.delta = delta; p.A = A; p.b = b; p.c = c; p.h0 = h0; p.y = y; p.hT = hT; p.H = H;
   p.Dskip = mamba ? Dskip : nullptr;
+  p.hck = hck;
+  p.nck = (int32_t)ceil_div(r.T, sscan::kCkptSteps);
   p.x_bs = r.x_bs; p.bc_bs = r.bc_bs; p.y_bs = r.y_bs;
   p.B = (int32_t)r.B; p.T = (int32_t)r.T; p.D = (int32_t)r.D;
   p.chunks = chunks;
   p.chunk_len = (int32_t)ceil_div(r.T, chunks);
+  if (hck != nullptr && chunks > 1) {
+    // boundary blocks must not straddle chunks: chunks start on multiples of 64 steps
+    // (a multiple of every forward tile and of the block length)
+    p.chunk_len = (int32_t)(ceil_div(p.chunk_len, 64) * 64);
+    p.chunks = (int32_t)ceil_div(r.T, p.chunk_len);
+    chunks = p.chunks;
+  }
   const int64_t cpw = kThreads / lanes;
   const int64_t ntiles_d = ceil_div(r.D, cpw);
   p.ntiles_d = (int32_t)ntiles_d;
@@ -258,22 +292,31 @@ int fwd_impl(bool mamba, const sscan_desc* desc, const sscan_plan* plan, const v
 
 // The backward, plain or wrapped (then gdelta is for delta_raw, gA for A_log, gx includes
 // dy * Dskip, and gD, if not null, receives the gradient for Dskip).
+// hck (not null, H null): the H-free sweep, recomputing each tile's states from the
+// boundary states the forward kept.
 int bwd_impl(bool mamba, const sscan_desc* desc, const sscan_plan* plan, const void* dy, const float* dhT,
              const void* x, const void* delta, const float* A, const void* b, const void* c, const float* Dskip,
-             const float* h0, const float* H, float* gx, float* gdelta, float* gb, float* gc, float* gA, float* gD,
-             float* gh0, void* ws, size_t ws_bytes, hipStream_t stream) {
+             const float* h0, const float* H, const float* hck, float* gx, float* gdelta, float* gb, float* gc,
+             float* gA, float* gD, float* gh0, void* ws, size_t ws_bytes, hipStream_t stream) {
   Resolved r;
   int st = resolve_desc(desc, &r);
   if (st != SSCAN_OK) return st;
   int lanes, chunks;
   st = resolve_plan(r, plan, true, &lanes, &chunks);
   if (st != SSCAN_OK) return st;
+  const bool hf = hck != nullptr;
+  if (hf) {
+    if (H != nullptr) return fail(SSCAN_ERR_UNSUPPORTED, "H and boundary states are alternatives");
+    st = resolve_hf_plan(r, plan, &lanes, &chunks);
+    if (st != SSCAN_OK) return st;
+  }
   const bool steps = r.T > 0 && r.B > 0;
   if (r.D > 0 && gA == nullptr) return fail(SSCAN_ERR_NULL, "gA is required");
   if (steps && r.D > 0 &&
       (dy == nullptr || x == nullptr || delta == nullptr || A == nullptr || b == nullptr || c == nullptr ||
-       H == nullptr || gx == nullptr || gdelta == nullptr || gb == nullptr || gc == nullptr))
-    return fail(SSCAN_ERR_NULL, "dy, x, delta, A, b, c, H, gx, gdelta, gb and gc are required when T > 0");
+       (H == nullptr && !hf) || gx == nullptr || gdelta == nullptr || gb == nullptr || gc == nullptr))
+    return fail(SSCAN_ERR_NULL, "dy, x, delta, A, b, c, H (or the boundary states), gx, gdelta, gb and gc are "
+                                "required when T > 0");
   if (steps && r.D == 0 && (gb == nullptr || gc == nullptr))
     return fail(SSCAN_ERR_NULL, "gb and gc are required when T > 0");
   const size_t es = r.io_size;
@@ -286,6 +329,7 @@ int bwd_impl(bool mamba, const sscan_desc* desc, const sscan_plan* plan, const v
   if (misaligned(A, 16) || misaligned(h0, 16) || misaligned(H, 16) || misaligned(dhT, 16) || misaligned(gA, 16) ||
       misaligned(gh0, 16))
     return fail(SSCAN_ERR_ALIGN, "A, h0, H, dhT, gA and gh0 must be 16-byte aligned");
+  if (misaligned(hck, 16)) return fail(SSCAN_ERR_ALIGN, "hck must be 16-byte aligned");
 
   if (!steps || r.D == 0) {
     // No step to sweep: gA = 0, gh0 = dhT (zeros if absent); gb, gc over D = 0 channels are 0.
@@ -314,6 +358,8 @@ int bwd_impl(bool mamba, const sscan_desc* desc, const sscan_plan* plan, const v
   p.gin = reinterpret_cast<const float*>(wsb + lay.gin_off);
   p.Dskip = mamba ? Dskip : nullptr;
   p.part_D = gD != nullptr ? reinterpret_cast<float*>(wsb + lay.d_off) : nullptr;
+  p.hck = hck;
+  p.nck = (int32_t)ceil_div(r.T, sscan::kCkptSteps);
   p.chunk_len = (int32_t)lay.chunk_len;
   p.chunks = (int32_t)lay.chunks;
   p.x_bs = r.x_bs; p.bc_bs = r.bc_bs; p.y_bs = r.y_bs;
@@ -336,7 +382,9 @@ int bwd_impl(bool mamba, const sscan_desc* desc, const sscan_plan* plan, const v
     e = sscan::launch_bwd_carry(cp, stream);
     if (e != hipSuccess) return hip_fail(e, "backward chunk carry");
   }
-  e = sscan::launch_bwd(r.io, (int)r.DS, lanes, false, mamba, p, (unsigned)(lay.ntiles_d * r.B * lay.chunks), stream);
+  const unsigned sweep_grid = (unsigned)(lay.ntiles_d * r.B * lay.chunks);
+  e = hf ? sscan::launch_bwd_hf(r.io, (int)r.DS, lanes, mamba, p, sweep_grid, stream)
+         : sscan::launch_bwd(r.io, (int)r.DS, lanes, false, mamba, p, sweep_grid, stream);
   if (e != hipSuccess) return hip_fail(e, "backward sweep");
   sscan::ReduceParams q{};
   q.part_bc = p.part_bc; q.part_A = p.part_A; q.gb = gb; q.gc = gc; q.gA = gA;
@@ -424,29 +472,68 @@ int sscan_mamba_bwd_workspace(const sscan_desc* desc, const sscan_plan* plan, si
 int sscan_fwd(const sscan_desc* desc, const sscan_plan* plan, const void* x, const void* delta, const float* A,
               const void* b, const void* c, const float* h0, void* y, float* hT, float* H, void* ws, size_t ws_bytes,
               hipStream_t stream) {
-  return fwd_impl(false, desc, plan, x, delta, A, b, c, nullptr, h0, y, hT, H, ws, ws_bytes, stream);
+  return fwd_impl(false, desc, plan, x, delta, A, b, c, nullptr, h0, y, hT, H, nullptr, ws, ws_bytes, stream);
 }
 
 int sscan_mamba_fwd(const sscan_desc* desc, const sscan_plan* plan, const void* x, const void* delta_raw,
                     const float* A_log, const void* b, const void* c, const float* Dskip, const float* h0, void* y,
                     float* hT, float* H, void* ws, size_t ws_bytes, hipStream_t stream) {
-  return fwd_impl(true, desc, plan, x, delta_raw, A_log, b, c, Dskip, h0, y, hT, H, ws, ws_bytes, stream);
+  return fwd_impl(true, desc, plan, x, delta_raw, A_log, b, c, Dskip, h0, y, hT, H, nullptr, ws, ws_bytes, stream);
 }
 
 int sscan_bwd(const sscan_desc* desc, const sscan_plan* plan, const void* dy, const float* dhT, const void* x,
               const void* delta, const float* A, const void* b, const void* c, const float* h0, const float* H,
               float* gx, float* gdelta, float* gb, float* gc, float* gA, float* gh0, void* ws, size_t ws_bytes,
               hipStream_t stream) {
-  return bwd_impl(false, desc, plan, dy, dhT, x, delta, A, b, c, nullptr, h0, H, gx, gdelta, gb, gc, gA, nullptr,
-                  gh0, ws, ws_bytes, stream);
+  return bwd_impl(false, desc, plan, dy, dhT, x, delta, A, b, c, nullptr, h0, H, nullptr, gx, gdelta, gb, gc, gA,
+                  nullptr, gh0, ws, ws_bytes, stream);
 }
 
 int sscan_mamba_bwd(const sscan_desc* desc, const sscan_plan* plan, const void* dy, const float* dhT, const void* x,
                     const void* delta_raw, const float* A_log, const void* b, const void* c, const float* Dskip,
                     const float* h0, const float* H, float* gx, float* gdelta_raw, float* gA_log, float* gb,
                     float* gc, float* gDskip, float* gh0, void* ws, size_t ws_bytes, hipStream_t stream) {
-  return bwd_impl(true, desc, plan, dy, dhT, x, delta_raw, A_log, b, c, Dskip, h0, H, gx, gdelta_raw, gb, gc, gA_log,
-                  gDskip, gh0, ws, ws_bytes, stream);
+  return bwd_impl(true, desc, plan, dy, dhT, x, delta_raw, A_log, b, c, Dskip, h0, H, nullptr, gx, gdelta_raw, gb, gc,
+                  gA_log, gDskip, gh0, ws, ws_bytes, stream);
+}
+
+int sscan_fwd_ckpt(const sscan_desc* desc, const sscan_plan* plan, int wrapper, const void* x, const void* delta,
+                   const float* A, const void* b, const void* c, const float* Dskip, const float* h0, void* y,
+                   float* hT, float* hck, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (wrapper != SSCAN_WRAP_NONE && wrapper != SSCAN_WRAP_MAMBA)
+    return fail(SSCAN_ERR_UNSUPPORTED, "wrapper %d is unknown", wrapper);
+  if (hck == nullptr && desc != nullptr && desc->T > 0 && desc->B > 0 && desc->D > 0)
+    return fail(SSCAN_ERR_NULL, "hck is required");
+  return fwd_impl(wrapper == SSCAN_WRAP_MAMBA, desc, plan, x, delta, A, b, c, Dskip, h0, y, hT, nullptr, hck, ws,
+                  ws_bytes, stream);
+}
+
+int sscan_bwd_ckpt(const sscan_desc* desc, const sscan_plan* plan, int wrapper, const void* dy, const float* dhT,
+                   const void* x, const void* delta, const float* A, const void* b, const void* c, const float* Dskip,
+                   const float* hck, float* gx, float* gdelta, float* gb, float* gc, float* gA, float* gDskip,
+                   float* gh0, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (wrapper != SSCAN_WRAP_NONE && wrapper != SSCAN_WRAP_MAMBA)
+    return fail(SSCAN_ERR_UNSUPPORTED, "wrapper %d is unknown", wrapper);
+  if (hck == nullptr && desc != nullptr && desc->T > 0 && desc->B > 0 && desc->D > 0)
+    return fail(SSCAN_ERR_NULL, "hck is required");
+  return bwd_impl(wrapper == SSCAN_WRAP_MAMBA, desc, plan, dy, dhT, x, delta, A, b, c, Dskip, nullptr, nullptr, hck,
+                  gx, gdelta, gb, gc, gA, gDskip, gh0, ws, ws_bytes, stream);
+}
+
+int sscan_bwd_ckpt_workspace(const sscan_desc* desc, const sscan_plan* plan, int wrapper, size_t* bytes) {
+  Resolved r;
+  int st = resolve_desc(desc, &r);
+  if (st != SSCAN_OK) return st;
+  if (bytes == nullptr) return fail(SSCAN_ERR_NULL, "bytes is NULL");
+  if (wrapper != SSCAN_WRAP_NONE && wrapper != SSCAN_WRAP_MAMBA)
+    return fail(SSCAN_ERR_UNSUPPORTED, "wrapper %d is unknown", wrapper);
+  int lanes, chunks;
+  st = resolve_plan(r, plan, true, &lanes, &chunks);
+  if (st != SSCAN_OK) return st;
+  st = resolve_hf_plan(r, plan, &lanes, &chunks);
+  if (st != SSCAN_OK) return st;
+  *bytes = (r.B == 0 || r.D == 0 || r.T == 0) ? 0 : bwd_layout(r, lanes, chunks, wrapper == SSCAN_WRAP_MAMBA).total;
+  return ok();
 }
 
 int sscan_decode(const sscan_desc* desc, const void* x, const void* delta, const float* A, const void* b,

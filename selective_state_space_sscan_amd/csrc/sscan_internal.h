@@ -7,6 +7,7 @@
 namespace sscan {
 
 constexpr int kThreads = 256;  // every kernel runs 256-thread workgroups (4 wave64)
+constexpr int kCkptSteps = 32;  // steps between the boundary states of the H-free path
 
 // Storage type for bf16 I/O: the raw 16 bits.
 struct bf16_t {
@@ -36,6 +37,8 @@ struct FwdParams {
   float2* pairs;       // two-level scan: (decay product, local end state) per chunk, (C-1,B,D,DS)
   const float* hin;    // two-level scan: start state of chunks 1..C-1, (C-1,B,D,DS)
   const float* Dskip;  // Mamba wrapper: per-channel skip weight (D,), may be null (no skip)
+  float* hck;          // H-free path: state entering every kCkptSteps-step block, (B,nck,D,DS), or null
+  int32_t nck;         // ceil(T / kCkptSteps)
   int64_t x_bs;        // batch stride of x, delta (elements)
   int64_t bc_bs;       // batch stride of b, c (elements)
   int64_t y_bs;        // batch stride of y (elements)
@@ -73,6 +76,8 @@ struct BwdParams {
   const float* gin;    // two-level sweep: carry entering chunks 0..C-2 from the right, (C-1,B,D,DS)
   const float* Dskip;  // Mamba wrapper: per-channel skip weight (D,), may be null (zero)
   float* part_D;       // Mamba wrapper: per-(chunk, batch row) partial sums of dy*x, (chunks,B,D), or null
+  const float* hck;    // H-free sweep: state entering every kCkptSteps-step block, (B,nck,D,DS)
+  int32_t nck;         // ceil(T / kCkptSteps)
   int64_t x_bs;        // x, delta, dy
   int64_t bc_bs;       // b, c
   int64_t y_bs;        // gx, gdelta
@@ -134,6 +139,9 @@ hipError_t launch_bwd_plain(int io, int DS, int lanes, bool local_pass, const Bw
                             hipStream_t s);
 hipError_t launch_bwd_mamba(int io, int DS, int lanes, bool local_pass, const BwdParams& p, unsigned blocks,
                             hipStream_t s);
+// The H-free sweep (boundary states in p.hck, every kCkptSteps steps); lanes must give
+// kCkptSteps-step tiles.  Its local pass is launch_bwd's.
+hipError_t launch_bwd_hf(int io, int DS, int lanes, bool mamba, const BwdParams& p, unsigned blocks, hipStream_t s);
 hipError_t launch_bwd_carry(const BwdCarryParams& p, hipStream_t s);
 hipError_t launch_bwd_reduce(const ReduceParams& p, hipStream_t s);
 hipError_t launch_decode(int io, int DS, const DecodeParams& p, hipStream_t s);

@@ -205,3 +205,25 @@ def test_decode_validation(lib):
     assert dec(lib, desc(T=1, DS=3)) == E_UNSUP
     # nothing to do: no pointer is looked at
     assert dec(lib, desc(B=0, T=1), x=None, delta=None, A=None, b=None, c=None, si=None, so=None, y=None) == OK
+
+
+def test_ckpt_validation(lib):
+    p = sscan_plan()
+    n = ctypes.c_size_t()
+    # the H-free backward runs 8 or 16 lanes per channel: DS >= 8, plan.lanes >= 8
+    assert lib.sscan_bwd_ckpt_workspace(ctypes.byref(desc(DS=4)), None, 0, ctypes.byref(n)) == E_UNSUP
+    p.lanes = 4
+    assert lib.sscan_bwd_ckpt_workspace(ctypes.byref(desc(DS=16)), ctypes.byref(p), 0, ctypes.byref(n)) == E_UNSUP
+    assert lib.sscan_bwd_ckpt_workspace(ctypes.byref(desc(DS=16)), None, 7, ctypes.byref(n)) == E_UNSUP
+    assert lib.sscan_bwd_ckpt_workspace(ctypes.byref(desc(DS=16)), None, 1, ctypes.byref(n)) == OK
+    v = lambda a: ctypes.c_void_p(a)
+    # forward: hck required, H-free and wrapper checks happen before any launch
+    d = desc(DS=16)
+    assert lib.sscan_fwd_ckpt(ctypes.byref(d), None, 0, *([v(FAKE)] * 5), None, None, v(FAKE), None, None, None,
+                              ctypes.c_size_t(0), None) == E_NULL
+    assert lib.sscan_fwd_ckpt(ctypes.byref(d), None, 3, *([v(FAKE)] * 5), None, None, v(FAKE), None, v(FAKE), None,
+                              ctypes.c_size_t(0), None) == E_UNSUP
+    assert lib.sscan_fwd_ckpt(ctypes.byref(d), None, 0, *([v(FAKE)] * 5), None, None, v(FAKE), None, v(FAKE + 4),
+                              None, ctypes.c_size_t(0), None) == E_ALIGN
+    # backward: hck required
+    assert lib.sscan_bwd_ckpt(ctypes.byref(d), None, 0, *([None] * 16), None, ctypes.c_size_t(0), None) == E_NULL
