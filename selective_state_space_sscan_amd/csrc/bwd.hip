@@ -1,22 +1,9 @@
-// Backward entry points without the wrapper, and the kernels of the backward that do not
-// depend on it (chunk carry composition, fixed-order reduction of the partial sums).
+// Backward entry points without the wrapper, and the kernel of the backward that does not
+// depend on it (fixed-order reduction of the partial sums).
 #include "bwd_kernel.h"
 
 namespace sscan {
 namespace {
-
-// Right-to-left composition of the chunk carry maps: gin[k] is the adjoint entering chunk
-// k from the right (chunk C-1 receives dhT).
-__global__ __launch_bounds__(kThreads) void bwd_carry_kernel(const BwdCarryParams p) {
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= p.n) return;
-  float G = p.dhT != nullptr ? p.dhT[i] : 0.f;
-  for (int k = p.chunks - 1; k >= 1; --k) {
-    const float2 pr = p.pairs[(int64_t)(k - 1) * p.n + i];
-    G = fmaf(pr.x, G, pr.y);
-    p.gin[(int64_t)(k - 1) * p.n + i] = G;
-  }
-}
 
 // gb, gc: add the per-workgroup partials over channel tiles in ascending tile order.
 // gA: add the per-(chunk, batch row) partials in ascending order (then, for the Mamba
@@ -29,9 +16,24 @@ __global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(const ReduceParams
     const int64_t per_b = (int64_t)p.T * p.DS;
     const int64_t bb = i / per_b;
     const int64_t r = i - bb * per_b;
+    // partials of one element lie B*T*DS float2 apart: issue eight loads at a time (the
+    // sum stays in ascending order, so the result does not depend on the batching)
+    const float2* src = p.part_bc + (int64_t)bb * per_b + r;
+    const int64_t stride = (int64_t)p.B * per_b;
     float sb = 0.f, sc = 0.f;
-    for (int k = 0; k < p.ntiles_d; ++k) {
-      const float2 v = p.part_bc[((int64_t)k * p.B + bb) * per_b + r];
+    int k = 0;
+    for (; k + 8 <= p.ntiles_d; k += 8) {
+      float2 v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = src[(int64_t)(k + q) * stride];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        sb += v[q].x;
+        sc += v[q].y;
+      }
+    }
+    for (; k < p.ntiles_d; ++k) {
+      const float2 v = src[(int64_t)k * stride];
       sb += v.x;
       sc += v.y;
     }
@@ -63,12 +65,6 @@ hipError_t launch_bwd(int io, int DS, int lanes, bool local_pass, bool mamba, co
                       hipStream_t s) {
   return mamba ? launch_bwd_mamba(io, DS, lanes, local_pass, p, grid, s)
                : launch_bwd_plain(io, DS, lanes, local_pass, p, grid, s);
-}
-
-hipError_t launch_bwd_carry(const BwdCarryParams& p, hipStream_t s) {
-  const int64_t blocks = (p.n + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL(bwd_carry_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
-  return hipGetLastError();
 }
 
 hipError_t launch_bwd_reduce(const ReduceParams& p, hipStream_t s) {

@@ -164,12 +164,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
   for (int i = 0; i < K; ++i) { Av[i] = 0.f; G[i] = 0.f; gA[i] = 0.f; hcur[i] = 0.f; }
   if (dvalid) {
     load_k<K>(p.A + (int64_t)d * DS + j * K, Av);
-    // the adjoint entering this chunk from the right: dhT for the last chunk, else the
-    // composed carry of the chunks after it
-    if (chunk < p.chunks - 1)
-      load_k<K>(p.gin + (int64_t)chunk * nstate + soff, G);
-    else if (p.dhT != nullptr)
-      load_k<K>(p.dhT + soff, G);
+    // the adjoint entering this chunk from the right: dhT composed, right to left, with
+    // the carry maps G -> P G + Gloc of every sub-chunk after this chunk (the local pass
+    // left one pair per sub-chunk of chunks 1 .. C-1)
+    if (p.dhT != nullptr) load_k<K>(p.dhT + soff, G);
+    for (int k = p.chunks * p.subs - 1; k >= (chunk + 1) * p.subs; --k) {
+      const float2* pr = p.pairs + (int64_t)(k - p.subs) * nstate + soff;
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+        const float2 m = pr[i];
+        G[i] = fmaf(m.x, G[i], m.y);
+      }
+    }
     if (!HF && t_hi > t_lo) load_k<K>(Hrow + (int64_t)(t_hi - 1) * D * DS + d * DS + j * K, hcur);
   }
 #pragma unroll
@@ -534,19 +540,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
   }
 }
 
-// Local pass of the two-level reverse sweep: chunk k (1..C-1) runs its steps from a zero
-// adjoint and records, per (b, d, n), its decay product exp(A * sum(delta)) and the carry
-// it hands to the chunk before it.  The carry map of a chunk is G -> P G + Gloc.
+// Local pass of the two-level reverse sweep.  The chunks 1..C-1 of the sweep are split
+// into `subs` sub-chunks each, so that this pass has several times the sweep's parallelism;
+// every sub-chunk runs its steps from a zero adjoint and records, per (b, d, n), its decay
+// product exp(A * sum(delta)) and the carry it hands to the sub-chunk before it.  The carry
+// map of a sub-chunk is G -> P G + Gloc; each workgroup of the sweep composes the maps of
+// the sub-chunks after its chunk, right to left from dhT.
 template <typename IO, int DS, int L, bool MAMBA>
 __global__ __launch_bounds__(kThreads) void bwd_local_kernel(const BwdParams p) {
   constexpr int K = DS / L;
   constexpr int CPW = kThreads / L;
-  constexpr int TB = fwd_tile_steps(L);
+  constexpr int TB = (2048 / CPW) < 64 ? (2048 / CPW) : 64;  // 16 KiB of staged (delta, dy) at most
   constexpr int TILE = TB * CPW;
   constexpr int PER = TILE / kThreads;
   constexpr int BC = TB * DS;
   constexpr int PER_BC = (BC + kThreads - 1) / kThreads;
-  constexpr int S = (16 / K) < 1 ? 1 : ((16 / K) < TB ? (16 / K) : TB);
+  constexpr int S = (32 / K) < 1 ? 1 : ((32 / K) < TB ? (32 / K) : TB);  // steps per batch
   constexpr uint32_t ES = sizeof(IO);
   static_assert(TILE % kThreads == 0 && TB % S == 0, "tile shape");
 
@@ -557,15 +566,15 @@ __global__ __launch_bounds__(kThreads) void bwd_local_kernel(const BwdParams p) 
   const int dtile = lin % p.ntiles_d;
   const int rest = lin / p.ntiles_d;
   const int bb = rest % p.B;
-  const int chunk = 1 + rest / p.B;
+  const int sub = p.subs + rest / p.B;  // sub-chunk index; those of chunk 0 are not needed
 
   const int tid = threadIdx.x;
   const int ch = tid / L;
   const int j = tid % L;
   const int d0 = dtile * CPW;
   const int D = p.D;
-  const int t_lo = chunk * p.chunk_len;
-  const int t_hi = min(p.T, t_lo + p.chunk_len);
+  const int t_lo = min(p.T, sub * p.sub_len);
+  const int t_hi = min(p.T, t_lo + p.sub_len);
   const int d = d0 + ch;
   const bool dvalid = d < D;
   const int64_t nstate = (int64_t)p.B * D * DS;
@@ -640,28 +649,29 @@ __global__ __launch_bounds__(kThreads) void bwd_local_kernel(const BwdParams p) 
     }
     __syncthreads();
     if (it > 0) load_tile(t_lo + (it - 1) * TB);
-#pragma unroll 1
+    // batches of S steps, all of a tile unrolled: each batch reads its inputs and forms
+    // its decays up front, then runs the carry through them
+#pragma unroll
     for (int s0 = TB - S; s0 >= 0; s0 -= S) {
-      float a[S][K];
+      float a[S][K], cv[S][K];
       float2 dd[S];
 #pragma unroll
       for (int s = 0; s < S; ++s) {
         dd[s] = s_dd[(s0 + s) * CPW + ch];
+        lds_load_vec<K>(&s_c[(s0 + s) * DS + j * K], cv[s]);
 #pragma unroll
         for (int i = 0; i < K; ++i) a[s][i] = exp2_hw(dd[s].x * A2[i]);
       }
 #pragma unroll
       for (int s = S - 1; s >= 0; --s) {
-        float cv[K];
-        lds_load_vec<K>(&s_c[(s0 + s) * DS + j * K], cv);
 #pragma unroll
-        for (int i = 0; i < K; ++i) G[i] = a[s][i] * fmaf(dd[s].y, cv[i], G[i]);
+        for (int i = 0; i < K; ++i) G[i] = a[s][i] * fmaf(dd[s].y, cv[s][i], G[i]);
         dsum += dd[s].x;
       }
     }
   }
   if (!dvalid) return;
-  float2* pr = p.pairs + (int64_t)(chunk - 1) * nstate + soff;
+  float2* pr = p.pairs + (int64_t)(sub - p.subs) * nstate + soff;
 #pragma unroll
   for (int i = 0; i < K; ++i)
     pr[i] = make_float2(exp2_hw(static_cast<float>(static_cast<double>(A2[i]) * dsum)), G[i]);

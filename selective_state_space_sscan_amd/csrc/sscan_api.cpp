@@ -75,13 +75,6 @@ int resolve_desc(const sscan_desc* desc, Resolved* r) {
 }
 
 // Smallest lane count L (power of two, <= min(DS,16)) with B*D*L >= target lanes.
-int pick_lanes(const Resolved& r, int64_t target) {
-  const int64_t maxl = r.DS < 16 ? r.DS : 16;
-  int64_t l = 1;
-  while (l < maxl && r.B * r.D * l < target) l *= 2;
-  return (int)l;
-}
-
 int resolve_plan(const Resolved& r, const sscan_plan* plan, bool backward, int* lanes, int* chunks) {
   if (plan != nullptr) {
     for (int i = 0; i < 6; ++i)
@@ -92,17 +85,19 @@ int resolve_plan(const Resolved& r, const sscan_plan* plan, bool backward, int* 
       return fail(SSCAN_ERR_UNSUPPORTED, "plan.chunks=%d out of range", plan->chunks);
   }
   // Measured on MI355X: the forward runs best with 8 lanes per channel (two states per
-  // lane) on every size tried, the backward with one state per lane.
+  // lane) on every size tried; the backward with 4 lanes (four states per lane: a quarter
+  // of the per-workgroup gb/gc partials of one state per lane, and fewer cross-lane sums),
+  // split along T for occupancy (8x2048x768x16: 4 lanes and 8 chunks 0.285 ms, 16 lanes
+  // and 2 chunks 0.304 ms).
   int l = (plan != nullptr && plan->lanes != 0) ? plan->lanes
-                                                : (backward ? pick_lanes(r, 98304) : (int)(r.DS < 8 ? r.DS : 8));
+                                                : (backward ? (int)(r.DS < 4 ? r.DS : 4) : (int)(r.DS < 8 ? r.DS : 8));
   int c = 1;
   if (backward) {
     if (plan != nullptr && plan->chunks != 0) {
       c = plan->chunks;
     } else {
-      // Split the reverse sweep until there are three waves per SIMD (one state per lane
-      // leaves 1.5 at 8x2048x768x16, and half the SIMDs would run two); every chunk keeps
-      // at least four tiles.
+      // Split the reverse sweep until there are three waves per SIMD (at 8x2048x768x16 a
+      // single pass would leave 0.375); every chunk keeps at least four tiles.
       const int64_t lanes_total = r.B * r.D * l;
       const int64_t tb = sscan::bwd_tile_steps(l);
       if (lanes_total > 0 && lanes_total < 3 * kLanesOneWavePerSimd) {
@@ -153,11 +148,15 @@ FwdLayout fwd_layout(const Resolved& r, int chunks) {
 }
 
 struct BwdLayout {
-  size_t bc_off, a_off, pairs_off, gin_off, d_off, total;
-  int64_t ntiles_d, chunk_len, chunks;
+  size_t bc_off, a_off, pairs_off, d_off, total;
+  int64_t ntiles_d, chunk_len, chunks, subs, sub_len;
 };
 
 // Chunks of the reverse sweep are whole tiles long; the last one takes the remainder.
+// The local pass splits chunks 1..C-1 into `subs` sub-chunks each (a power of two that
+// divides the chunk length, sub-chunks at least 64 steps long), doubling it while the pass
+// stays within about six waves per SIMD: it reads only delta, dy and c, and more
+// parallelism is what it lacks.
 // with_D: room for the Mamba wrapper's per-(chunk, batch row) partial sums of dy * x.
 BwdLayout bwd_layout(const Resolved& r, int lanes, int chunks, bool with_D) {
   BwdLayout L{};
@@ -166,12 +165,19 @@ BwdLayout bwd_layout(const Resolved& r, int lanes, int chunks, bool with_D) {
   L.ntiles_d = ceil_div(r.D, cpw);
   L.chunk_len = r.T > 0 ? ceil_div(ceil_div(r.T, chunks), tb) * tb : tb;
   L.chunks = r.T > 0 ? ceil_div(r.T, L.chunk_len) : 1;
+  L.subs = 1;
+  if (L.chunks > 1) {
+    const int64_t waves = L.ntiles_d * r.B * (L.chunks - 1) * (kThreads / 64);
+    while (L.subs < 8 && waves * L.subs * 2 <= 6 * 1024 && L.chunk_len % (L.subs * 2) == 0 &&
+           L.chunk_len / (L.subs * 2) >= 64)
+      L.subs *= 2;
+  }
+  L.sub_len = L.chunk_len / L.subs;
   const size_t nstate = (size_t)(r.B * r.D * r.DS);
   L.bc_off = 0;
   L.a_off = align_up((size_t)(L.ntiles_d * r.B * r.T * r.DS) * sizeof(float2), 256);
   L.pairs_off = align_up(L.a_off + (size_t)L.chunks * nstate * sizeof(float), 256);
-  L.gin_off = align_up(L.pairs_off + (size_t)(L.chunks - 1) * nstate * sizeof(float2), 256);
-  L.d_off = align_up(L.gin_off + (size_t)(L.chunks - 1) * nstate * sizeof(float), 256);
+  L.d_off = align_up(L.pairs_off + (size_t)((L.chunks - 1) * L.subs) * nstate * sizeof(float2), 256);
   L.total = with_D ? align_up(L.d_off + (size_t)(L.chunks * r.B * r.D) * sizeof(float), 256) : L.d_off;
   return L;
 }
@@ -355,32 +361,25 @@ int bwd_impl(bool mamba, const sscan_desc* desc, const sscan_plan* plan, const v
   p.part_bc = reinterpret_cast<float2*>(wsb + lay.bc_off);
   p.part_A = reinterpret_cast<float*>(wsb + lay.a_off);
   p.pairs = reinterpret_cast<float2*>(wsb + lay.pairs_off);
-  p.gin = reinterpret_cast<const float*>(wsb + lay.gin_off);
   p.Dskip = mamba ? Dskip : nullptr;
   p.part_D = gD != nullptr ? reinterpret_cast<float*>(wsb + lay.d_off) : nullptr;
   p.hck = hck;
   p.nck = (int32_t)ceil_div(r.T, sscan::kCkptSteps);
   p.chunk_len = (int32_t)lay.chunk_len;
   p.chunks = (int32_t)lay.chunks;
+  p.subs = (int32_t)lay.subs;
+  p.sub_len = (int32_t)lay.sub_len;
   p.x_bs = r.x_bs; p.bc_bs = r.bc_bs; p.y_bs = r.y_bs;
   p.B = (int32_t)r.B; p.T = (int32_t)r.T; p.D = (int32_t)r.D;
   p.ntiles_d = (int32_t)lay.ntiles_d;
   p.xcd_group = xcd_group(lanes, r.io_size);
-  if (lay.ntiles_d * r.B * lay.chunks > std::numeric_limits<int32_t>::max())
+  if (lay.ntiles_d * r.B * lay.chunks * lay.subs > std::numeric_limits<int32_t>::max())
     return fail(SSCAN_ERR_UNSUPPORTED, "too many workgroups");
   hipError_t e;
   if (lay.chunks > 1) {
-    e = sscan::launch_bwd(r.io, (int)r.DS, lanes, true, mamba, p, (unsigned)(lay.ntiles_d * r.B * (lay.chunks - 1)),
-                          stream);
+    e = sscan::launch_bwd(r.io, (int)r.DS, lanes, true, mamba, p,
+                          (unsigned)(lay.ntiles_d * r.B * (lay.chunks - 1) * lay.subs), stream);
     if (e != hipSuccess) return hip_fail(e, "backward local pass");
-    sscan::BwdCarryParams cp{};
-    cp.pairs = p.pairs;
-    cp.dhT = dhT;
-    cp.gin = reinterpret_cast<float*>(wsb + lay.gin_off);
-    cp.n = r.B * r.D * r.DS;
-    cp.chunks = (int32_t)lay.chunks;
-    e = sscan::launch_bwd_carry(cp, stream);
-    if (e != hipSuccess) return hip_fail(e, "backward chunk carry");
   }
   const unsigned sweep_grid = (unsigned)(lay.ntiles_d * r.B * lay.chunks);
   e = hf ? sscan::launch_bwd_hf(r.io, (int)r.DS, lanes, mamba, p, sweep_grid, stream)

@@ -72,8 +72,8 @@ struct BwdParams {
   float* gh0;          // may be null
   float2* part_bc;     // (ntiles_d, B, T, DS): per-workgroup (gb, gc) partial sums
   float* part_A;       // (chunks, B, D, DS): per-(chunk, batch row) gA partial sums
-  float2* pairs;       // two-level sweep: (decay product, local carry) of chunks 1..C-1, (C-1,B,D,DS)
-  const float* gin;    // two-level sweep: carry entering chunks 0..C-2 from the right, (C-1,B,D,DS)
+  float2* pairs;       // two-level sweep: (decay product, local carry) of the sub-chunks of chunks
+                       // 1..C-1, ((C-1)*subs,B,D,DS)
   const float* Dskip;  // Mamba wrapper: per-channel skip weight (D,), may be null (zero)
   float* part_D;       // Mamba wrapper: per-(chunk, batch row) partial sums of dy*x, (chunks,B,D), or null
   const float* hck;    // H-free sweep: state entering every kCkptSteps-step block, (B,nck,D,DS)
@@ -86,14 +86,8 @@ struct BwdParams {
   int32_t xcd_group;
   int32_t chunk_len;   // steps per chunk, a multiple of the tile
   int32_t chunks;
-};
-
-struct BwdCarryParams {
-  const float2* pairs;  // (C-1,B,D,DS)
-  const float* dhT;     // may be null
-  float* gin;           // (C-1,B,D,DS)
-  int64_t n;            // B*D*DS
-  int32_t chunks;
+  int32_t subs;        // two-level sweep: sub-chunks per chunk in the local pass (divides chunk_len)
+  int32_t sub_len;     // chunk_len / subs
 };
 
 struct ReduceParams {
@@ -142,7 +136,6 @@ hipError_t launch_bwd_mamba(int io, int DS, int lanes, bool local_pass, const Bw
 // The H-free sweep (boundary states in p.hck, every kCkptSteps steps); lanes must give
 // kCkptSteps-step tiles.  Its local pass is launch_bwd's.
 hipError_t launch_bwd_hf(int io, int DS, int lanes, bool mamba, const BwdParams& p, unsigned blocks, hipStream_t s);
-hipError_t launch_bwd_carry(const BwdCarryParams& p, hipStream_t s);
 hipError_t launch_bwd_reduce(const ReduceParams& p, hipStream_t s);
 hipError_t launch_decode(int io, int DS, const DecodeParams& p, hipStream_t s);
 hipError_t launch_fill(float* dst, int64_t n, hipStream_t s);                         // dst[i] = 0

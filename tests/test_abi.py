@@ -176,15 +176,15 @@ def test_plan_select_and_workspace_sizes(lib):
     assert lib.sscan_plan_select(ctypes.byref(d), 0, ctypes.byref(p)) == OK
     assert p.lanes == 8 and p.chunks == 4
     assert lib.sscan_plan_select(ctypes.byref(d), 1, ctypes.byref(p)) == OK
-    assert p.lanes == 16 and p.chunks == 6  # 2048 channels x 16 lanes x 6 chunks = 3 waves per SIMD
+    assert p.lanes == 4 and p.chunks == 16  # 2048 channels x 4 lanes x 16 chunks = 2 waves per SIMD (T caps it)
     d = desc(B=8, T=2048, D=768, DS=16)
     assert lib.sscan_plan_select(ctypes.byref(d), 1, ctypes.byref(p)) == OK
-    assert p.lanes == 16 and p.chunks == 2  # 1.5 -> 3 waves per SIMD
+    assert p.lanes == 4 and p.chunks == 8  # 0.375 -> 3 waves per SIMD
     # backward partial buffers: one (gb, gc) pair per channel tile, step and state, plus gA per batch row
     d = desc(B=8, T=2048, D=768, DS=16)
     n = ctypes.c_size_t()
     assert lib.sscan_bwd_workspace(ctypes.byref(d), None, ctypes.byref(n)) == OK
-    tiles = (768 + 15) // 16
+    tiles = (768 + 63) // 64
     assert n.value >= tiles * 8 * 2048 * 16 * 8 + 8 * 768 * 16 * 4
 
 
