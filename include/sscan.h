@@ -206,7 +206,8 @@ int sscan_bwd_ckpt_workspace(const sscan_desc* desc, const sscan_plan* plan, int
 int sscan_decode(const sscan_desc* desc, const void* x, const void* delta, const float* A, const void* b,
                  const void* c, const float* state_in, float* state_out, void* y, hipStream_t stream);
 
-/* The plan the library picks for desc (backward != 0: for sscan_bwd) -> *plan.  Uses no GPU. */
+/* The plan the library picks for desc -> *plan: backward 0 for the forward entry points,
+ * 2 for sscan_mamba_bwd, any other value for sscan_bwd.  Uses no GPU. */
 int sscan_plan_select(const sscan_desc* desc, int backward, sscan_plan* plan);
 
 /* Static text for a status code. */

@@ -116,11 +116,14 @@ def sscan_version() -> int:
     return int(_lib.load().sscan_version())
 
 
-def sscan_plan_select(B: int, T: int, D: int, DS: int, io: torch.dtype = torch.float32, backward: bool = False) -> Plan:
+def sscan_plan_select(B: int, T: int, D: int, DS: int, io: torch.dtype = torch.float32, backward: bool = False,
+                      mamba: bool = False) -> Plan:
+    """The plan the library picks: the forward's, or with ``backward`` the backward's (with
+    ``mamba`` that of the wrapper's backward)."""
     lib = _lib.load()
     d = _desc(B, T, D, DS, _IO[io])
     p = sscan_plan()
-    _lib.check(lib.sscan_plan_select(ctypes.byref(d), int(bool(backward)), ctypes.byref(p)))
+    _lib.check(lib.sscan_plan_select(ctypes.byref(d), (2 if mamba else 1) if backward else 0, ctypes.byref(p)))
     return Plan(p.lanes, p.chunks)
 
 

@@ -75,7 +75,11 @@ int resolve_desc(const sscan_desc* desc, Resolved* r) {
 }
 
 // Smallest lane count L (power of two, <= min(DS,16)) with B*D*L >= target lanes.
-int resolve_plan(const Resolved& r, const sscan_plan* plan, bool backward, int* lanes, int* chunks) {
+// Plan kinds: the forward, the backward, and the backward of the Mamba-style wrapper.
+enum PlanKind { kPlanFwd = 0, kPlanBwd = 1, kPlanMambaBwd = 2 };
+
+int resolve_plan(const Resolved& r, const sscan_plan* plan, PlanKind kind, int* lanes, int* chunks) {
+  const bool backward = kind != kPlanFwd;
   if (plan != nullptr) {
     for (int i = 0; i < 6; ++i)
       if (plan->reserved[i] != 0) return fail(SSCAN_ERR_UNSUPPORTED, "plan.reserved must be 0");
@@ -88,9 +92,22 @@ int resolve_plan(const Resolved& r, const sscan_plan* plan, bool backward, int* 
   // lane) on every size tried; the backward with 4 lanes (four states per lane: a quarter
   // of the per-workgroup gb/gc partials of one state per lane, and fewer cross-lane sums),
   // split along T for occupancy (8x2048x768x16: 4 lanes and 8 chunks 0.285 ms, 16 lanes
-  // and 2 chunks 0.304 ms).
-  int l = (plan != nullptr && plan->lanes != 0) ? plan->lanes
-                                                : (backward ? (int)(r.DS < 4 ? r.DS : 4) : (int)(r.DS < 8 ? r.DS : 8));
+  // and 2 chunks 0.304 ms); the wrapper's backward, whose staging does more per element,
+  // with the fewest lanes (up to 16) that give 1.5 waves per SIMD before the T split
+  // (the same size: 16 lanes 0.311 ms, 4 lanes 0.329 ms).
+  int l;
+  if (plan != nullptr && plan->lanes != 0) {
+    l = plan->lanes;
+  } else if (kind == kPlanFwd) {
+    l = (int)(r.DS < 8 ? r.DS : 8);
+  } else if (kind == kPlanBwd) {
+    l = (int)(r.DS < 4 ? r.DS : 4);
+  } else {
+    const int64_t maxl = r.DS < 16 ? r.DS : 16;
+    int64_t v = 1;
+    while (v < maxl && r.B * r.D * v < 3 * kLanesOneWavePerSimd / 2) v *= 2;
+    l = (int)v;
+  }
   int c = 1;
   if (backward) {
     if (plan != nullptr && plan->chunks != 0) {
@@ -227,7 +244,7 @@ int fwd_impl(bool mamba, const sscan_desc* desc, const sscan_plan* plan, const v
   int st = resolve_desc(desc, &r);
   if (st != SSCAN_OK) return st;
   int lanes, chunks;
-  st = resolve_plan(r, plan, false, &lanes, &chunks);
+  st = resolve_plan(r, plan, kPlanFwd, &lanes, &chunks);
   if (st != SSCAN_OK) return st;
   if (r.B == 0 || r.D == 0) return ok();
   const bool steps = r.T > 0;
@@ -308,7 +325,7 @@ int bwd_impl(bool mamba, const sscan_desc* desc, const sscan_plan* plan, const v
   int st = resolve_desc(desc, &r);
   if (st != SSCAN_OK) return st;
   int lanes, chunks;
-  st = resolve_plan(r, plan, true, &lanes, &chunks);
+  st = resolve_plan(r, plan, mamba ? kPlanMambaBwd : kPlanBwd, &lanes, &chunks);
   if (st != SSCAN_OK) return st;
   const bool hf = hck != nullptr;
   if (hf) {
@@ -424,7 +441,8 @@ int sscan_plan_select(const sscan_desc* desc, int backward, sscan_plan* plan) {
   if (st != SSCAN_OK) return st;
   if (plan == nullptr) return fail(SSCAN_ERR_NULL, "plan is NULL");
   int lanes, chunks;
-  st = resolve_plan(r, nullptr, backward != 0, &lanes, &chunks);
+  st = resolve_plan(r, nullptr, backward == 0 ? kPlanFwd : (backward == 2 ? kPlanMambaBwd : kPlanBwd), &lanes,
+                    &chunks);
   if (st != SSCAN_OK) return st;
   memset(plan, 0, sizeof(*plan));
   plan->lanes = lanes;
@@ -438,7 +456,7 @@ int sscan_fwd_workspace(const sscan_desc* desc, const sscan_plan* plan, size_t* 
   if (st != SSCAN_OK) return st;
   if (bytes == nullptr) return fail(SSCAN_ERR_NULL, "bytes is NULL");
   int lanes, chunks;
-  st = resolve_plan(r, plan, false, &lanes, &chunks);
+  st = resolve_plan(r, plan, kPlanFwd, &lanes, &chunks);
   if (st != SSCAN_OK) return st;
   *bytes = (r.B == 0 || r.D == 0 || r.T == 0) ? 0 : fwd_layout(r, chunks).total;
   return ok();
@@ -450,7 +468,7 @@ int sscan_bwd_workspace(const sscan_desc* desc, const sscan_plan* plan, size_t* 
   if (st != SSCAN_OK) return st;
   if (bytes == nullptr) return fail(SSCAN_ERR_NULL, "bytes is NULL");
   int lanes, chunks;
-  st = resolve_plan(r, plan, true, &lanes, &chunks);
+  st = resolve_plan(r, plan, kPlanBwd, &lanes, &chunks);
   if (st != SSCAN_OK) return st;
   *bytes = (r.B == 0 || r.D == 0 || r.T == 0) ? 0 : bwd_layout(r, lanes, chunks, false).total;
   return ok();
@@ -462,7 +480,7 @@ int sscan_mamba_bwd_workspace(const sscan_desc* desc, const sscan_plan* plan, si
   if (st != SSCAN_OK) return st;
   if (bytes == nullptr) return fail(SSCAN_ERR_NULL, "bytes is NULL");
   int lanes, chunks;
-  st = resolve_plan(r, plan, true, &lanes, &chunks);
+  st = resolve_plan(r, plan, kPlanMambaBwd, &lanes, &chunks);
   if (st != SSCAN_OK) return st;
   *bytes = (r.B == 0 || r.D == 0 || r.T == 0) ? 0 : bwd_layout(r, lanes, chunks, true).total;
   return ok();
@@ -527,7 +545,7 @@ int sscan_bwd_ckpt_workspace(const sscan_desc* desc, const sscan_plan* plan, int
   if (wrapper != SSCAN_WRAP_NONE && wrapper != SSCAN_WRAP_MAMBA)
     return fail(SSCAN_ERR_UNSUPPORTED, "wrapper %d is unknown", wrapper);
   int lanes, chunks;
-  st = resolve_plan(r, plan, true, &lanes, &chunks);
+  st = resolve_plan(r, plan, wrapper == SSCAN_WRAP_MAMBA ? kPlanMambaBwd : kPlanBwd, &lanes, &chunks);
   if (st != SSCAN_OK) return st;
   st = resolve_hf_plan(r, plan, &lanes, &chunks);
   if (st != SSCAN_OK) return st;
