@@ -59,6 +59,42 @@ __device__ __forceinline__ float rows_reduce_scatter(float b0, float c0, float b
   return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
+// Sums over the four DPP banks (4-lane groups) of each 16-lane row, reduce-scattered: on
+// entry every lane holds b[0..3] and c[0..3]; on exit b[0] and c[0] of a lane in bank k
+// hold the row totals of b[k] and c[k] over its four banks (lanes l, l^4, l^8, l^12).
+// Stage 1 pairs banks k and k^2 (row_ror:8): banks 0, 1 keep items 0, 1 and banks 2, 3
+// items 2, 3; stage 2 pairs banks k and k^1 (row_shl / row_shr by 4).  Each pair costs two
+// bank-masked DPP adds that write disjoint banks, the first reading the partner's copy
+// before the second overwrites it.  The leading s_nop gives the two wait states a DPP read
+// of a register written by the previous vector instruction requires; within the block every
+// DPP source was written at least two instructions earlier.
+__device__ __forceinline__ void bank_reduce_scatter(float (&b)[4], float (&c)[4]) {
+  asm("s_nop 1\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %0, %4, %4 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %1, %1, %1 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %1, %5, %5 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %2, %2, %2 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %2, %6, %6 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %3, %3, %3 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %3, %7, %7 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_shl:4 row_mask:0xf bank_mask:0x5\n\t"
+      "v_add_f32_dpp %0, %1, %1 row_shr:4 row_mask:0xf bank_mask:0xa\n\t"
+      "v_add_f32_dpp %2, %2, %2 row_shl:4 row_mask:0xf bank_mask:0x5\n\t"
+      "v_add_f32_dpp %2, %3, %3 row_shr:4 row_mask:0xf bank_mask:0xa"
+      : "+v"(b[0]), "+v"(b[1]), "+v"(c[0]), "+v"(c[1])
+      : "v"(b[2]), "v"(b[3]), "v"(c[2]), "v"(c[3]));
+}
+
+// Sum over the four 16-lane rows of a wave for a pair (b, c) of per-lane values: rows 0
+// and 1 receive the total of b, rows 2 and 3 the total of c (gfx950 row-swap permutes).
+__device__ __forceinline__ float rows_pair_sum(float b, float c) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(b), __float_as_uint(c), false, false);
+  const float v = __uint_as_float(p[0]) + __uint_as_float(p[1]);  // rows 0-1: b over rows (r, r+2); 2-3: c
+  auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
 // DPP pattern that pairs each lane with one whose lane-index bit M differs and whose
 // higher bits agree (M = 1, 2, 4, 8).
 template <int M>
@@ -100,7 +136,7 @@ __device__ __forceinline__ void reduce_scatter(float (&v)[V], int j, int& idx0) 
 // blocks are both kCkptSteps long), with the forward's own arithmetic, so the states
 // are the forward's bit for bit.  They go to a per-wave LDS block that the sweep reads.
 template <typename IO, int DS, int L, bool MAMBA, bool HF>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 16 && L == 16 ? (HF ? 2 : 3) : (DS / L >= 8 ? 1 : 2)))) void bwd_kernel(const BwdParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 16 && (L == 16 || L == 4) ? (HF ? 2 : 3) : (DS / L >= 8 ? 1 : 2)))) void bwd_kernel(const BwdParams p) {
   constexpr int K = DS / L;
   constexpr int CPW = kThreads / L;
   constexpr int TB = bwd_tile_steps(L);
@@ -455,6 +491,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
           }
         }
         // phase E: sums over the channels of the wave -> one (gb, gc) slot per wave
+        if constexpr (L == 4 && K == 4 && S == 1) {
+          // Four lanes per channel: the four channels of a 16-lane row sit in its four DPP
+          // banks.  Reduce-scatter the 8 values of each lane over the banks with bank-masked
+          // DPP adds (each bank keeps one state; no selects), then over the wave's rows.
+          bank_reduce_scatter(gbv[0], gcv[0]);
+          const float v = rows_pair_sum(gbv[0][0], gcv[0][0]);
+          const int n = j * K + ((lane >> 2) & 3);
+          s_red[(row >> 1) * (NWAVE * BC) + wave * BC + tt0 * DS + n] = v;
+        } else {
 #pragma unroll
         for (int s = 0; s < S; ++s) {
 #pragma unroll
@@ -472,6 +517,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
           const int ss = sel ? s_b2 : s_a;
           const int ii = sel ? i_b : i_a;
           s_red[(row >> 1) * (NWAVE * BC) + wave * BC + (tt0 + ss) * DS + j * K + ii] = v;
+        }
         }
       }
     }
