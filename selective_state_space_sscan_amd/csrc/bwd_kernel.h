@@ -304,7 +304,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
   constexpr int DB = (HBLK * 4) % (64 * 16) == 0 ? 16 : 4;      // bytes per lane and load
   constexpr int NQ = HBLK * 4 / (64 * DB);                      // loads per block
   static_assert(NQ * 64 * DB == HBLK * 4, "an H block is a whole number of loads");
-  __shared__ float s_h[HF ? 1 : NWAVE * HBLK];
+  __shared__ float s_h[(HF || (K == 4 && DB == 16)) ? 1 : NWAVE * HBLK];
   // H-free: rows 0..TB of a wave's block hold H_{ts-1} .. H_{ts+TB-1} of the current tile
   __shared__ float s_hs[HF ? NWAVE * (TB + 1) * WROW : 1];
   float* const hsw = s_hs + (HF ? wave * (TB + 1) * WROW : 0);
@@ -319,8 +319,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
   const int wd0 = d0 + wave * (64 / L);                         // first channel of this wave
   const uint32_t wbytes = static_cast<uint32_t>(max(0, min(64 / L, D - wd0)) * DS * 4);
   const uint32_t whoff = static_cast<uint32_t>(wd0) * DS * 4u;
-  float* const hblk = s_h + (HF ? 0 : wave * HBLK);
+  float* const hblk = s_h + ((HF || (K == 4 && DB == 16)) ? 0 : wave * HBLK);
+  // With four states per lane every 16-byte load of a block is one step row and each lane
+  // fetches exactly its own states, so the block goes straight to registers (hb) instead of
+  // through the per-wave LDS block.
+  constexpr bool HDIRECT = !HF && K == 4 && DB == 16;
+  static_assert(!HDIRECT || NQ == HB, "one load per step row");
   float hq[NQ][DB / 4];
+  float hb[HDIRECT ? NQ : 1][DB / 4];
   float hzero[K];
 #pragma unroll
   for (int i = 0; i < K; ++i) hzero[i] = 0.f;
@@ -341,6 +347,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
     }
   };
   auto park_hblock = [&](const float (&src)[NQ][DB / 4]) {
+    if constexpr (HDIRECT) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+#pragma unroll
+        for (int e = 0; e < DB / 4; ++e) hb[q][e] = src[q][e];
+      return;
+    }
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       float* dst = hblk + q * 16 * DB + lane * (DB / 4);
@@ -428,10 +441,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
         float hrow[S][K];  // H_{t-1} of the batch's steps
 #pragma unroll
         for (int s = 0; s < S; ++s) {
-          if constexpr (HF)
+          if constexpr (HF) {
             lds_load_vec<K>(&hsw[(tt0 + s) * WROW + lane * K], hrow[s]);
-          else
+          } else if constexpr (HDIRECT) {
+#pragma unroll
+            for (int i = 0; i < K; ++i) hrow[s][i] = hb[bt * S + s][i];
+          } else {
             lds_load_vec<K>(&hblk[(bt * S + s) * WROW + lane * K], hrow[s]);
+          }
         }
         if (!HF && bt == 0) {
           const bool first = ts + sb * HB == 0;  // step 0 of the sequence: H_{-1} = h0
