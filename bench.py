@@ -180,10 +180,12 @@ def main() -> int:
     fbytes = fwd_alg_bytes(B, T, D, DS, 4, with_H=True)
     bbytes = bwd_alg_bytes(B, T, D, DS, 4)
     f_avg, b_avg = float(fwd_ms.mean()), float(bwd_ms.mean())
-    # The dominant entry point is timed as one launch: sscan_bwd enqueues the sweep kernel and
-    # the kernel that adds its partial sums, back to back on the same stream.
+    # The dominant entry point is timed as one launch: sscan_bwd enqueues the local pass of
+    # its two-level sweep, the sweep and the kernel that adds its partial sums, back to back
+    # on the same stream.
     if b_avg >= f_avg:
-        dom, entry, dom_bytes, dom_ms = "sscan_bwd (bwd_kernel sweep + bwd_reduce_kernel)", "sscan_bwd", bbytes, b_avg
+        dom, entry, dom_bytes, dom_ms = ("sscan_bwd (bwd_local_kernel + bwd_kernel sweep + bwd_reduce_kernel)",
+                                         "sscan_bwd", bbytes, b_avg)
     else:
         dom, entry, dom_bytes, dom_ms = "sscan_fwd (fwd_kernel writing H)", "sscan_fwd", fbytes, f_avg
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
@@ -197,7 +199,7 @@ def main() -> int:
         "fwd_hbm_frac": round(fbytes / (f_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "bwd_hbm_frac": round(bbytes / (b_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "plan_fwd": {"lanes": plan_f.lanes, "chunks": plan_f.chunks},
-        "plan_bwd": {"lanes": plan_b.lanes},
+        "plan_bwd": {"lanes": plan_b.lanes, "chunks": plan_b.chunks},
         "wall_s_timed": round(wall, 4),
     }
     print(f"bench: step {step_ms:.4f} ms (fwd {f_avg:.4f}, bwd {b_avg:.4f})", file=sys.stderr, flush=True)

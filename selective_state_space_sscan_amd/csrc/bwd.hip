@@ -5,6 +5,22 @@
 namespace sscan {
 namespace {
 
+// src[0] + src[stride] + ... + src[(n-1) stride], added in that order, with eight loads
+// in flight at a time.
+__device__ __forceinline__ float ordered_sum(const float* src, int64_t stride, int n) {
+  float s = 0.f;
+  int k = 0;
+  for (; k + 8 <= n; k += 8) {
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = src[(int64_t)(k + q) * stride];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) s += v[q];
+  }
+  for (; k < n; ++k) s += src[(int64_t)k * stride];
+  return s;
+}
+
 // gb, gc: add the per-workgroup partials over channel tiles in ascending tile order.
 // gA: add the per-(chunk, batch row) partials in ascending order (then, for the Mamba
 // wrapper, scale by A = -exp(A_log): the gradient for A_log).  gDskip: likewise.
@@ -41,15 +57,12 @@ __global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(const ReduceParams
     p.gc[i] = sc;
   } else if (i < nbc + nA) {
     const int64_t e = i - nbc;
-    float s = 0.f;
-    for (int k = 0; k < p.chunks * p.B; ++k) s += p.part_A[(int64_t)k * nA + e];
+    float s = ordered_sum(p.part_A + e, nA, p.chunks * p.B);
     if (p.A_log != nullptr) s *= -expf(p.A_log[e]);
     p.gA[e] = s;
   } else if (p.gD != nullptr && i < nbc + nA + p.D) {
     const int64_t e = i - nbc - nA;
-    float s = 0.f;
-    for (int k = 0; k < p.chunks * p.B; ++k) s += p.part_D[(int64_t)k * p.D + e];
-    p.gD[e] = s;
+    p.gD[e] = ordered_sum(p.part_D + e, p.D, p.chunks * p.B);
   }
 }
 

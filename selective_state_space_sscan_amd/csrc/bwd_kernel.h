@@ -729,8 +729,12 @@ __global__ __launch_bounds__(kThreads) void bwd_local_kernel(const BwdParams p) 
       for (int s = S - 1; s >= 0; --s) {
 #pragma unroll
         for (int i = 0; i < K; ++i) G[i] = a[s][i] * fmaf(dd[s].y, cv[s][i], G[i]);
-        dsum += dd[s].x;
       }
+      // the batch's delta sum as a tree in fp32 (a few ulp), then one fp64 add per batch
+      float dls[S];
+#pragma unroll
+      for (int s = 0; s < S; ++s) dls[s] = dd[s].x;
+      dsum += static_cast<double>(tree_sum<S>(dls));
     }
   }
   if (!dvalid) return;

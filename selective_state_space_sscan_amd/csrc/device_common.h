@@ -175,6 +175,18 @@ __device__ __forceinline__ int xcd_grouped(int lin, int n, int G) {
   return base + (r % 8) * G + r / 8;
 }
 
+// v[0] + ... + v[N-1] as a balanced tree (N a power of two): the adds of each level are
+// independent, and the rounding grows with log2(N) rather than N.
+template <int N>
+__device__ __forceinline__ float tree_sum(const float* v) {
+  static_assert(N > 0 && (N & (N - 1)) == 0, "a power of two");
+  if constexpr (N == 1) {
+    return v[0];
+  } else {
+    return tree_sum<N / 2>(v) + tree_sum<N / 2>(v + N / 2);
+  }
+}
+
 // Hardware base-2 exponential (v_exp_f32).
 __device__ __forceinline__ float exp2_hw(float z) { return __builtin_amdgcn_exp2f(z); }
 

@@ -231,8 +231,7 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(const FwdParams p) {
         }
       }
       if constexpr (LOCAL) {
-#pragma unroll
-        for (int s = 0; s < S; ++s) dsum += dl[s];
+        dsum += static_cast<double>(tree_sum<S>(dl));  // the batch's delta sum as an fp32 tree
       } else {
         // readouts of S steps, independent of each other
 #pragma unroll
