@@ -89,24 +89,17 @@ int resolve_plan(const Resolved& r, const sscan_plan* plan, PlanKind kind, int* 
       return fail(SSCAN_ERR_UNSUPPORTED, "plan.chunks=%d out of range", plan->chunks);
   }
   // Measured on MI355X: the forward runs best with 8 lanes per channel (two states per
-  // lane) on every size tried; the backward with 4 lanes (four states per lane: a quarter
-  // of the per-workgroup gb/gc partials of one state per lane, and fewer cross-lane sums),
-  // split along T for occupancy (8x2048x768x16: 4 lanes and 8 chunks 0.285 ms, 16 lanes
-  // and 2 chunks 0.304 ms); the wrapper's backward, whose staging does more per element,
-  // with the fewest lanes (up to 16) that give 1.5 waves per SIMD before the T split
-  // (the same size: 16 lanes 0.311 ms, 4 lanes 0.329 ms).
+  // lane) on every size tried; the backward, plain or wrapped, with 4 lanes (four states per
+  // lane: a quarter of the per-workgroup gb/gc partials of one state per lane, and fewer
+  // cross-lane sums), split along T for occupancy (8x2048x768x16: 4 lanes and 8 chunks
+  // 0.268 ms, 16 lanes and 2 chunks 0.304 ms; the wrapper's 0.273 and 0.302 ms).
   int l;
   if (plan != nullptr && plan->lanes != 0) {
     l = plan->lanes;
   } else if (kind == kPlanFwd) {
     l = (int)(r.DS < 8 ? r.DS : 8);
-  } else if (kind == kPlanBwd) {
-    l = (int)(r.DS < 4 ? r.DS : 4);
   } else {
-    const int64_t maxl = r.DS < 16 ? r.DS : 16;
-    int64_t v = 1;
-    while (v < maxl && r.B * r.D * v < 3 * kLanesOneWavePerSimd / 2) v *= 2;
-    l = (int)v;
+    l = (int)(r.DS < 4 ? r.DS : 4);
   }
   int c = 1;
   if (backward) {

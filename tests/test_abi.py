@@ -181,7 +181,7 @@ def test_plan_select_and_workspace_sizes(lib):
     assert lib.sscan_plan_select(ctypes.byref(d), 1, ctypes.byref(p)) == OK
     assert p.lanes == 4 and p.chunks == 8  # 0.375 -> 3 waves per SIMD
     assert lib.sscan_plan_select(ctypes.byref(d), 2, ctypes.byref(p)) == OK  # the wrapper's backward
-    assert p.lanes == 16 and p.chunks == 2  # 1.5 -> 3 waves per SIMD
+    assert p.lanes == 4 and p.chunks == 8
     # backward partial buffers: one (gb, gc) pair per channel tile, step and state, plus gA per batch row
     d = desc(B=8, T=2048, D=768, DS=16)
     n = ctypes.c_size_t()
