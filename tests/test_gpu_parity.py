@@ -124,6 +124,9 @@ CHUNKED_BWD = [
     (2, 257, 70, 8, "f32", True, True, 8, 2),
     (2, 513, 20, 4, "bf16", True, True, 4, 4),
     (1, 128, 16, 16, "f32", True, True, 16, 4),
+    # four lanes per channel (the default), ragged T and D, two and eight sub-chunks per chunk
+    (2, 1000, 100, 16, "f32", True, True, 4, 8),
+    (1, 2048, 70, 16, "bf16", True, True, 4, 4),
 ]
 
 
