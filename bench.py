@@ -422,7 +422,8 @@ def bench_fwd_only(dev, warmup, reps):
         ms = e0.elapsed_time(e1) / reps
         elems = w.B * w.T * w.D
         states = elems * w.DS
-        out[name] = {"workload": w.note, "calls": len(bounds), "plan": {"lanes": plan.lanes, "chunks": plan.chunks},
+        out[name] = {"workload": w.note, "calls": len(bounds),
+                     "plan": {"lanes": plan.lanes, "chunks": plan.chunks, "layout": plan.layout},
                      "ms": round(ms, 5), "elems_per_s": elems / (ms * 1e-3),
                      "alu_frac": round(states / (ms * 1e-3) / peak, 4),
                      "hbm_frac": round(fwd_alg_bytes(w.B, w.T, w.D, w.DS, s) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}

@@ -95,11 +95,19 @@ typedef struct sscan_desc {
   int64_t y_bstride;  /* elements between batch rows of y, gx, gdelta; 0 means T*D */
 } sscan_desc;
 
+/* Forward layouts.  LANES: a 64-lane wave holds 64/lanes channels, the states of a channel
+ * split over `lanes` consecutive lanes (the only layout of the backward and of a forward
+ * that writes H).  STATE_GROUPS: lane l of every wave of a workgroup is channel d0 + l and
+ * wave w holds states 2w, 2w+1 of the workgroup's 64 channels (DS in {4, 8, 16}, D a
+ * multiple of 4, no H; its plan.lanes, the threads per channel, is DS/2). */
+typedef enum sscan_layout { SSCAN_LAYOUT_AUTO = 0, SSCAN_LAYOUT_LANES = 1, SSCAN_LAYOUT_STATE_GROUPS = 2 } sscan_layout;
+
 /* Launch plan.  Pass NULL wherever a plan is accepted to let the library choose. */
 typedef struct sscan_plan {
   int32_t lanes;       /* lanes sharing one channel's DS states: 1,2,4,8,16 and <= DS; 0 = choose */
   int32_t chunks;      /* T-chunks of the in-kernel two-level scan (forward) or sweep (backward); 1 = single pass, 0 = choose */
-  int32_t reserved[6]; /* must be 0 */
+  int32_t layout;      /* sscan_layout of the forward; AUTO = choose.  Entry points of the backward take AUTO or LANES */
+  int32_t reserved[5]; /* must be 0 */
 } sscan_plan;
 
 /* Forward.

@@ -34,6 +34,9 @@ EXPORTED = ("sscan_fwd", "sscan_fwd_workspace", "sscan_bwd", "sscan_bwd_workspac
 SSCAN_CKPT_STEPS = 32
 SSCAN_WRAP_NONE = 0
 SSCAN_WRAP_MAMBA = 1
+SSCAN_LAYOUT_AUTO = 0
+SSCAN_LAYOUT_LANES = 1
+SSCAN_LAYOUT_STATE_GROUPS = 2
 
 
 class sscan_desc(ctypes.Structure):
@@ -43,7 +46,8 @@ class sscan_desc(ctypes.Structure):
 
 
 class sscan_plan(ctypes.Structure):
-    _fields_ = [("lanes", ctypes.c_int32), ("chunks", ctypes.c_int32), ("reserved", ctypes.c_int32 * 6)]
+    _fields_ = [("lanes", ctypes.c_int32), ("chunks", ctypes.c_int32), ("layout", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 5)]
 
 
 class SScanError(RuntimeError):

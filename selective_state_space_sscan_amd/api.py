@@ -24,20 +24,27 @@ _IO = {torch.float32: _lib.SSCAN_F32, torch.bfloat16: _lib.SSCAN_BF16}
 
 
 class Plan:
-    """Launch plan override: ``lanes`` per channel and forward ``chunks`` (0 = library's choice)."""
+    """Launch plan override: ``lanes`` per channel, T-``chunks`` and the forward's ``layout``
+    (``"lanes"`` or ``"state_groups"``); 0 / None = the library's choice."""
 
-    def __init__(self, lanes: int = 0, chunks: int = 0):
+    _LAYOUTS = {None: 0, "lanes": 1, "state_groups": 2}
+
+    def __init__(self, lanes: int = 0, chunks: int = 0, layout: Optional[str] = None):
+        if layout not in self._LAYOUTS:
+            raise ValueError(f"layout must be one of {list(self._LAYOUTS)}, got {layout!r}")
         self.lanes = int(lanes)
         self.chunks = int(chunks)
+        self.layout = layout
 
     def _c(self) -> sscan_plan:
         p = sscan_plan()
         p.lanes = self.lanes
         p.chunks = self.chunks
+        p.layout = self._LAYOUTS[self.layout]
         return p
 
     def __repr__(self):
-        return f"Plan(lanes={self.lanes}, chunks={self.chunks})"
+        return f"Plan(lanes={self.lanes}, chunks={self.chunks}, layout={self.layout!r})"
 
 
 def _plan_ptr(plan: Optional[Plan]):
@@ -124,7 +131,7 @@ def sscan_plan_select(B: int, T: int, D: int, DS: int, io: torch.dtype = torch.f
     d = _desc(B, T, D, DS, _IO[io])
     p = sscan_plan()
     _lib.check(lib.sscan_plan_select(ctypes.byref(d), (2 if mamba else 1) if backward else 0, ctypes.byref(p)))
-    return Plan(p.lanes, p.chunks)
+    return Plan(p.lanes, p.chunks, "state_groups" if p.layout == 2 else "lanes")
 
 
 def sscan_fwd_workspace(B: int, T: int, D: int, DS: int, io: torch.dtype = torch.float32,

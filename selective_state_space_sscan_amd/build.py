@@ -22,7 +22,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsscan.so")
 
 ARCH = os.environ.get("SSCAN_OFFLOAD_ARCH", "gfx950")
-SOURCES = ["sscan_api.cpp", "fwd.hip", "fwd_mamba.hip", "bwd.hip", "bwd_mamba.hip", "bwd_hf.hip", "decode.hip"]
+SOURCES = ["sscan_api.cpp", "fwd.hip", "fwd_mamba.hip", "fwd_sg.hip", "fwd_sg_mamba.hip", "bwd.hip", "bwd_mamba.hip",
+           "bwd_hf.hip", "decode.hip"]
 
 
 def hipcc() -> str:

@@ -61,6 +61,23 @@ __device__ __forceinline__ void buf_store_io(rsrc_t r, uint32_t off, float v) {
   buf_store_elem(r, off, v, static_cast<IO*>(nullptr));
 }
 
+// Four consecutive elements of type IO at byte offset off (one 16-byte store for fp32,
+// one 8-byte store for bf16); the caller keeps all four inside the row.
+template <typename IO>
+__device__ __forceinline__ void store4_io(rsrc_t r, uint32_t off, float4 v) {
+  if constexpr (sizeof(IO) == 4) {
+    __attribute__((ext_vector_type(4))) uint32_t t;
+    t[0] = __float_as_uint(v.x); t[1] = __float_as_uint(v.y);
+    t[2] = __float_as_uint(v.z); t[3] = __float_as_uint(v.w);
+    __builtin_amdgcn_raw_buffer_store_b128(t, r, off, 0, 0);
+  } else {
+    __attribute__((ext_vector_type(2))) uint32_t t;
+    t[0] = static_cast<uint32_t>(from_f32<bf16_t>(v.x).bits) | (static_cast<uint32_t>(from_f32<bf16_t>(v.y).bits) << 16);
+    t[1] = static_cast<uint32_t>(from_f32<bf16_t>(v.z).bits) | (static_cast<uint32_t>(from_f32<bf16_t>(v.w).bits) << 16);
+    __builtin_amdgcn_raw_buffer_store_b64(t, r, off, 0, 0);
+  }
+}
+
 // Mamba-style step size: the softplus of a raw value in the thresholded form of the
 // POPCORNBENCH page (the argument itself above 20, else log(1 + e^v)), and its
 // derivative (1 above the threshold, else the logistic 1 / (1 + e^-v)).  Both use the

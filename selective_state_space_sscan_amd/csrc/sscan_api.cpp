@@ -81,8 +81,12 @@ enum PlanKind { kPlanFwd = 0, kPlanBwd = 1, kPlanMambaBwd = 2 };
 int resolve_plan(const Resolved& r, const sscan_plan* plan, PlanKind kind, int* lanes, int* chunks) {
   const bool backward = kind != kPlanFwd;
   if (plan != nullptr) {
-    for (int i = 0; i < 6; ++i)
+    for (int i = 0; i < 5; ++i)
       if (plan->reserved[i] != 0) return fail(SSCAN_ERR_UNSUPPORTED, "plan.reserved must be 0");
+    if (plan->layout < SSCAN_LAYOUT_AUTO || plan->layout > SSCAN_LAYOUT_STATE_GROUPS)
+      return fail(SSCAN_ERR_UNSUPPORTED, "plan.layout=%d is not an sscan_layout", plan->layout);
+    if (backward && plan->layout == SSCAN_LAYOUT_STATE_GROUPS)
+      return fail(SSCAN_ERR_UNSUPPORTED, "the backward runs the lanes layout only");
     if (plan->lanes != 0 && (!pow2_upto16(plan->lanes) || plan->lanes > r.DS))
       return fail(SSCAN_ERR_UNSUPPORTED, "plan.lanes=%d must be a power of two <= min(DS,16)", plan->lanes);
     if (plan->chunks < 0 || plan->chunks > 65535)
@@ -125,11 +129,12 @@ int resolve_plan(const Resolved& r, const sscan_plan* plan, PlanKind kind, int* 
       c = plan->chunks;
     } else {
       // Split the sequence when the single pass would leave at least half of the
-      // SIMDs idle; every chunk keeps at least 256 steps.
+      // SIMDs idle, aiming at two waves per SIMD; every chunk keeps at least 128 steps
+      // (8x1024x256x16 fp32: 8 chunks 0.031 ms, 4 chunks 0.036 ms, 16 chunks 0.034 ms).
       const int64_t lanes_total = r.B * r.D * l;
       if (lanes_total > 0 && 2 * lanes_total <= kLanesOneWavePerSimd) {
-        int64_t want = ceil_div(kLanesOneWavePerSimd, lanes_total);
-        int64_t cap = r.T / 256;
+        int64_t want = ceil_div(2 * kLanesOneWavePerSimd, lanes_total);
+        int64_t cap = r.T / 128;
         if (want > cap) want = cap;
         if (want > 16) want = 16;
         if (want > 1) c = (int)want;
@@ -143,17 +148,53 @@ int resolve_plan(const Resolved& r, const sscan_plan* plan, PlanKind kind, int* 
   return SSCAN_OK;
 }
 
+// The forward's plan: lanes, T-chunks and whether the state-group layout runs.  That
+// layout needs DS in {4, 8, 16}, D a multiple of 4 and no H (with_H).  Chosen by itself
+// where it measured faster: when there are at least 256 of its 64-channel workgroups per
+// pass (16x4096x1024x16 bf16: 0.334 ms with the packing against 0.347 ms); with fewer
+// its 512-thread workgroups cover too few CUs (4x2048x2048x16 bf16: 0.146 ms against
+// 0.125 ms), and split sequences gain nothing (8x1024x256x16 fp32: 0.049 against 0.039 ms).
+int resolve_fwd_plan(const Resolved& r, const sscan_plan* plan, bool with_H, int* lanes, int* chunks, bool* sg) {
+  const bool sg_ok = !with_H && (r.DS == 4 || r.DS == 8 || r.DS == 16) && r.D % 4 == 0;
+  const int sg_lanes = (int)(r.DS / sscan::kSgK);
+  const int want = plan != nullptr ? plan->layout : SSCAN_LAYOUT_AUTO;
+  if (want == SSCAN_LAYOUT_STATE_GROUPS) {
+    if (!sg_ok)
+      return fail(SSCAN_ERR_UNSUPPORTED, "the state-group layout needs DS in {4, 8, 16}, D a multiple of 4 and no H");
+    if (plan->lanes != 0 && plan->lanes != sg_lanes)
+      return fail(SSCAN_ERR_UNSUPPORTED, "the state-group layout runs DS/2 = %d threads per channel, not %d", sg_lanes,
+                  plan->lanes);
+  }
+  int st = resolve_plan(r, plan, kPlanFwd, lanes, chunks);
+  if (st != SSCAN_OK) return st;
+  *sg = false;
+  if (want == SSCAN_LAYOUT_STATE_GROUPS) {
+    *sg = true;
+  } else if (want == SSCAN_LAYOUT_AUTO && sg_ok && *lanes == sg_lanes) {
+    *sg = *chunks == 1 && r.B * ceil_div(r.D, 64) >= 256;
+  }
+  if (*sg) *lanes = sg_lanes;
+  return SSCAN_OK;
+}
+
 struct FwdLayout {
-  size_t pairs_off, hin_off, total;
+  size_t pairs_off, hin_off, bc_off, total;
+  int64_t tpad;  // state-group layout: steps of packed b/c per row
 };
 
-FwdLayout fwd_layout(const Resolved& r, int chunks) {
-  FwdLayout L{0, 0, 0};
-  if (chunks <= 1) return L;
+FwdLayout fwd_layout(const Resolved& r, int chunks, bool sg) {
+  FwdLayout L{0, 0, 0, 0, 0};
   const size_t nstate = (size_t)(r.B * r.D * r.DS);
-  L.pairs_off = 0;
-  L.hin_off = align_up(L.pairs_off + (size_t)(chunks - 1) * nstate * sizeof(float2), 256);
-  L.total = align_up(L.hin_off + (size_t)(chunks - 1) * nstate * sizeof(float), 256);
+  if (chunks > 1) {
+    L.pairs_off = 0;
+    L.hin_off = align_up(L.pairs_off + (size_t)(chunks - 1) * nstate * sizeof(float2), 256);
+    L.total = align_up(L.hin_off + (size_t)(chunks - 1) * nstate * sizeof(float), 256);
+  }
+  if (sg) {
+    L.tpad = ceil_div(r.T, sscan::kSgTile) * sscan::kSgTile;
+    L.bc_off = L.total;
+    L.total = align_up(L.bc_off + (size_t)(r.B * L.tpad * 2 * r.DS) * sizeof(float), 256);
+  }
   return L;
 }
 
@@ -237,7 +278,8 @@ int fwd_impl(bool mamba, const sscan_desc* desc, const sscan_plan* plan, const v
   int st = resolve_desc(desc, &r);
   if (st != SSCAN_OK) return st;
   int lanes, chunks;
-  st = resolve_plan(r, plan, kPlanFwd, &lanes, &chunks);
+  bool sg;
+  st = resolve_fwd_plan(r, plan, H != nullptr, &lanes, &chunks, &sg);
   if (st != SSCAN_OK) return st;
   if (r.B == 0 || r.D == 0) return ok();
   const bool steps = r.T > 0;
@@ -256,7 +298,7 @@ int fwd_impl(bool mamba, const sscan_desc* desc, const sscan_plan* plan, const v
     const hipError_t e = sscan::launch_copy_or_zero(hT, h0, r.B * r.D * r.DS, stream);
     return e == hipSuccess ? ok() : hip_fail(e, "hT <- h0");
   }
-  const FwdLayout lay = fwd_layout(r, chunks);
+  const FwdLayout lay = fwd_layout(r, chunks, sg);
   if (lay.total > 0) {
     if (ws == nullptr || ws_bytes < lay.total)
       return fail(SSCAN_ERR_WORKSPACE, "forward needs %zu workspace bytes, got %zu", lay.total, ws_bytes);
@@ -272,25 +314,37 @@ int fwd_impl(bool mamba, const sscan_desc* desc, const sscan_plan* plan, const v
   p.B = (int32_t)r.B; p.T = (int32_t)r.T; p.D = (int32_t)r.D;
   p.chunks = chunks;
   p.chunk_len = (int32_t)ceil_div(r.T, chunks);
-  if (hck != nullptr && chunks > 1) {
-    // boundary blocks must not straddle chunks: chunks start on multiples of 64 steps
-    // (a multiple of every forward tile and of the block length)
+  if ((hck != nullptr || sg) && chunks > 1) {
+    // boundary blocks must not straddle chunks, and the state-group layout's chunks are
+    // whole tiles: chunks start on multiples of 64 steps (a multiple of every forward
+    // tile and of the block length)
+    static_assert(64 % sscan::kSgTile == 0 && 64 % sscan::kCkptSteps == 0, "chunk alignment");
     p.chunk_len = (int32_t)(ceil_div(p.chunk_len, 64) * 64);
     p.chunks = (int32_t)ceil_div(r.T, p.chunk_len);
     chunks = p.chunks;
   }
-  const int64_t cpw = kThreads / lanes;
+  const int64_t cpw = sg ? 64 : kThreads / lanes;
   const int64_t ntiles_d = ceil_div(r.D, cpw);
   p.ntiles_d = (int32_t)ntiles_d;
-  p.xcd_group = xcd_group(lanes, r.io_size);
+  p.xcd_group = sg ? 1 : xcd_group(lanes, r.io_size);
   if (ntiles_d * r.B * chunks > std::numeric_limits<int32_t>::max())
     return fail(SSCAN_ERR_UNSUPPORTED, "too many workgroups");
   hipError_t e;
+  char* wsb = static_cast<char*>(ws);
+  if (sg) {
+    p.bcp = reinterpret_cast<float*>(wsb + lay.bc_off);
+    p.tpad = (int32_t)lay.tpad;
+    e = sscan::launch_bc_pack(r.io, (int)r.DS, p, stream);
+    if (e != hipSuccess) return hip_fail(e, "b/c packing");
+  }
+  auto pass = [&](bool local, unsigned blocks) {
+    return sg ? sscan::launch_fwd_sg(r.io, (int)r.DS, local, mamba, p, blocks, stream)
+              : sscan::launch_fwd(r.io, (int)r.DS, lanes, local, mamba, p, blocks, stream);
+  };
   if (chunks > 1) {
-    char* wsb = static_cast<char*>(ws);
     p.pairs = reinterpret_cast<float2*>(wsb + lay.pairs_off);
     p.hin = reinterpret_cast<const float*>(wsb + lay.hin_off);
-    e = sscan::launch_fwd(r.io, (int)r.DS, lanes, true, mamba, p, (unsigned)(ntiles_d * r.B * (chunks - 1)), stream);
+    e = pass(true, (unsigned)(ntiles_d * r.B * (chunks - 1)));
     if (e != hipSuccess) return hip_fail(e, "forward local pass");
     sscan::CarryParams cp{};
     cp.pairs = p.pairs;
@@ -301,7 +355,7 @@ int fwd_impl(bool mamba, const sscan_desc* desc, const sscan_plan* plan, const v
     e = sscan::launch_carry(cp, stream);
     if (e != hipSuccess) return hip_fail(e, "chunk carry");
   }
-  e = sscan::launch_fwd(r.io, (int)r.DS, lanes, false, mamba, p, (unsigned)(ntiles_d * r.B * chunks), stream);
+  e = pass(false, (unsigned)(ntiles_d * r.B * chunks));
   if (e != hipSuccess) return hip_fail(e, "forward pass");
   return ok();
 }
@@ -434,12 +488,16 @@ int sscan_plan_select(const sscan_desc* desc, int backward, sscan_plan* plan) {
   if (st != SSCAN_OK) return st;
   if (plan == nullptr) return fail(SSCAN_ERR_NULL, "plan is NULL");
   int lanes, chunks;
-  st = resolve_plan(r, nullptr, backward == 0 ? kPlanFwd : (backward == 2 ? kPlanMambaBwd : kPlanBwd), &lanes,
-                    &chunks);
+  bool sg = false;
+  if (backward == 0)
+    st = resolve_fwd_plan(r, nullptr, false, &lanes, &chunks, &sg);
+  else
+    st = resolve_plan(r, nullptr, backward == 2 ? kPlanMambaBwd : kPlanBwd, &lanes, &chunks);
   if (st != SSCAN_OK) return st;
   memset(plan, 0, sizeof(*plan));
   plan->lanes = lanes;
   plan->chunks = chunks;
+  plan->layout = sg ? SSCAN_LAYOUT_STATE_GROUPS : SSCAN_LAYOUT_LANES;
   return ok();
 }
 
@@ -449,9 +507,10 @@ int sscan_fwd_workspace(const sscan_desc* desc, const sscan_plan* plan, size_t* 
   if (st != SSCAN_OK) return st;
   if (bytes == nullptr) return fail(SSCAN_ERR_NULL, "bytes is NULL");
   int lanes, chunks;
-  st = resolve_plan(r, plan, kPlanFwd, &lanes, &chunks);
+  bool sg;
+  st = resolve_fwd_plan(r, plan, false, &lanes, &chunks, &sg);  // a call without H needs the most
   if (st != SSCAN_OK) return st;
-  *bytes = (r.B == 0 || r.D == 0 || r.T == 0) ? 0 : fwd_layout(r, chunks).total;
+  *bytes = (r.B == 0 || r.D == 0 || r.T == 0) ? 0 : fwd_layout(r, chunks, sg).total;
   return ok();
 }
 

@@ -8,6 +8,10 @@ namespace sscan {
 
 constexpr int kThreads = 256;  // every kernel runs 256-thread workgroups (4 wave64)
 constexpr int kCkptSteps = 32;  // steps between the boundary states of the H-free path
+// State-group forward: steps per tile (its two-level scan's chunks are whole tiles) and
+// states per lane (a workgroup has DS/kSgK waves of 64 channels).
+constexpr int kSgTile = 64;
+constexpr int kSgK = 2;
 
 // Storage type for bf16 I/O: the raw 16 bits.
 struct bf16_t {
@@ -39,6 +43,8 @@ struct FwdParams {
   const float* Dskip;  // Mamba wrapper: per-channel skip weight (D,), may be null (no skip)
   float* hck;          // H-free path: state entering every kCkptSteps-step block, (B,nck,D,DS), or null
   int32_t nck;         // ceil(T / kCkptSteps)
+  float* bcp;          // state-group forward: packed fp32 b/c, (B, DS/K, tpad, 2K)
+  int32_t tpad;        // state-group forward: steps of bcp per row (T rounded up to whole tiles)
   int64_t x_bs;        // batch stride of x, delta (elements)
   int64_t bc_bs;       // batch stride of b, c (elements)
   int64_t y_bs;        // batch stride of y (elements)
@@ -127,6 +133,14 @@ hipError_t launch_fwd_plain(int io, int DS, int lanes, bool local_pass, const Fw
 hipError_t launch_fwd_mamba(int io, int DS, int lanes, bool local_pass, const FwdParams& p, unsigned blocks,
                             hipStream_t s);
 hipError_t launch_carry(const CarryParams& p, hipStream_t s);
+// State-group forward (no H; DS in {4, 8, 16}, D a multiple of 4): the packing of b and c
+// into p.bcp, which must precede the passes, and a pass (local or full) over 64-channel
+// workgroups of DS/kSgK waves.
+hipError_t launch_bc_pack(int io, int DS, const FwdParams& p, hipStream_t s);
+hipError_t launch_fwd_sg(int io, int DS, bool local_pass, bool mamba, const FwdParams& p, unsigned blocks,
+                         hipStream_t s);
+hipError_t launch_fwd_sg_plain(int io, int DS, bool local_pass, const FwdParams& p, unsigned blocks, hipStream_t s);
+hipError_t launch_fwd_sg_mamba(int io, int DS, bool local_pass, const FwdParams& p, unsigned blocks, hipStream_t s);
 hipError_t launch_bwd(int io, int DS, int lanes, bool local_pass, bool mamba, const BwdParams& p, unsigned blocks,
                       hipStream_t s);
 hipError_t launch_bwd_plain(int io, int DS, int lanes, bool local_pass, const BwdParams& p, unsigned blocks,

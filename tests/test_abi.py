@@ -45,10 +45,11 @@ def fwd(lib, d, plan=None, x=FAKE, delta=FAKE, A=FAKE, b=FAKE, c=FAKE, h0=None, 
 
 
 def bwd(lib, d, dy=FAKE, x=FAKE, delta=FAKE, A=FAKE, b=FAKE, c=FAKE, h0=None, H=FAKE, gx=FAKE, gd=FAKE, gb=FAKE,
-        gc=FAKE, gA=FAKE, gh0=None, ws=None, ws_bytes=0):
+        gc=FAKE, gA=FAKE, gh0=None, ws=None, ws_bytes=0, plan=None):
     v = lambda p: None if p is None else ctypes.c_void_p(p)
-    return lib.sscan_bwd(ctypes.byref(d), None, v(dy), None, v(x), v(delta), v(A), v(b), v(c), v(h0), v(H), v(gx),
-                         v(gd), v(gb), v(gc), v(gA), v(gh0), v(ws), ctypes.c_size_t(ws_bytes), None)
+    return lib.sscan_bwd(ctypes.byref(d), None if plan is None else ctypes.byref(plan), v(dy), None, v(x), v(delta),
+                         v(A), v(b), v(c), v(h0), v(H), v(gx), v(gd), v(gb), v(gc), v(gA), v(gh0), v(ws),
+                         ctypes.c_size_t(ws_bytes), None)
 
 
 def test_header_declares_the_expected_functions():
@@ -119,6 +120,36 @@ def test_plan_validation(lib):
     assert fwd(lib, desc(), plan=p) == E_UNSUP
 
 
+def test_layout_validation_and_choice(lib):
+    LANES, SG = 1, 2
+    p = sscan_plan()
+    p.layout = 3
+    assert fwd(lib, desc(), plan=p) == E_UNSUP
+    p.layout = SG
+    assert fwd(lib, desc(DS=16), plan=p, H=FAKE) == E_UNSUP   # the state-group layout writes no H
+    assert fwd(lib, desc(DS=2), plan=p) == E_UNSUP            # DS in {4, 8, 16}
+    assert fwd(lib, desc(DS=16, D=18), plan=p) == E_UNSUP     # D a multiple of 4
+    p.lanes = 4                                                # it runs DS/2 = 8 threads per channel
+    assert fwd(lib, desc(DS=16), plan=p) == E_UNSUP
+    p.lanes = 0
+    assert fwd(lib, desc(DS=16), plan=p) == E_WS               # valid plan; b/c packing needs workspace
+    assert bwd(lib, desc(DS=16), plan=p) == E_UNSUP           # the backward runs the lanes layout only
+    # the library's choice: state groups where a single pass has 256 or more 64-channel
+    # workgroups, lanes otherwise
+    for (B, T, D, DS), (layout, lanes, chunks) in {(16, 4096, 1024, 16): (SG, 8, 1), (8, 1024, 256, 16): (LANES, 8, 8),
+                                                   (4, 2048, 2048, 16): (LANES, 8, 1),
+                                                   (8, 2048, 768, 16): (LANES, 8, 1)}.items():
+        d = desc(B=B, T=T, D=D, DS=DS)
+        q = sscan_plan()
+        assert lib.sscan_plan_select(ctypes.byref(d), 0, ctypes.byref(q)) == OK
+        assert (q.layout, q.lanes, q.chunks) == (layout, lanes, chunks), (B, T, D, DS)
+    # its workspace holds fp32 b and c for every step rounded up to 64
+    d = desc(B=16, T=4000, D=1024, DS=16)
+    n = ctypes.c_size_t()
+    assert lib.sscan_fwd_workspace(ctypes.byref(d), None, ctypes.byref(n)) == OK
+    assert n.value >= 16 * 4032 * 2 * 16 * 4
+
+
 def test_forward_workspace_required_for_chunked_plan(lib):
     p = sscan_plan()
     p.lanes, p.chunks = 4, 4
@@ -174,7 +205,7 @@ def test_plan_select_and_workspace_sizes(lib):
     d = desc(B=8, T=1024, D=256, DS=16)
     p = sscan_plan()
     assert lib.sscan_plan_select(ctypes.byref(d), 0, ctypes.byref(p)) == OK
-    assert p.lanes == 8 and p.chunks == 4
+    assert p.lanes == 8 and p.chunks == 8
     assert lib.sscan_plan_select(ctypes.byref(d), 1, ctypes.byref(p)) == OK
     assert p.lanes == 4 and p.chunks == 16  # 2048 channels x 4 lanes x 16 chunks = 2 waves per SIMD (T caps it)
     d = desc(B=8, T=2048, D=768, DS=16)
