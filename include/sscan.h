@@ -97,9 +97,9 @@ typedef struct sscan_desc {
 
 /* Forward layouts.  LANES: a 64-lane wave holds 64/lanes channels, the states of a channel
  * split over `lanes` consecutive lanes (the only layout of the backward and of a forward
- * that writes H).  STATE_GROUPS: lane l of every wave of a workgroup is channel d0 + l and
- * wave w holds states 2w, 2w+1 of the workgroup's 64 channels (DS in {4, 8, 16}, D a
- * multiple of 4, no H; its plan.lanes, the threads per channel, is DS/2). */
+ * that writes H).  STATE_GROUPS: a workgroup holds 64 (or 32) channels, one per lane, and
+ * the states of a channel in pairs across its waves (DS in {4, 8, 16}, D a multiple of 4,
+ * T < 2^24, no H; its plan.lanes, the threads per channel, is DS/2). */
 typedef enum sscan_layout { SSCAN_LAYOUT_AUTO = 0, SSCAN_LAYOUT_LANES = 1, SSCAN_LAYOUT_STATE_GROUPS = 2 } sscan_layout;
 
 /* Launch plan.  Pass NULL wherever a plan is accepted to let the library choose. */

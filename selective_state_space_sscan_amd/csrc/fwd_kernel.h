@@ -40,9 +40,10 @@ __host__ __device__ constexpr int fwd_batch_steps() {
 }
 
 // MODE: kLocal (local pass of the two-level scan: no outputs but the chunk pair),
-// kFull (y and hT), kFullH (y, hT and H).  Whether H is stored is a compile-time
-// choice so that the stores are unconditional in the step code.
-constexpr int kLocal = 0, kFull = 1, kFullH = 2;
+// kFull (y and hT), kFullH (y, hT and H), kFullCk (y, hT and the H-free path's boundary
+// states).  What is stored is a compile-time choice so that the stores are unconditional
+// in the step code.
+constexpr int kLocal = 0, kFull = 1, kFullH = 2, kFullCk = 3;
 
 // MAMBA: the Mamba-style wrapper -- delta is read as delta_raw and passed through the
 // thresholded softplus when it is staged, A is read as A_log (A = -exp(A_log)), and the
@@ -92,6 +93,8 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(const FwdParams p) {
 
   const int64_t nstate = (int64_t)p.B * D * DS;
   const int64_t soff = ((int64_t)bb * D + d) * DS + j * K;  // this lane's states in (B,D,DS)
+  const rsrc_t rCk = make_rsrc(MODE == kFullCk ? p.hck + (int64_t)bb * p.nck * D * DS : nullptr,
+                               MODE == kFullCk ? static_cast<uint32_t>((int64_t)p.nck * D * DS * 4) : 0u);
 
   float A2[K], h[K];
   if (dvalid) {
@@ -199,12 +202,17 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(const FwdParams p) {
     const rsrc_t rH = make_rsrc(Hrow + (int64_t)ts * D * DS, static_cast<uint32_t>(rows) * hstep);
 #pragma unroll
     for (int s0 = 0; s0 < TB; s0 += S) {
-      if constexpr (MODE == kFull) {
-        // H-free path: the state entering every block of kCkptSteps steps (S divides it and
-        // every tile starts on a multiple of S, so each block start begins a batch).  Batches
-        // past the end of the chunk are padding: their block indices lie beyond the array.
-        if (p.hck != nullptr && dvalid && ts + s0 < t_end && ((ts + s0) % kCkptSteps) == 0)
-          store_state<K>(p.hck + (((int64_t)bb * p.nck + (ts + s0) / kCkptSteps) * D + d) * DS + j * K, h);
+      if constexpr (MODE == kFullCk) {
+        // H-free path: the state entering every block of kCkptSteps steps.  S divides the
+        // block length and tiles start on multiples of min(TB, kCkptSteps), so block starts
+        // are batch starts; where the tile holds whole blocks they are fixed batches.  The
+        // store is unconditional (out of range elsewhere, and past the end of the chunk, where
+        // batches are padding), so the wait counts stay the same on every path.
+        if (s0 % (TB < kCkptSteps ? TB : kCkptSteps) == 0) {  // a constant once the loop is unrolled
+          const bool ok = dvalid && ts + s0 < t_end && (ts + s0) % kCkptSteps == 0;
+          buf_store_vec<K>(rCk, ok ? static_cast<uint32_t>((((ts + s0) / kCkptSteps) * D + d) * DS + j * K) * 4u
+                                   : kOutOfRange, h);
+        }
       }
       // decays and injections of S steps: independent of the state, issued together
       float a[S][K], u[S][K];
@@ -281,6 +289,8 @@ hipError_t launch_fwd_t(bool local_pass, const FwdParams& p, unsigned blocks, hi
     hipLaunchKernelGGL((fwd_kernel<IO, DS, L, kLocal, MAMBA>), dim3(blocks), dim3(kThreads), 0, s, p);
   else if (p.H != nullptr)
     hipLaunchKernelGGL((fwd_kernel<IO, DS, L, kFullH, MAMBA>), dim3(blocks), dim3(kThreads), 0, s, p);
+  else if (p.hck != nullptr)
+    hipLaunchKernelGGL((fwd_kernel<IO, DS, L, kFullCk, MAMBA>), dim3(blocks), dim3(kThreads), 0, s, p);
   else
     hipLaunchKernelGGL((fwd_kernel<IO, DS, L, kFull, MAMBA>), dim3(blocks), dim3(kThreads), 0, s, p);
   return hipGetLastError();

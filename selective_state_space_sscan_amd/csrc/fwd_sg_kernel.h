@@ -5,21 +5,22 @@
 // Recurrence ("pssa-100m/pssa_kernels.py" page, module docstring and scan_fwd):
 //   h_t = exp(delta_t * A) * h_{t-1} + delta_t * b_t * x_t,   y_t = <h_t, c_t>.
 //
-// Work decomposition.  A workgroup owns one batch row and 64 consecutive channels: lane
-// l of every wave is channel d0 + l, and wave w holds the K states n = wK .. wK+K-1 of
-// all 64 channels (NW = DS/K waves).  Within a wave, b_t and c_t of its K states are the
-// same for every lane.  A small packing kernel lays them out per (batch row, state
-// group) as fp32, contiguous over steps; each 16-lane row of a wave loads the same block
-// of them (lane p holds floats 4p .. 4p+3 of a 64-float block), and every use reads the
-// value it needs from the lane that holds it with a DPP row broadcast folded into the
-// multiply (row_newbcast), so b and c cost neither LDS traffic nor extra instructions.
-// The workgroup stages (delta, delta*x) of a tile once in LDS (each element converted by
-// one thread, the softplus of the wrapper applied there), and every wave reads its lane's
-// channel from it.  Each wave leaves its partial sum over its K states of h * c per (step,
-// channel) in LDS, and after the tile the workgroup adds the NW partials and stores y
-// coalesced.  Per (step, state) a lane does one v_exp_f32 and four fp32 operations, with
-// no other cross-lane traffic: about 5.6 instructions per state against 7 for the
-// lane-split forward, which spends 1.5 on DPP sums over a channel's lanes.
+// Work decomposition.  A workgroup owns one batch row and CW consecutive channels (CW =
+// 64 or 32): lane l of a wave is channel d0 + l % CW, and the wave's 64/CW groups of CW
+// lanes hold state groups of K states each, NG = DS/K groups over the workgroup's waves.
+// Within a 16-lane row, b_t and c_t of its group's K states are the same for every lane.
+// A small packing kernel lays them out per (batch row, state group) as fp32, contiguous
+// over steps; each row loads its group's block of them (lane q holds floats 4q .. 4q+3 of
+// a 64-float block), and every use reads the value it needs from the lane that holds it
+// with a DPP row broadcast folded into the multiply (row_newbcast), so b and c cost
+// neither LDS traffic nor extra instructions.  The workgroup stages (delta, delta*x) of a
+// tile once in LDS (each element converted by one thread, the softplus of the wrapper
+// applied there), and every lane reads its channel's from it.  Each group leaves its
+// partial sum over its K states of h * c per (step, channel) in LDS, and after the tile
+// the workgroup adds the NG partials and stores y coalesced.  Per (step, state) a lane
+// does one v_exp_f32 and four fp32 operations, with no other cross-lane traffic: about 5.7
+// instructions per state against 7 for the lane-split forward, which spends 1.5 on DPP
+// sums over a channel's lanes.
 //
 // Steps past the end of the chunk load delta = 0 and b = c = 0 (buffer range checks),
 // which leaves the state bit-for-bit unchanged.
@@ -29,26 +30,26 @@
 namespace sscan {
 namespace {
 
-// Packed b/c: element (bb, w, t, e) at ((bb * NW + w) * tpad + t) * 2K + e holds
-// b[bb, t, wK + e] for e < K and c[bb, t, wK + e - K] otherwise; zero for t >= T.  One
-// thread per (bb, w, t) writes its 2K floats together; neighbouring threads take
-// neighbouring steps, so the stores are contiguous.
+// Packed b/c: element (bb, g, t, e) at ((bb * NG + g) * tpad + t) * 2K + e holds
+// b[bb, t, gK + e] for e < K and c[bb, t, gK + e - K] otherwise (state group g of NG =
+// DS/K); zero for t >= T.  One thread per (bb, g, t) writes its 2K floats together;
+// neighbouring threads take neighbouring steps, so the stores are contiguous.
 template <typename IO, int DS, int K>
 __global__ __launch_bounds__(kThreads) void bc_pack_kernel(const FwdParams p) {
-  constexpr int NW = DS / K;
+  constexpr int NG = DS / K;
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const int64_t total = (int64_t)p.B * NW * p.tpad;
+  const int64_t total = (int64_t)p.B * NG * p.tpad;
   if (i >= total) return;
   const int t = static_cast<int>(i % p.tpad);
   const int64_t r = i / p.tpad;
-  const int w = static_cast<int>(r % NW);
-  const int64_t bb = r / NW;
+  const int g = static_cast<int>(r % NG);
+  const int64_t bb = r / NG;
   float v[2 * K];
 #pragma unroll
   for (int e = 0; e < 2 * K; ++e) v[e] = 0.f;
   if (t < p.T) {
-    const IO* b = static_cast<const IO*>(p.b) + bb * p.bc_bs + (int64_t)t * DS + w * K;
-    const IO* c = static_cast<const IO*>(p.c) + bb * p.bc_bs + (int64_t)t * DS + w * K;
+    const IO* b = static_cast<const IO*>(p.b) + bb * p.bc_bs + (int64_t)t * DS + g * K;
+    const IO* c = static_cast<const IO*>(p.c) + bb * p.bc_bs + (int64_t)t * DS + g * K;
 #pragma unroll
     for (int e = 0; e < K; ++e) {
       v[e] = to_f32(b[e]);
@@ -106,38 +107,47 @@ __device__ __forceinline__ void fmac_bcast_rt(float& acc, float c, float h, int 
 }
 
 // MODE: 0 the two-level scan's local pass (only the chunk pair leaves the kernel), 1 y and
-// hT, 2 y, hT and the H-free path's boundary states.
-template <typename IO, int DS, int K, int MODE, bool MAMBA>
-__global__ __launch_bounds__(64 * (DS / K)) void fwd_sg_kernel(const FwdParams p) {
+// hT, 2 y, hT and the H-free path's boundary states.  CW: channels per wave (64 or 32); a
+// wave holds 64/CW state groups, one per CW/16 rows, so every 16-lane row belongs to a
+// single group and its DPP row broadcasts stay within it.
+template <typename IO, int DS, int K, int CW, int MODE, bool MAMBA>
+__global__ __launch_bounds__(64 * (DS / K) / (64 / CW)) void fwd_sg_kernel(const FwdParams p) {
   constexpr bool LOCAL = MODE == 0;
-  constexpr int NW = DS / K;
+  constexpr int NG = DS / K;        // state groups
+  constexpr int GPW = 64 / CW;      // state groups per wave
+  constexpr int NW = NG / GPW;      // waves per workgroup
   constexpr int NT = 64 * NW;
   constexpr int TB = kSgTile;
   constexpr int S = 4;  // steps per batch
   constexpr int E2 = 2 * K;
   constexpr uint32_t ES = sizeof(IO);
-  constexpr int TILE = TB * 64;     // (step, channel) elements of a tile
+  constexpr int TILE = TB * CW;     // (step, channel) elements of a tile
   constexpr int PER = TILE / NT;    // elements each thread stages
-  constexpr int GROUPS = TB * 16;   // (step, 4-channel group) items of a tile's readout
+  constexpr int C4 = CW / 4;        // 4-channel groups of a step
+  constexpr int GROUPS = TB * C4;   // (step, 4-channel group) items of a tile's readout
   constexpr int NB = TB * E2 / 64;  // 64-float blocks of packed b/c per tile
-  static_assert(TILE % NT == 0 && TB % S == 0 && kCkptSteps % S == 0 && (TB * E2) % 64 == 0, "tile shape");
+  static_assert(CW % 16 == 0 && NG % GPW == 0 && NW >= 1, "rows of one state group");
+  static_assert(TILE % NT == 0 && TB % S == 0 && TB % kCkptSteps == 0 && kCkptSteps % S == 0 && (TB * E2) % 64 == 0,
+                "tile shape");
 
-  // (delta, delta*x) at [step*64 + channel]; with the wrapper (delta, x), so that the
-  // first wave can add the skip term Dskip * x to its partial sums
+  // (delta, delta*x) at [step*CW + channel]; with the wrapper (delta, x), so that the
+  // first state group can add the skip term Dskip * x to its partial sums
   __shared__ float2 s_dw[TILE];
-  __shared__ float4 s_y[LOCAL ? 1 : NW * TB * 16];  // [w][step][channel / 4]
+  __shared__ float4 s_y[LOCAL ? 1 : NG * TB * C4];  // [group][step][channel / 4]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane % CW;             // this lane's channel within the workgroup
+  const int grp = w * GPW + lane / CW;  // this lane's state group
   const int lin = blockIdx.x;
   const int dtile = lin % p.ntiles_d;
   const int rest = lin / p.ntiles_d;
   const int bb = rest % p.B;
   const int chunk = rest / p.B;
   const int D = p.D;
-  const int d0 = dtile * 64;
-  const int d = d0 + lane;
+  const int d0 = dtile * CW;
+  const int d = d0 + c;
   const bool dvalid = d < D;
   const int t_begin = chunk * p.chunk_len;
   const int t_end = min(p.T, t_begin + p.chunk_len);
@@ -145,17 +155,19 @@ __global__ __launch_bounds__(64 * (DS / K)) void fwd_sg_kernel(const FwdParams p
   const IO* xrow = static_cast<const IO*>(p.x) + (int64_t)bb * p.x_bs;
   const IO* drow = static_cast<const IO*>(p.delta) + (int64_t)bb * p.x_bs;
   IO* yrow = static_cast<IO*>(p.y) + (int64_t)bb * p.y_bs;
-  // this wave's packed b/c row; lane p of each 16-lane row loads floats 4p .. 4p+3 of
-  // every 64-float block
-  const rsrc_t rBC = make_rsrc(p.bcp + ((int64_t)bb * NW + w) * p.tpad * E2, static_cast<uint32_t>(p.tpad) * E2 * 4u);
-  const uint32_t bclane = static_cast<uint32_t>(lane & 15) * 16u;
+  // the packed b/c rows of this batch row; lane q of each 16-lane row loads floats
+  // 4q .. 4q+3 of every 64-float block of its group's row
+  const rsrc_t rBC = make_rsrc(p.bcp + (int64_t)bb * NG * p.tpad * E2, static_cast<uint32_t>(NG * p.tpad * E2) * 4u);
+  const uint32_t bcrow = static_cast<uint32_t>(grp * p.tpad * E2) * 4u + static_cast<uint32_t>(lane & 15) * 16u;
 
   const int64_t nstate = (int64_t)p.B * D * DS;
-  const int64_t soff = ((int64_t)bb * D + d) * DS + w * K;  // this lane's states in (B,D,DS)
+  const int64_t soff = ((int64_t)bb * D + d) * DS + grp * K;  // this lane's states in (B,D,DS)
+  const rsrc_t rCk = make_rsrc(MODE == 2 ? p.hck + (int64_t)bb * p.nck * D * DS : nullptr,
+                               MODE == 2 ? static_cast<uint32_t>((int64_t)p.nck * D * DS * 4) : 0u);
 
   float A2[K], h[K];
   if (dvalid) {
-    lds_load_vec<K>(p.A + (int64_t)d * DS + w * K, A2);
+    lds_load_vec<K>(p.A + (int64_t)d * DS + grp * K, A2);
 #pragma unroll
     for (int i = 0; i < K; ++i) A2[i] = (MAMBA ? -expf(A2[i]) : A2[i]) * kLog2e;
     if (LOCAL || (chunk == 0 && p.h0 == nullptr)) {
@@ -172,17 +184,17 @@ __global__ __launch_bounds__(64 * (DS / K)) void fwd_sg_kernel(const FwdParams p
   }
   double dsum = 0.0;  // local pass: sum of delta over the chunk
 
-  // staged elements: idx = tid + e*NT is (step idx / 64, channel idx % 64); columns past D
+  // staged elements: idx = tid + e*NT is (step idx / CW, channel idx % CW); columns past D
   // are forced out of range, rows past the chunk fall outside the resource
   uint32_t xoff[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     const int idx = tid + e * NT;
-    const int dd = d0 + (idx & 63);
-    xoff[e] = dd < D ? static_cast<uint32_t>((idx >> 6) * D + dd) * ES : kOutOfRange;
+    const int dd = d0 + (idx % CW);
+    xoff[e] = dd < D ? static_cast<uint32_t>((idx / CW) * D + dd) * ES : kOutOfRange;
   }
-  // the skip weight of this lane's channel (used by the first wave)
-  const float dskip = (MAMBA && !LOCAL && w == 0 && p.Dskip != nullptr && dvalid) ? p.Dskip[d] : 0.f;
+  // the skip weight of this lane's channel (used by the first state group)
+  const float dskip = (MAMBA && !LOCAL && grp == 0 && p.Dskip != nullptr && dvalid) ? p.Dskip[d] : 0.f;
   float rx[PER], rd[PER];
   int pend_rows = 0;
   auto load_tile = [&](int ts) {
@@ -202,7 +214,7 @@ __global__ __launch_bounds__(64 * (DS / K)) void fwd_sg_kernel(const FwdParams p
     for (int e = 0; e < PER; ++e) {
       // padded steps and channels keep delta = 0 (a multiply by a 0/1 mask: a select
       // lets the compiler branch around the softplus)
-      const float keep = (((tid + e * NT) >> 6) < pend_rows && xoff[e] != kOutOfRange) ? 1.f : 0.f;
+      const float keep = (((tid + e * NT) / CW) < pend_rows && xoff[e] != kOutOfRange) ? 1.f : 0.f;
       const float dl = MAMBA ? softplus_th(rd[e]) * keep : rd[e];
       s_dw[tid + e * NT] = make_float2(dl, MAMBA ? rx[e] : dl * rx[e]);
     }
@@ -211,7 +223,10 @@ __global__ __launch_bounds__(64 * (DS / K)) void fwd_sg_kernel(const FwdParams p
   auto load_bc = [&](int ts, float (&dst)[NB][4]) {
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
-      const auto t = __builtin_amdgcn_raw_buffer_load_b128(rBC, static_cast<uint32_t>(ts) * E2 * 4u + k * 256u + bclane, 0, 0);
+      // past the end of the row a load reads the next group's (or no) data: such a tile
+      // is never processed
+      const auto t = __builtin_amdgcn_raw_buffer_load_b128(rBC, bcrow + static_cast<uint32_t>(ts) * E2 * 4u + k * 256u,
+                                                           0, 0);
       dst[k][0] = __uint_as_float(t[0]); dst[k][1] = __uint_as_float(t[1]);
       dst[k][2] = __uint_as_float(t[2]); dst[k][3] = __uint_as_float(t[3]);
     }
@@ -239,14 +254,21 @@ __global__ __launch_bounds__(64 * (DS / K)) void fwd_sg_kernel(const FwdParams p
 #pragma unroll
     for (int s0 = 0; s0 < TB; s0 += S) {
       if constexpr (MODE == 2) {
-        if (dvalid && ts + s0 < t_end && ((ts + s0) % kCkptSteps) == 0)
-          store_state<K>(p.hck + (((int64_t)bb * p.nck + (ts + s0) / kCkptSteps) * D + d) * DS + w * K, h);
+        // the state entering every kCkptSteps-step block: tiles start on multiples of the
+        // block length, so block starts are fixed batches of the tile; the store is
+        // unconditional (out of range past the chunk), so the wait counts stay the same on
+        // every path
+        if (s0 % kCkptSteps == 0) {  // a constant once the batch loop is unrolled
+          const bool ok = dvalid && ts + s0 < t_end;
+          buf_store_vec<K>(rCk, ok ? static_cast<uint32_t>((((ts + s0) / kCkptSteps) * D + d) * DS + grp * K) * 4u
+                                   : kOutOfRange, h);
+        }
       }
       float2 dw[S];
       float xs[S];  // with the wrapper: x of the step (dw[s].y becomes delta * x)
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        dw[s] = s_dw[(s0 + s) * 64 + lane];
+        dw[s] = s_dw[(s0 + s) * CW + c];
         xs[s] = dw[s].y;
         if constexpr (MAMBA) dw[s].y *= dw[s].x;
       }
@@ -275,7 +297,7 @@ __global__ __launch_bounds__(64 * (DS / K)) void fwd_sg_kernel(const FwdParams p
         for (int s = 0; s < S; ++s) dls[s] = dw[s].x;
         dsum += static_cast<double>(tree_sum<S>(dls));
       } else {
-        float* sy = reinterpret_cast<float*>(s_y) + (w * TB + s0) * 64 + lane;
+        float* sy = reinterpret_cast<float*>(s_y) + (grp * TB + s0) * CW + c;
 #pragma unroll
         for (int s = 0; s < S; ++s) {
           float yp;
@@ -284,8 +306,8 @@ __global__ __launch_bounds__(64 * (DS / K)) void fwd_sg_kernel(const FwdParams p
             const int q = (s0 + s) * E2 + K + i;  // c_i
             fmac_bcast_rt(yp, bcv[q / 64][q % 4], a[s][i], (q % 64) / 4, i == 0);
           }
-          if constexpr (MAMBA) yp = fmaf(dskip, xs[s], yp);  // the skip term (dskip = 0 past the first wave)
-          sy[s * 64] = yp;
+          if constexpr (MAMBA) yp = fmaf(dskip, xs[s], yp);  // the skip term (dskip = 0 past the first group)
+          sy[s * CW] = yp;
         }
       }
     }
@@ -295,19 +317,19 @@ __global__ __launch_bounds__(64 * (DS / K)) void fwd_sg_kernel(const FwdParams p
       const rsrc_t rY = make_rsrc(yrow + (int64_t)ts * D, static_cast<uint32_t>(rows * D) * ES);
 #pragma unroll
       for (int g0 = 0; g0 < GROUPS; g0 += NT) {
-        // every thread stores (out of range when it has no group), so the number of
+        // every thread stores (out of range when it has no item), so the number of
         // stores in flight does not depend on the thread
         const int g = g0 + tid;
         const bool act = GROUPS % NT == 0 || g < GROUPS;
-        const int s = act ? (g >> 4) : 0;
-        const int c4 = g & 15;
-        float4 acc = s_y[s * 16 + c4];
+        const int s = act ? (g / C4) : 0;
+        const int c4 = g % C4;
+        float4 acc = s_y[s * C4 + c4];
 #pragma unroll
-        for (int ww = 1; ww < NW; ++ww) {
-          const float4 v = s_y[(ww * TB + s) * 16 + c4];
+        for (int gg = 1; gg < NG; ++gg) {
+          const float4 v = s_y[(gg * TB + s) * C4 + c4];
           acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
         }
-        // D is a multiple of 4 for this kernel: a group is wholly inside or outside
+        // D is a multiple of 4 for this kernel: a 4-channel item is wholly inside or outside
         const int dd = d0 + 4 * c4;
         store4_io<IO>(rY, (act && dd < D) ? static_cast<uint32_t>(s * D + dd) * ES : kOutOfRange, acc);
       }
@@ -328,24 +350,52 @@ __global__ __launch_bounds__(64 * (DS / K)) void fwd_sg_kernel(const FwdParams p
 
 template <typename IO, int DS, int K>
 hipError_t launch_bc_pack_t(const FwdParams& p, hipStream_t s) {
-  constexpr int NW = DS / K;
-  const int64_t npack = (int64_t)p.B * NW * p.tpad;
+  constexpr int NG = DS / K;
+  const int64_t npack = (int64_t)p.B * NG * p.tpad;
   if (npack > 0)
     hipLaunchKernelGGL((bc_pack_kernel<IO, DS, K>), dim3((unsigned)((npack + kThreads - 1) / kThreads)),
                        dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
-template <typename IO, int DS, int K, bool MAMBA>
+template <typename IO, int DS, int K, int CW, bool MAMBA>
 hipError_t launch_fwd_sg_t(bool local_pass, const FwdParams& p, unsigned blocks, hipStream_t s) {
-  constexpr int NW = DS / K;
+  constexpr int NT = 64 * (DS / K) / (64 / CW);
   if (local_pass)
-    hipLaunchKernelGGL((fwd_sg_kernel<IO, DS, K, 0, MAMBA>), dim3(blocks), dim3(64 * NW), 0, s, p);
+    hipLaunchKernelGGL((fwd_sg_kernel<IO, DS, K, CW, 0, MAMBA>), dim3(blocks), dim3(NT), 0, s, p);
   else if (p.hck != nullptr)
-    hipLaunchKernelGGL((fwd_sg_kernel<IO, DS, K, 2, MAMBA>), dim3(blocks), dim3(64 * NW), 0, s, p);
+    hipLaunchKernelGGL((fwd_sg_kernel<IO, DS, K, CW, 2, MAMBA>), dim3(blocks), dim3(NT), 0, s, p);
   else
-    hipLaunchKernelGGL((fwd_sg_kernel<IO, DS, K, 1, MAMBA>), dim3(blocks), dim3(64 * NW), 0, s, p);
+    hipLaunchKernelGGL((fwd_sg_kernel<IO, DS, K, CW, 1, MAMBA>), dim3(blocks), dim3(NT), 0, s, p);
   return hipGetLastError();
+}
+
+// Dispatch on DS and the channels per wave (io: 0 fp32, 1 bf16).
+template <bool MAMBA, int CW>
+hipError_t launch_fwd_sg_cw(int io, int DS, bool local_pass, const FwdParams& p, unsigned blocks, hipStream_t s) {
+  switch (DS) {
+    case 4:
+      return io == 0 ? launch_fwd_sg_t<float, 4, kSgK, CW, MAMBA>(local_pass, p, blocks, s)
+                     : launch_fwd_sg_t<bf16_t, 4, kSgK, CW, MAMBA>(local_pass, p, blocks, s);
+    case 8:
+      return io == 0 ? launch_fwd_sg_t<float, 8, kSgK, CW, MAMBA>(local_pass, p, blocks, s)
+                     : launch_fwd_sg_t<bf16_t, 8, kSgK, CW, MAMBA>(local_pass, p, blocks, s);
+    case 16:
+      return io == 0 ? launch_fwd_sg_t<float, 16, kSgK, CW, MAMBA>(local_pass, p, blocks, s)
+                     : launch_fwd_sg_t<bf16_t, 16, kSgK, CW, MAMBA>(local_pass, p, blocks, s);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+template <bool MAMBA>
+hipError_t launch_fwd_sg_io(int io, int DS, int cw, bool local_pass, const FwdParams& p, unsigned blocks,
+                            hipStream_t s) {
+  switch (cw) {
+    case 64: return launch_fwd_sg_cw<MAMBA, 64>(io, DS, local_pass, p, blocks, s);
+    case 32: return launch_fwd_sg_cw<MAMBA, 32>(io, DS, local_pass, p, blocks, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace

@@ -148,30 +148,40 @@ int resolve_plan(const Resolved& r, const sscan_plan* plan, PlanKind kind, int* 
   return SSCAN_OK;
 }
 
-// The forward's plan: lanes, T-chunks and whether the state-group layout runs.  That
-// layout needs DS in {4, 8, 16}, D a multiple of 4 and no H (with_H).  Chosen by itself
-// where it measured faster: when there are at least 256 of its 64-channel workgroups per
-// pass (16x4096x1024x16 bf16: 0.334 ms with the packing against 0.347 ms); with fewer
-// its 512-thread workgroups cover too few CUs (4x2048x2048x16 bf16: 0.146 ms against
-// 0.125 ms), and split sequences gain nothing (8x1024x256x16 fp32: 0.049 against 0.039 ms).
-int resolve_fwd_plan(const Resolved& r, const sscan_plan* plan, bool with_H, int* lanes, int* chunks, bool* sg) {
-  const bool sg_ok = !with_H && (r.DS == 4 || r.DS == 8 || r.DS == 16) && r.D % 4 == 0;
+// The forward's plan: lanes, T-chunks, whether the state-group layout runs and its
+// channels per workgroup (cw).  That layout needs DS in {4, 8, 16}, D a multiple of 4,
+// T < 2^24 and no H (with_H).  Chosen by itself for a single pass with at least 256
+// 64-channel or 128 32-channel workgroups (16x4096x1024x16 bf16: 0.321 ms against 0.333 ms
+// for lanes, warm inputs); split sequences gain nothing (8x1024x256x16 fp32: 0.034 ms
+// against 0.031 ms).
+int resolve_fwd_plan(const Resolved& r, const sscan_plan* plan, bool with_H, bool with_ck, int* lanes, int* chunks,
+                     bool* sg, int* cw) {
+  const bool sg_ok = !with_H && (r.DS == 4 || r.DS == 8 || r.DS == 16) && r.D % 4 == 0 && r.T < (1 << 24);
   const int sg_lanes = (int)(r.DS / sscan::kSgK);
   const int want = plan != nullptr ? plan->layout : SSCAN_LAYOUT_AUTO;
   if (want == SSCAN_LAYOUT_STATE_GROUPS) {
     if (!sg_ok)
-      return fail(SSCAN_ERR_UNSUPPORTED, "the state-group layout needs DS in {4, 8, 16}, D a multiple of 4 and no H");
+      return fail(SSCAN_ERR_UNSUPPORTED, "the state-group layout needs DS in {4, 8, 16}, D a multiple of 4, "
+                                         "T < 2^24 and no H");
     if (plan->lanes != 0 && plan->lanes != sg_lanes)
       return fail(SSCAN_ERR_UNSUPPORTED, "the state-group layout runs DS/2 = %d threads per channel, not %d", sg_lanes,
                   plan->lanes);
   }
   int st = resolve_plan(r, plan, kPlanFwd, lanes, chunks);
   if (st != SSCAN_OK) return st;
+  // channels per workgroup: 64 when that gives at least 256 workgroups per pass, else 32
+  // (whose four-wave workgroups measured better from 128 workgroups up: 4x2048x2048x16
+  // bf16 0.115 ms against 0.125 ms for lanes and 0.150 ms with 64 channels; 8x2048x768x16
+  // fp32 0.113 against 0.120 and 0.149 ms)
+  const int64_t wgs64 = r.B * ceil_div(r.D, 64) * *chunks, wgs32 = r.B * ceil_div(r.D, 32) * *chunks;
+  *cw = wgs64 >= 256 ? 64 : 32;
   *sg = false;
   if (want == SSCAN_LAYOUT_STATE_GROUPS) {
     *sg = true;
-  } else if (want == SSCAN_LAYOUT_AUTO && sg_ok && *lanes == sg_lanes) {
-    *sg = *chunks == 1 && r.B * ceil_div(r.D, 64) >= 256;
+  } else if (want == SSCAN_LAYOUT_AUTO && sg_ok && !with_ck && *lanes == sg_lanes) {
+    // (its boundary-state stores, 2K floats per lane 16 floats apart, do not coalesce:
+    // the H-free forward runs the lanes layout)
+    *sg = *chunks == 1 && (wgs64 >= 256 || wgs32 >= 128);
   }
   if (*sg) *lanes = sg_lanes;
   return SSCAN_OK;
@@ -279,7 +289,8 @@ int fwd_impl(bool mamba, const sscan_desc* desc, const sscan_plan* plan, const v
   if (st != SSCAN_OK) return st;
   int lanes, chunks;
   bool sg;
-  st = resolve_fwd_plan(r, plan, H != nullptr, &lanes, &chunks, &sg);
+  int cw;
+  st = resolve_fwd_plan(r, plan, H != nullptr, hck != nullptr, &lanes, &chunks, &sg, &cw);
   if (st != SSCAN_OK) return st;
   if (r.B == 0 || r.D == 0) return ok();
   const bool steps = r.T > 0;
@@ -323,7 +334,7 @@ int fwd_impl(bool mamba, const sscan_desc* desc, const sscan_plan* plan, const v
     p.chunks = (int32_t)ceil_div(r.T, p.chunk_len);
     chunks = p.chunks;
   }
-  const int64_t cpw = sg ? 64 : kThreads / lanes;
+  const int64_t cpw = sg ? cw : kThreads / lanes;
   const int64_t ntiles_d = ceil_div(r.D, cpw);
   p.ntiles_d = (int32_t)ntiles_d;
   p.xcd_group = sg ? 1 : xcd_group(lanes, r.io_size);
@@ -338,7 +349,7 @@ int fwd_impl(bool mamba, const sscan_desc* desc, const sscan_plan* plan, const v
     if (e != hipSuccess) return hip_fail(e, "b/c packing");
   }
   auto pass = [&](bool local, unsigned blocks) {
-    return sg ? sscan::launch_fwd_sg(r.io, (int)r.DS, local, mamba, p, blocks, stream)
+    return sg ? sscan::launch_fwd_sg(r.io, (int)r.DS, cw, local, mamba, p, blocks, stream)
               : sscan::launch_fwd(r.io, (int)r.DS, lanes, local, mamba, p, blocks, stream);
   };
   if (chunks > 1) {
@@ -489,8 +500,9 @@ int sscan_plan_select(const sscan_desc* desc, int backward, sscan_plan* plan) {
   if (plan == nullptr) return fail(SSCAN_ERR_NULL, "plan is NULL");
   int lanes, chunks;
   bool sg = false;
+  int cw;
   if (backward == 0)
-    st = resolve_fwd_plan(r, nullptr, false, &lanes, &chunks, &sg);
+    st = resolve_fwd_plan(r, nullptr, false, false, &lanes, &chunks, &sg, &cw);
   else
     st = resolve_plan(r, nullptr, backward == 2 ? kPlanMambaBwd : kPlanBwd, &lanes, &chunks);
   if (st != SSCAN_OK) return st;
@@ -508,7 +520,8 @@ int sscan_fwd_workspace(const sscan_desc* desc, const sscan_plan* plan, size_t* 
   if (bytes == nullptr) return fail(SSCAN_ERR_NULL, "bytes is NULL");
   int lanes, chunks;
   bool sg;
-  st = resolve_fwd_plan(r, plan, false, &lanes, &chunks, &sg);  // a call without H needs the most
+  int cw;
+  st = resolve_fwd_plan(r, plan, false, false, &lanes, &chunks, &sg, &cw);  // a call without H needs the most
   if (st != SSCAN_OK) return st;
   *bytes = (r.B == 0 || r.D == 0 || r.T == 0) ? 0 : fwd_layout(r, chunks, sg).total;
   return ok();

@@ -134,13 +134,15 @@ hipError_t launch_fwd_mamba(int io, int DS, int lanes, bool local_pass, const Fw
                             hipStream_t s);
 hipError_t launch_carry(const CarryParams& p, hipStream_t s);
 // State-group forward (no H; DS in {4, 8, 16}, D a multiple of 4): the packing of b and c
-// into p.bcp, which must precede the passes, and a pass (local or full) over 64-channel
-// workgroups of DS/kSgK waves.
+// into p.bcp, which must precede the passes, and a pass (local or full) over workgroups of
+// cw channels (64 or 32) and DS/kSgK state groups.
 hipError_t launch_bc_pack(int io, int DS, const FwdParams& p, hipStream_t s);
-hipError_t launch_fwd_sg(int io, int DS, bool local_pass, bool mamba, const FwdParams& p, unsigned blocks,
+hipError_t launch_fwd_sg(int io, int DS, int cw, bool local_pass, bool mamba, const FwdParams& p, unsigned blocks,
                          hipStream_t s);
-hipError_t launch_fwd_sg_plain(int io, int DS, bool local_pass, const FwdParams& p, unsigned blocks, hipStream_t s);
-hipError_t launch_fwd_sg_mamba(int io, int DS, bool local_pass, const FwdParams& p, unsigned blocks, hipStream_t s);
+hipError_t launch_fwd_sg_plain(int io, int DS, int cw, bool local_pass, const FwdParams& p, unsigned blocks,
+                               hipStream_t s);
+hipError_t launch_fwd_sg_mamba(int io, int DS, int cw, bool local_pass, const FwdParams& p, unsigned blocks,
+                               hipStream_t s);
 hipError_t launch_bwd(int io, int DS, int lanes, bool local_pass, bool mamba, const BwdParams& p, unsigned blocks,
                       hipStream_t s);
 hipError_t launch_bwd_plain(int io, int DS, int lanes, bool local_pass, const BwdParams& p, unsigned blocks,

@@ -134,11 +134,11 @@ def test_layout_validation_and_choice(lib):
     p.lanes = 0
     assert fwd(lib, desc(DS=16), plan=p) == E_WS               # valid plan; b/c packing needs workspace
     assert bwd(lib, desc(DS=16), plan=p) == E_UNSUP           # the backward runs the lanes layout only
-    # the library's choice: state groups where a single pass has 256 or more 64-channel
-    # workgroups, lanes otherwise
+    # the library's choice: state groups for a single pass with 256 or more 64-channel or 128
+    # or more 32-channel workgroups, lanes otherwise (a call with H always runs lanes)
     for (B, T, D, DS), (layout, lanes, chunks) in {(16, 4096, 1024, 16): (SG, 8, 1), (8, 1024, 256, 16): (LANES, 8, 8),
-                                                   (4, 2048, 2048, 16): (LANES, 8, 1),
-                                                   (8, 2048, 768, 16): (LANES, 8, 1)}.items():
+                                                   (4, 2048, 2048, 16): (SG, 8, 1), (8, 2048, 768, 16): (SG, 8, 1),
+                                                   (2, 4096, 1024, 16): (LANES, 8, 8)}.items():
         d = desc(B=B, T=T, D=D, DS=DS)
         q = sscan_plan()
         assert lib.sscan_plan_select(ctypes.byref(d), 0, ctypes.byref(q)) == OK

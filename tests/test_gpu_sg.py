@@ -1,5 +1,6 @@
 """GPU parity of the state-group forward layout (Plan(layout="state_groups"): one channel
-per lane, a channel's states across the waves of its workgroup) against the fp64 oracle on
+per lane, a channel's states across the waves of its workgroup, 64 or 32 channels per
+workgroup by the workgroup count) against the fp64 oracle on
 the same seeded inputs, and against the lanes layout: its states come from the same
 operations in the same order, so hT and the boundary states of the H-free path agree bit
 for bit on a single pass; y differs only in the order of the sum over states.
@@ -28,6 +29,7 @@ CASES = [
     (1, 513, 40, 16, "bf16", True, 3),
     (1, 1, 4, 4, "f32", True, 1),
     (2, 64, 128, 16, "f32", True, 1),     # exactly one tile
+    (2, 1024, 512, 16, "f32", True, 16),  # 256 workgroups: 64 channels per workgroup (32 otherwise)
 ]
 
 
