@@ -47,6 +47,7 @@ def alu_peak_states_per_s() -> float:
 
 
 PROFILE = os.path.join(ROOT, "profiles", "fwd_bwd_f32_B8_T2048_D768_DS16.md")
+NSETS = 3  # input copies the step-type lines take in turn
 KERNEL_SOURCES = ("fwd_kernel.h", "fwd.hip", "bwd_kernel.h", "bwd.hip", "device_common.h", "sscan_internal.h",
                   "sscan_api.cpp")
 
@@ -135,7 +136,9 @@ def main() -> int:
     B, T, D, DS = w.B, w.T, w.D, w.DS
     print(f"bench: {w.name} {w.note} on {torch.cuda.get_device_name(dev)}", file=sys.stderr, flush=True)
     inp = workloads.make_inputs(w)
-    g = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
+    # Consecutive steps take different batches (NSETS copies of the inputs in turn), so no
+    # step finds its inputs in the 256 MB last-level cache where the step before left them.
+    sets = [{k: (None if v is None else v.to(dev)) for k, v in inp.items()} for _ in range(NSETS)]
     f32 = dict(dtype=torch.float32, device=dev)
     y = torch.empty((B, T, D), **f32)
     hT = torch.empty((B, D, DS), **f32)
@@ -147,15 +150,17 @@ def main() -> int:
     plan_f = sscan_plan_select(B, T, D, DS)
     plan_b = sscan_plan_select(B, T, D, DS, backward=True)
 
-    def fwd():
+    def fwd(k):
+        g = sets[k % NSETS]
         sscan_fwd(g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"], y=y, hT=hT, H=H, workspace=ws_f)
 
-    def bwd():
+    def bwd(k):
+        g = sets[k % NSETS]
         sscan_bwd(g["dy"], g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"], H, None, workspace=ws_b, out=outs)
 
-    for _ in range(args.warmup):
-        fwd()
-        bwd()
+    for k in range(args.warmup):
+        fwd(k)
+        bwd(k)
     torch.cuda.synchronize()
 
     K = args.steps
@@ -165,9 +170,9 @@ def main() -> int:
     t0 = time.perf_counter()
     for k in range(K):
         ev[k][0].record(stream)
-        fwd()
+        fwd(k)
         ev[k][1].record(stream)
-        bwd()
+        bwd(k)
         ev[k][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -204,8 +209,8 @@ def main() -> int:
     }
     print(f"bench: step {step_ms:.4f} ms (fwd {f_avg:.4f}, bwd {b_avg:.4f})", file=sys.stderr, flush=True)
 
-    mamba = None if args.no_fwd_only else bench_mamba(g, y, hT, H, outs, B, T, D, args.warmup, max(10, K // 2))
-    hfree = None if args.no_fwd_only else bench_hfree(g, y, hT, outs, B, T, D, DS, args.warmup, max(10, K // 2))
+    mamba = None if args.no_fwd_only else bench_mamba(sets, y, hT, H, outs, B, T, D, args.warmup, max(10, K // 2))
+    hfree = None if args.no_fwd_only else bench_hfree(sets, y, hT, outs, B, T, D, DS, args.warmup, max(10, K // 2))
     fwd_only = None if args.no_fwd_only else bench_fwd_only(dev, args.warmup, max(5, K // 5))
     decode = None if args.no_fwd_only else bench_decode(dev, args.warmup, max(5, K // 5))
 
@@ -228,33 +233,35 @@ def main() -> int:
     return 0
 
 
-def bench_hfree(g, y, hT, outs, B, T, D, DS, warmup, reps):
+def bench_hfree(sets, y, hT, outs, B, T, D, DS, warmup, reps):
     """The H-free path on the same workload: the forward keeps the state entering every
     32-step block instead of H, the backward recomputes each tile's states from them."""
     import torch
 
     from selective_state_space_sscan_amd import sscan_bwd_ckpt, sscan_fwd_ckpt
 
-    dev = g["x"].device
+    dev = sets[0]["x"].device
     hck = torch.empty((B, (T + 31) // 32, D, DS), dtype=torch.float32, device=dev)
 
-    def fwd():
+    def fwd(k):
+        g = sets[k % NSETS]
         sscan_fwd_ckpt(g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"], y=y, hT=hT, hck=hck)
 
-    def bwd():
+    def bwd(k):
+        g = sets[k % NSETS]
         sscan_bwd_ckpt(g["dy"], g["x"], g["delta"], g["A"], g["b"], g["c"], hck, None, out=outs)
 
-    for _ in range(warmup):
-        fwd()
-        bwd()
+    for k in range(warmup):
+        fwd(k)
+        bwd(k)
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     f_ms = b_ms = 0.0
-    for _ in range(reps):
+    for k in range(reps):
         ev[0].record()
-        fwd()
+        fwd(k)
         ev[1].record()
-        bwd()
+        bwd(k)
         ev[2].record()
         torch.cuda.synchronize()
         f_ms += ev[0].elapsed_time(ev[1])
@@ -269,36 +276,38 @@ def bench_hfree(g, y, hT, outs, B, T, D, DS, warmup, reps):
             "state_bytes": hck.numel() * 4, "H_bytes": B * T * D * DS * 4}
 
 
-def bench_mamba(g, y, hT, H, outs, B, T, D, warmup, reps):
+def bench_mamba(sets, y, hT, H, outs, B, T, D, warmup, reps):
     """The Mamba-style wrapper (softplus step, A = -exp(A_log), skip term fused into the
     scan kernels) on the same workload and buffers: forward with H and backward."""
     import torch
 
     from selective_state_space_sscan_amd import sscan_mamba_bwd, sscan_mamba_bwd_workspace, sscan_mamba_fwd
 
-    dev = g["x"].device
+    dev = sets[0]["x"].device
     ws_b = torch.empty(max(1, sscan_mamba_bwd_workspace(B, T, D, H.shape[-1])), dtype=torch.uint8, device=dev)
     gD = torch.empty((D,), dtype=torch.float32, device=dev)
     mouts = tuple(outs) + (gD,)
 
-    def fwd():
+    def fwd(k):
+        g = sets[k % NSETS]
         sscan_mamba_fwd(g["x"], g["delta_raw"], g["A_log"], g["b"], g["c"], g["Dskip"], g["h0"], y=y, hT=hT, H=H)
 
-    def bwd():
+    def bwd(k):
+        g = sets[k % NSETS]
         sscan_mamba_bwd(g["dy"], g["x"], g["delta_raw"], g["A_log"], g["b"], g["c"], g["Dskip"], g["h0"], H, None,
                         workspace=ws_b, out=mouts)
 
-    for _ in range(warmup):
-        fwd()
-        bwd()
+    for k in range(warmup):
+        fwd(k)
+        bwd(k)
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     f_ms = b_ms = 0.0
-    for _ in range(reps):
+    for k in range(reps):
         ev[0].record()
-        fwd()
+        fwd(k)
         ev[1].record()
-        bwd()
+        bwd(k)
         ev[2].record()
         torch.cuda.synchronize()
         f_ms += ev[0].elapsed_time(ev[1])

@@ -343,7 +343,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
       const uint32_t b = static_cast<uint32_t>(pos % (WROW * 4));
       const int tp = tf - 1 + r;
       const uint32_t off = (tp >= 0 && b < wbytes) ? static_cast<uint32_t>(tp - h_lo) * hstep + whoff + b : kOutOfRange;
-      buf_load_vec<DB / 4>(rH, off, dst[q]);
+      buf_load_vec<DB / 4, kNonTemporal>(rH, off, dst[q]);
     }
   };
   auto park_hblock = [&](const float (&src)[NQ][DB / 4]) {

@@ -179,7 +179,7 @@ int resolve_fwd_plan(const Resolved& r, const sscan_plan* plan, bool with_H, boo
   if (want == SSCAN_LAYOUT_STATE_GROUPS) {
     *sg = true;
   } else if (want == SSCAN_LAYOUT_AUTO && sg_ok && !with_ck && *lanes == sg_lanes) {
-    // (its boundary-state stores, 2K floats per lane 16 floats apart, do not coalesce:
+    // (its boundary-state stores, two floats per lane with lanes 16 floats apart, do not coalesce:
     // the H-free forward runs the lanes layout)
     *sg = *chunks == 1 && (wgs64 >= 256 || wgs32 >= 128);
   }
