@@ -4,15 +4,21 @@
 One step = one pass of the whole hot path over one batch: the forward with the
 per-step states H materialised, then the backward reverse sweep returning all six
 gradients, on the fp32 workload B=8, T=2048, D=768, DS=16 (synthetic seeded
-inputs, resident in HBM before timing starts).  ``value`` is B*T*D elements per
-second of that step.  The JSON line also carries:
+inputs, resident in HBM before timing starts; consecutive steps take three
+copies of the inputs in turn, so no step starts with its inputs in the last-level
+cache).  ``value`` is B*T*D elements per second of that step.  The JSON line
+also carries:
 
-* ``roofline`` for the kernel pair that dominates the step, timed live with HIP
-  events on the stream the library launches on (torch's current stream);
+* ``roofline`` for the entry point that dominates the step, timed live with HIP
+  events on the stream the library launches on (torch's current stream), and the
+  HBM traffic per launch from the committed rocprofv3 counter summary;
 * ``cpu_baseline``: the fp64 CPU oracle timed on this host on the same workload;
+* ``mamba`` and ``hfree``: the same step through the Mamba-style wrapper, and
+  with boundary states every 32 steps in place of H;
 * ``fwd_only``: forward-only throughput on the three forward workloads
   (fp32 8x1024x256x16; bf16 16x4096x1024x16; bf16 4x16384x2048x16 as 8 calls
-  carrying hT -> h0), each with its ALU roofline fraction.
+  carrying hT -> h0), each with its ALU roofline fraction;
+* ``decode``: one-token steps at 16x1024x16, replayed from a HIP graph.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-fwd-only]
 """
