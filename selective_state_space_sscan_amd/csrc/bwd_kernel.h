@@ -311,9 +311,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
   // boundary state of the next tile to sweep, loaded one tile ahead
   float hck_next[K];
   const float* ckrow = HF ? p.hck + (int64_t)bb * p.nck * D * DS : nullptr;
+  // (tiles are one boundary block long: the resource covers just the tile's block, so
+  // offsets stay 32-bit at any T)
   auto load_ckpt = [&](int ts, bool valid) {
-    const rsrc_t rK = make_rsrc(ckrow, valid ? static_cast<uint32_t>(p.nck) * D * DS * 4u : 0u);
-    const uint32_t off = dvalid ? static_cast<uint32_t>(((ts / kCkptSteps) * D + d) * DS + j * K) * 4u : kOutOfRange;
+    const rsrc_t rK = make_rsrc(HF ? ckrow + (int64_t)(max(ts, 0) / kCkptSteps) * D * DS : nullptr,
+                                valid ? static_cast<uint32_t>(D * DS) * 4u : 0u);
+    const uint32_t off = dvalid ? static_cast<uint32_t>(d * DS + j * K) * 4u : kOutOfRange;
     buf_load_vec<K>(rK, off, hck_next);
   };
   const int wd0 = d0 + wave * (64 / L);                         // first channel of this wave

@@ -93,8 +93,10 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(const FwdParams p) {
 
   const int64_t nstate = (int64_t)p.B * D * DS;
   const int64_t soff = ((int64_t)bb * D + d) * DS + j * K;  // this lane's states in (B,D,DS)
-  const rsrc_t rCk = make_rsrc(MODE == kFullCk ? p.hck + (int64_t)bb * p.nck * D * DS : nullptr,
-                               MODE == kFullCk ? static_cast<uint32_t>((int64_t)p.nck * D * DS * 4) : 0u);
+  // boundary states of this batch row; each tile addresses the (at most kCkBlocks) blocks it
+  // touches through a resource based at its first block, so offsets stay 32-bit at any T
+  const float* ckrow = MODE == kFullCk ? p.hck + (int64_t)bb * p.nck * D * DS : nullptr;
+  constexpr int kCkBlocks = (TB + kCkptSteps - 1) / kCkptSteps;
 
   float A2[K], h[K];
   if (dvalid) {
@@ -200,6 +202,9 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(const FwdParams p) {
     load_tile(ts + TB);
 
     const rsrc_t rH = make_rsrc(Hrow + (int64_t)ts * D * DS, static_cast<uint32_t>(rows) * hstep);
+    const int kb0 = ts / kCkptSteps;  // first boundary block of the tile
+    const rsrc_t rCk = make_rsrc(MODE == kFullCk ? ckrow + (int64_t)kb0 * D * DS : nullptr,
+                                 MODE == kFullCk ? static_cast<uint32_t>(min(p.nck - kb0, kCkBlocks) * D * DS) * 4u : 0u);
 #pragma unroll
     for (int s0 = 0; s0 < TB; s0 += S) {
       if constexpr (MODE == kFullCk) {
@@ -210,7 +215,7 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(const FwdParams p) {
         // batches are padding), so the wait counts stay the same on every path.
         if (s0 % (TB < kCkptSteps ? TB : kCkptSteps) == 0) {  // a constant once the loop is unrolled
           const bool ok = dvalid && ts + s0 < t_end && (ts + s0) % kCkptSteps == 0;
-          buf_store_vec<K>(rCk, ok ? static_cast<uint32_t>((((ts + s0) / kCkptSteps) * D + d) * DS + j * K) * 4u
+          buf_store_vec<K>(rCk, ok ? static_cast<uint32_t>((((ts + s0) / kCkptSteps - kb0) * D + d) * DS + j * K) * 4u
                                    : kOutOfRange, h);
         }
       }

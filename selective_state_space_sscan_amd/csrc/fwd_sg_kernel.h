@@ -162,8 +162,9 @@ __global__ __launch_bounds__(64 * (DS / K) / (64 / CW)) void fwd_sg_kernel(const
 
   const int64_t nstate = (int64_t)p.B * D * DS;
   const int64_t soff = ((int64_t)bb * D + d) * DS + grp * K;  // this lane's states in (B,D,DS)
-  const rsrc_t rCk = make_rsrc(MODE == 2 ? p.hck + (int64_t)bb * p.nck * D * DS : nullptr,
-                               MODE == 2 ? static_cast<uint32_t>((int64_t)p.nck * D * DS * 4) : 0u);
+  // boundary states of this batch row, addressed per tile from the tile's first block
+  const float* ckrow = MODE == 2 ? p.hck + (int64_t)bb * p.nck * D * DS : nullptr;
+  constexpr int kCkBlocks = TB / kCkptSteps;
 
   float A2[K], h[K];
   if (dvalid) {
@@ -243,6 +244,9 @@ __global__ __launch_bounds__(64 * (DS / K) / (64 / CW)) void fwd_sg_kernel(const
   for (int it = 0; it < ntiles; ++it) {
     const int ts = t_begin + it * TB;
     const int rows = min(TB, t_end - ts);
+    const int kb0 = ts / kCkptSteps;  // first boundary block of the tile
+    const rsrc_t rCk = make_rsrc(MODE == 2 ? ckrow + (int64_t)kb0 * D * DS : nullptr,
+                                 MODE == 2 ? static_cast<uint32_t>(min(p.nck - kb0, kCkBlocks) * D * DS) * 4u : 0u);
     __syncthreads();  // this tile's inputs are in LDS; the previous tile's partial sums are read
 #pragma unroll
     for (int k = 0; k < NB; ++k)
@@ -260,7 +264,7 @@ __global__ __launch_bounds__(64 * (DS / K) / (64 / CW)) void fwd_sg_kernel(const
         // every path
         if (s0 % kCkptSteps == 0) {  // a constant once the batch loop is unrolled
           const bool ok = dvalid && ts + s0 < t_end;
-          buf_store_vec<K>(rCk, ok ? static_cast<uint32_t>((((ts + s0) / kCkptSteps) * D + d) * DS + grp * K) * 4u
+          buf_store_vec<K>(rCk, ok ? static_cast<uint32_t>((((ts + s0) / kCkptSteps - kb0) * D + d) * DS + grp * K) * 4u
                                    : kOutOfRange, h);
         }
       }

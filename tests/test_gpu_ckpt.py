@@ -151,3 +151,44 @@ def test_ckpt_forward_writes_no_block_past_the_end(gpu, T):
     torch.cuda.synchronize()
     assert bool((buf[n:] == 12345.0).all()), "a boundary state was written past the array"
     assert torch.equal(hck[:, 0], g["h0"])  # block 0 of every row is h0 itself
+
+
+def test_ckpt_boundary_states_past_4gib(gpu):
+    """Boundary states of one batch row spanning more than 4 GiB (D*DS = 2^22 states, 258
+    blocks of 16 MiB): each tile addresses its blocks from a base of its own.  The last
+    block must equal hT of a forward over the steps before it, and the gradients of the
+    last 64 steps (dy zero elsewhere, no dhT) must equal those of the 64-step problem that
+    starts from the boundary state there (the same sweep arithmetic on the same states)."""
+    if torch.cuda.get_device_properties(gpu).total_memory < 96 * 2**30:
+        pytest.skip("needs about 70 GiB of device memory")
+    B, D, DS, T = 1, 1 << 18, 16, 8224  # 257 full blocks and the state entering the last one
+    nck = (T + CK - 1) // CK
+    assert nck * D * DS * 4 > 2**32
+    announce(f"ckpt past 4 GiB: B={B} T={T} D={D} DS={DS} bf16 io, {nck} boundary blocks")
+    gen = torch.Generator(device=gpu).manual_seed(4242)
+    bf = torch.bfloat16
+    x = torch.randn((B, T, D), generator=gen, device=gpu).to(bf)
+    delta = torch.nn.functional.softplus(torch.randn((B, T, D), generator=gen, device=gpu) - 2.0).to(bf)
+    b = torch.randn((B, T, DS), generator=gen, device=gpu).to(bf)
+    c = torch.randn((B, T, DS), generator=gen, device=gpu).to(bf)
+    A = -(torch.arange(1, DS + 1, device=gpu, dtype=torch.float32)[None, :]
+          * (0.5 + torch.rand((D, DS), generator=gen, device=gpu)))
+    y, hT, hck = sscan_fwd_ckpt(x, delta, A, b, c, None)
+    t_cut = (nck - 1) * CK
+    _, hT_cut = sscan_fwd(x[:, :t_cut], delta[:, :t_cut], A, b[:, :t_cut], c[:, :t_cut], None)
+    torch.cuda.synchronize()
+    assert torch.equal(hck[:, nck - 1], hT_cut), "last boundary block differs from the forward's state"
+    del y, hT_cut
+    # backward: dy only on the last 64 steps
+    t0 = T - 64
+    dy = torch.zeros((B, T, D), device=gpu, dtype=bf)
+    dy[:, t0:] = torch.randn((B, 64, D), generator=gen, device=gpu).to(bf)
+    gx, gd, gb, gc, _, _ = sscan_bwd_ckpt(dy, x, delta, A, b, c, hck, None)
+    sl = slice(t0, T)
+    _, _, hck2 = sscan_fwd_ckpt(x[:, sl], delta[:, sl], A, b[:, sl], c[:, sl], hck[:, t0 // CK].contiguous())
+    gx2, gd2, gb2, gc2, _, _ = sscan_bwd_ckpt(dy[:, sl], x[:, sl], delta[:, sl], A, b[:, sl], c[:, sl], hck2, None)
+    torch.cuda.synchronize()
+    assert torch.equal(hck2[:, 1], hck[:, t0 // CK + 1])
+    for name, a, r in (("gx", gx[:, sl], gx2), ("gdelta", gd[:, sl], gd2), ("gb", gb[:, sl], gb2),
+                       ("gc", gc[:, sl], gc2)):
+        assert torch.equal(a, r), f"{name} of the last 64 steps differs"
