@@ -1,6 +1,7 @@
 """GPU parity over seeded random problem shapes and launch plans: the forward (with and
 without H, either layout where it applies) and the backward (any lane count and T-chunk
-count), and the H-free pair where DS >= 8, against the fp64 oracle.  The shapes are small
+count), and the H-free pair where DS >= 8, against the fp64 oracle; then the same for the
+Mamba-style wrapper against its oracle.  The shapes are small
 (the oracle finishes in well under a second each) but cover ragged T and D, single steps
 and channels, every DS and both I/O dtypes."""
 import numpy as np
@@ -14,14 +15,14 @@ pytestmark = pytest.mark.gpu
 
 sscan = pytest.importorskip("selective_state_space_sscan_amd")
 from selective_state_space_sscan_amd import (Plan, sscan_bwd, sscan_bwd_ckpt, sscan_fwd,  # noqa: E402
-                                             sscan_fwd_ckpt)
+                                             sscan_fwd_ckpt, sscan_mamba_bwd, sscan_mamba_fwd)
 
 GR = ["gx", "gdelta", "gb", "gc", "gA", "gh0"]
 N_CASES = 48
 N_SG = 12  # the last N_SG cases draw only shapes the state-group layout takes, and use it
 
 
-def draw_case(i):
+def draw_case(i, force_sg=None):
     rng = np.random.default_rng(5000 + i)
     B = int(rng.integers(1, 4))
     T = int(rng.choice([1, 2, 31, 32, 33, 63, 64, 65, int(rng.integers(1, 400)), int(rng.integers(400, 1200))]))
@@ -37,7 +38,7 @@ def draw_case(i):
     layout = rng.choice([None, "lanes", "state_groups", "state_groups"] if sg_ok else [None, "lanes"])
     b_lanes = int(rng.choice(lane_opts))
     b_chunks = int(rng.choice([0, 1, 2, 4]))
-    if i >= N_CASES - N_SG:
+    if force_sg if force_sg is not None else N_CASES - N_SG <= i < N_CASES:
         DS = int(rng.choice([4, 8, 16]))
         D = 4 * int(rng.integers(1, 40))
         f_lanes = int(rng.choice([0, DS // 2]))
@@ -78,4 +79,51 @@ def test_random_shape_and_plan(gpu, i):
         g2 = sscan_bwd_ckpt(g["dy"], g["x"], g["delta"], g["A"], g["b"], g["c"], hck, g["dhT"],
                             plan=Plan(hf_lanes, bplan[1]))
         for name, a, r in zip(GR, g2, ref):
+            assert_close(name + " (H-free)", a, r, TOL_F32)
+
+
+MGR = ["gx", "gdelta_raw", "gb", "gc", "gA_log", "gh0", "gDskip"]
+N_MAMBA = 16
+
+
+@pytest.mark.parametrize("i", range(N_MAMBA))
+def test_random_mamba_wrapper(gpu, i):
+    B, T, D, DS, io, h0, dhT, fplan, bplan = draw_case(100 + i, force_sg=i % 3 == 0)
+    with_D = bool(np.random.default_rng(9000 + i).random() < 0.75)
+    announce(f"random mamba #{i}: B={B} T={T} D={D} DS={DS} io={io} h0={h0} dhT={dhT} Dskip={with_D} "
+             f"fwd plan={fplan} bwd plan={bplan}")
+    w = workloads.custom(B, T, D, DS, io=io, seed=8000 + i, h0_std=0.3 if h0 else 0.0, delta_mu=-1.0,
+                         with_dy=True, with_dhT=dhT)
+    inp = workloads.make_inputs(w)
+    g = to_dev(inp, gpu)
+    Dk = g["Dskip"] if with_D else None
+    Dr = inp["Dskip"] if with_D else None
+    yr, hTr = oracle.mamba_fwd(inp["x"], inp["delta_raw"], inp["A_log"], inp["b"], inp["c"], Dr, inp["h0"])
+    gx, gdr, gAl, gb, gc, gD, gh0 = oracle.mamba_bwd(inp["dy"], inp["x"], inp["delta_raw"], inp["A_log"], inp["b"],
+                                                     inp["c"], Dr, inp["h0"], inp["dhT"])
+    # the gradient for Dskip is formed whether or not the skip term is present
+    gD = np.sum(inp["dy"].double().numpy() * inp["x"].double().numpy(), axis=(0, 1))
+    ref = [gx, gdr, gb, gc, gAl, gh0, gD]
+
+    y, hT = sscan_mamba_fwd(g["x"], g["delta_raw"], g["A_log"], g["b"], g["c"], Dk, g["h0"], plan=Plan(*fplan))
+    assert_close("y", y, yr, tol_for(io))
+    assert_close("hT", hT, hTr, TOL_F32)
+    hplan = Plan(fplan[0] if fplan[2] != "state_groups" else 0, fplan[1])
+    _, _, H = sscan_mamba_fwd(g["x"], g["delta_raw"], g["A_log"], g["b"], g["c"], Dk, g["h0"], return_H=True,
+                              plan=hplan)
+    grads = sscan_mamba_bwd(g["dy"], g["x"], g["delta_raw"], g["A_log"], g["b"], g["c"], Dk, g["h0"], H, g["dhT"],
+                            plan=Plan(*bplan))
+    for name, a, r in zip(MGR, grads, ref):
+        if name == "gh0" and not h0:
+            continue
+        assert_close(name, a, r, TOL_F32)
+
+    if DS >= 8:
+        _, _, hck = sscan_fwd_ckpt(g["x"], g["delta_raw"], g["A_log"], g["b"], g["c"], g["h0"], mamba=True,
+                                   Dskip=Dk, plan=hplan)
+        g2 = sscan_bwd_ckpt(g["dy"], g["x"], g["delta_raw"], g["A_log"], g["b"], g["c"], hck, g["dhT"], mamba=True,
+                            Dskip=Dk, plan=Plan(bplan[0] if bplan[0] >= 8 else 0, bplan[1]))
+        for name, a, r in zip(MGR, g2, ref):
+            if name == "gh0" and not h0:
+                continue
             assert_close(name + " (H-free)", a, r, TOL_F32)
