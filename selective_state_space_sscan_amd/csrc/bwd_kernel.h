@@ -19,9 +19,11 @@
 // workgroup walks tiles of TB steps from the end of the sequence to the start; the
 // x / delta / dy tiles and the b / c rows are loaded cooperatively one tile ahead and
 // parked in LDS as fp32.  The states H_{t-1} of a wave's channels are fetched a
-// sub-block ahead with 16-byte loads per lane (a wave's channels cover consecutive
-// addresses of each step row), parked in a per-wave LDS block when their sub-block
-// starts, and read back by each lane for its own states; H_t is kept from the step
+// sub-block ahead with 16-byte non-temporal loads per lane (a wave's channels cover
+// consecutive addresses of each step row; H is read once, and kept out of the caches
+// it would otherwise flush), parked in a per-wave LDS block when their sub-block starts
+// (with four states per lane each lane's load is exactly its own states, which stay in
+// registers), and read back by each lane for its own states; H_t is kept from the step
 // before.  Sums over a channel's states
 // use DPP; sums over channels use DPP row rotations, the gfx950 row-swap permutes and
 // one LDS slot per wave, and each workgroup writes one (gb, gc) partial per (step,
