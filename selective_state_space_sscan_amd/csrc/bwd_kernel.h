@@ -138,7 +138,7 @@ __device__ __forceinline__ void reduce_scatter(float (&v)[V], int j, int& idx0) 
 // blocks are both kCkptSteps long), with the forward's own arithmetic, so the states
 // are the forward's bit for bit.  They go to a per-wave LDS block that the sweep reads.
 template <typename IO, int DS, int L, bool MAMBA, bool HF>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 16 && (L == 16 || L == 4) ? (HF ? 2 : 3) : (DS / L >= 8 ? 1 : 2)))) void bwd_kernel(const BwdParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 16 && (L == 16 || L == 4) ? 3 : (DS / L >= 8 ? 1 : 2)))) void bwd_kernel(const BwdParams p) {
   constexpr int K = DS / L;
   constexpr int CPW = kThreads / L;
   constexpr int TB = bwd_tile_steps(L);
@@ -307,9 +307,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
   constexpr int NQ = HBLK * 4 / (64 * DB);                      // loads per block
   static_assert(NQ * 64 * DB == HBLK * 4, "an H block is a whole number of loads");
   __shared__ float s_h[(HF || (K == 4 && DB == 16)) ? 1 : NWAVE * HBLK];
-  // H-free: rows 0..TB of a wave's block hold H_{ts-1} .. H_{ts+TB-1} of the current tile
-  __shared__ float s_hs[HF ? NWAVE * (TB + 1) * WROW : 1];
-  float* const hsw = s_hs + (HF ? wave * (TB + 1) * WROW : 0);
   // boundary state of the next tile to sweep, loaded one tile ahead
   float hck_next[K];
   const float* ckrow = HF ? p.hck + (int64_t)bb * p.nck * D * DS : nullptr;
@@ -390,6 +387,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
     // H-free sweep: the tile's decays, formed once by the recomputation and reused by the
     // sweep (the same values the sweep would form again)
     float at[HF ? TB : 1][K];
+    // and its states: hrec[r] = H_{ts+r-1}, r = 0..TB (each lane keeps its own)
+    float hrec[HF ? TB + 1 : 1][K];
     if constexpr (HF) {
       // recompute the tile's states from its boundary state, as the forward formed them:
       // a = exp2(delta * A log2 e), h = fma(a, h, (delta x) b); padded steps leave h as is
@@ -397,7 +396,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
 #pragma unroll
       for (int i = 0; i < K; ++i) hs[i] = hck_next[i];
       load_ckpt(ts - TB, it > 0);
-      store_state<K>(hsw + lane * K, hs);
+#pragma unroll
+      for (int i = 0; i < K; ++i) hrec[0][i] = hs[i];
 #pragma unroll
       for (int t = 0; t < TB; ++t) {
         const float4 in4 = s_in[t * CPW + ch];
@@ -408,7 +408,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
           at[t][i] = exp2_hw(in4.x * A2[i]);
           hs[i] = fmaf(at[t][i], hs[i], in4.w * bv[i]);
         }
-        store_state<K>(hsw + (t + 1) * WROW + lane * K, hs);
+#pragma unroll
+        for (int i = 0; i < K; ++i) hrec[t + 1][i] = hs[i];
       }
 #pragma unroll
       for (int i = 0; i < K; ++i) hcur[i] = hs[i];  // H_t of the tile's last step
@@ -453,7 +454,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
 #pragma unroll
         for (int s = 0; s < S; ++s) {
           if constexpr (HF) {
-            lds_load_vec<K>(&hsw[(tt0 + s) * WROW + lane * K], hrow[s]);
+#pragma unroll
+            for (int i = 0; i < K; ++i) hrow[s][i] = hrec[tt0 + s][i];
           } else if constexpr (HDIRECT) {
 #pragma unroll
             for (int i = 0; i < K; ++i) hrow[s][i] = hb[bt * S + s][i];

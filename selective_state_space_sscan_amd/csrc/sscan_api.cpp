@@ -259,10 +259,9 @@ int hip_fail(hipError_t e, const char* what) {
 // The forward, plain (mamba = false) or wrapped: delta holds delta_raw, A holds A_log and
 // Dskip (may be null) adds the skip term.
 // The H-free sweep takes one boundary block per tile: lanes with kCkptSteps-step tiles
-// (8 or 16 lanes per channel, so DS >= 8).  Its LDS holds a tile of states, which allows
-// two workgroups per CU, and it measured fastest with more T-chunks than the sweep over H
-// (8x2048x768x16: 287 us with 4 chunks, 323 us with 2): the default aims at six waves'
-// worth of lanes per SIMD.
+// (8 or 16 lanes per channel, so DS >= 8).  Each lane keeps its tile of recomputed states
+// in registers, which allows three waves per SIMD; the default T-chunk count fills them
+// once (8x2048x768x16: 223 us with 2 chunks, 236 us with 4, 237 us with 8).
 int resolve_hf_plan(const Resolved& r, const sscan_plan* plan, int* lanes, int* chunks) {
   if (r.DS < 8) return fail(SSCAN_ERR_UNSUPPORTED, "the H-free backward needs DS >= 8, got DS=%lld", (long long)r.DS);
   if (plan != nullptr && plan->lanes != 0 && plan->lanes < 8)
@@ -271,7 +270,7 @@ int resolve_hf_plan(const Resolved& r, const sscan_plan* plan, int* lanes, int* 
   if (*lanes < 8) *lanes = (int)(r.DS < 16 ? r.DS : 16);
   if (plan == nullptr || plan->chunks == 0) {
     const int64_t lanes_total = r.B * r.D * *lanes;
-    int64_t c = lanes_total > 0 ? ceil_div(6 * kLanesOneWavePerSimd, lanes_total) : 1;
+    int64_t c = lanes_total > 0 ? ceil_div(3 * kLanesOneWavePerSimd, lanes_total) : 1;
     const int64_t cap = r.T / (4 * sscan::kCkptSteps);
     if (c > cap) c = cap;
     if (c > 16) c = 16;
