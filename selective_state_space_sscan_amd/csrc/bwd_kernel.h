@@ -23,8 +23,9 @@
 // consecutive addresses of each step row; H is read once, and kept out of the caches
 // it would otherwise flush), parked in a per-wave LDS block when their sub-block starts
 // (with four states per lane each lane's load is exactly its own states, which stay in
-// registers), and read back by each lane for its own states; H_t is kept from the step
-// before.  Sums over a channel's states
+// registers; then only every other row is read, and the row between is formed from it by
+// the forward's own update, bitwise equal to the stored row), and read back by each lane
+// for its own states; H_t is kept from the step before.  Sums over a channel's states
 // use DPP; sums over channels use DPP row rotations, the gfx950 row-swap permutes and
 // one LDS slot per wave, and each workgroup writes one (gb, gc) partial per (step,
 // state) and one gA partial per (batch row, channel, state).  A second kernel adds the
@@ -327,6 +328,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
   // through the per-wave LDS block.
   constexpr bool HDIRECT = !HF && K == 4 && DB == 16;
   static_assert(!HDIRECT || NQ == HB, "one load per step row");
+  // With one step per batch, only the first row of each HB-row block is read; the rows
+  // after it are formed from it with the forward's own operations on the same inputs, so
+  // they are bitwise the rows the forward stored, for half the H traffic at HB = 2 (a
+  // deeper block needs more registers than the three-waves-per-SIMD budget leaves).
+  constexpr bool HALF = HDIRECT && S == 1;
   float hq[NQ][DB / 4];
   float hb[HDIRECT ? NQ : 1][DB / 4];
   float hzero[K];
@@ -340,6 +346,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
     const rsrc_t rH = make_rsrc(Hrow + (int64_t)h_lo * D * DS, nrow * hstep);
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
+      if (HALF && q > 0) continue;  // the later rows are formed from the first
       const int pos = q * 64 * DB + lane * DB;  // byte within the wave's block
       const int r = pos / (WROW * 4);
       const uint32_t b = static_cast<uint32_t>(pos % (WROW * 4));
@@ -424,6 +431,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
         else
           load_hblock(hq, ts - TB + (NSUB - 1) * HB, it > 0);
       }
+      float aq[HALF ? HB - 1 : 1][K];  // decays of the sub-block's steps but the last
+      if constexpr (HALF) {
+        // only the row entering the sub-block was loaded: the states after its steps are
+        // formed from it exactly as the forward formed them (same operations, same inputs)
+        const bool first = ts + sb * HB == 0;  // step 0 of the sequence: H_{-1} = h0
+#pragma unroll
+        for (int i = 0; i < K; ++i) hb[0][i] = first ? hzero[i] : hb[0][i];
+#pragma unroll
+        for (int r = 1; r < HB; ++r) {
+          const int tq = sb * HB + r - 1;
+          const float4 inq = s_in[tq * CPW + ch];
+          float bq[K];
+          lds_load_vec<K>(&s_b[tq * DS + j * K], bq);
+#pragma unroll
+          for (int i = 0; i < K; ++i) {
+            aq[r - 1][i] = exp2_hw(inq.x * A2[i]);
+            hb[r][i] = fmaf(aq[r - 1][i], hb[r - 1][i], inq.w * bq[i]);
+          }
+        }
+      }
 
 #pragma unroll
       for (int bt = NBAT - 1; bt >= 0; --bt) {
@@ -436,7 +463,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
           in[s] = s_in[(tt0 + s) * CPW + ch];
           lds_load_vec<K>(&s_c[(tt0 + s) * DS + j * K], cv[s]);
 #pragma unroll
-          for (int i = 0; i < K; ++i) a[s][i] = HF ? at[tt0 + s][i] : exp2_hw(in[s].x * A2[i]);
+          for (int i = 0; i < K; ++i)
+            a[s][i] = HF ? at[tt0 + s][i] : ((HALF && bt < HB - 1) ? aq[HALF ? bt : 0][i] : exp2_hw(in[s].x * A2[i]));
         }
         // phase B: the adjoint carry, last step first; a[s] becomes the carry a_t g_t
 #pragma unroll
