@@ -96,10 +96,10 @@ def fwd_alg_bytes(B, T, D, DS, s, with_H=False):
     return byt
 
 
-def bwd_alg_bytes(B, T, D, DS, s, h_read=0.5):
+def bwd_alg_bytes(B, T, D, DS, s, h_read=0.25):
     """Bytes the backward must move: dy, x, delta in; H in; gx, gdelta out; b, c in; gb, gc out;
     A in, gA out; h0 in, gh0 out.  h_read: the fraction of H's rows the sweep reads (with four
-    states per lane it reads every other row and forms the row between from it, bitwise)."""
+    states per lane it reads every fourth row and forms the three after it, bitwise)."""
     n = B * T * D
     return (3 * s * n + int(h_read * 4 * n * DS) + 2 * 4 * n + 2 * s * B * T * DS + 2 * 4 * B * T * DS
             + 2 * 4 * D * DS + 2 * 4 * B * D * DS)

@@ -149,7 +149,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
   constexpr int PER_BC = (BC + kThreads - 1) / kThreads;
   constexpr int NWAVE = kThreads / 64;
   constexpr int S = bwd_batch_steps<K, TB>();
-  constexpr int HB = (2 * S) < (TB / 2) ? (2 * S) : (TB / 2);  // steps of H per prefetch block
+  // steps of H per prefetch block (four with four states per lane, where only its first row
+  // is read)
+  constexpr int HB = (!HF && K == 4) ? 4 : (2 * S) < (TB / 2) ? (2 * S) : (TB / 2);
   constexpr int NSUB = TB / HB;
   constexpr int NBAT = HB / S;
   constexpr int NITEM = S * K;
@@ -330,9 +332,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
   static_assert(!HDIRECT || NQ == HB, "one load per step row");
   // With one step per batch, only the first row of each HB-row block is read; the rows
   // after it are formed from it with the forward's own operations on the same inputs, so
-  // they are bitwise the rows the forward stored, for half the H traffic at HB = 2 (a
-  // deeper block needs more registers than the three-waves-per-SIMD budget leaves).
-  constexpr bool HALF = HDIRECT && S == 1;
+  // they are bitwise the rows the forward stored: a quarter of the H traffic at HB = 4.
+  constexpr bool HFIRST = HDIRECT && S == 1;
   float hq[NQ][DB / 4];
   float hb[HDIRECT ? NQ : 1][DB / 4];
   float hzero[K];
@@ -346,7 +347,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
     const rsrc_t rH = make_rsrc(Hrow + (int64_t)h_lo * D * DS, nrow * hstep);
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-      if (HALF && q > 0) continue;  // the later rows are formed from the first
+      if (HFIRST && q > 0) continue;  // the later rows are formed from the first
       const int pos = q * 64 * DB + lane * DB;  // byte within the wave's block
       const int r = pos / (WROW * 4);
       const uint32_t b = static_cast<uint32_t>(pos % (WROW * 4));
@@ -431,8 +432,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
         else
           load_hblock(hq, ts - TB + (NSUB - 1) * HB, it > 0);
       }
-      float aq[HALF ? HB - 1 : 1][K];  // decays of the sub-block's steps but the last
-      if constexpr (HALF) {
+      float aq[HFIRST ? HB - 1 : 1][K];  // decays of the sub-block's steps but the last
+      if constexpr (HFIRST) {
         // only the row entering the sub-block was loaded: the states after its steps are
         // formed from it exactly as the forward formed them (same operations, same inputs)
         const bool first = ts + sb * HB == 0;  // step 0 of the sequence: H_{-1} = h0
@@ -464,7 +465,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
           lds_load_vec<K>(&s_c[(tt0 + s) * DS + j * K], cv[s]);
 #pragma unroll
           for (int i = 0; i < K; ++i)
-            a[s][i] = HF ? at[tt0 + s][i] : ((HALF && bt < HB - 1) ? aq[HALF ? bt : 0][i] : exp2_hw(in[s].x * A2[i]));
+            a[s][i] = HF ? at[tt0 + s][i] : ((HFIRST && bt < HB - 1) ? aq[HFIRST ? bt : 0][i] : exp2_hw(in[s].x * A2[i]));
         }
         // phase B: the adjoint carry, last step first; a[s] becomes the carry a_t g_t
 #pragma unroll

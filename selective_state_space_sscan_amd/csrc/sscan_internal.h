@@ -24,8 +24,11 @@ struct bf16_t {
 __host__ __device__ constexpr int fwd_tile_steps(int lanes) {
   return (4096 / (kThreads / lanes)) < 64 ? (4096 / (kThreads / lanes)) : 64;
 }
+// Steps per tile of the backward sweep: 4 KiB of staged (delta, x, dy, delta x) rows per
+// workgroup, at most 32; with four lanes per channel 8 steps, which keeps the unrolled tile
+// (four states per lane, four-row H blocks) within the registers of three waves per SIMD.
 __host__ __device__ constexpr int bwd_tile_steps(int lanes) {
-  return (1024 / (kThreads / lanes)) < 32 ? (1024 / (kThreads / lanes)) : 32;
+  return lanes == 4 ? 8 : (1024 / (kThreads / lanes)) < 32 ? (1024 / (kThreads / lanes)) : 32;
 }
 
 struct FwdParams {
