@@ -248,6 +248,30 @@ def test_backward_is_bitwise_reproducible(gpu):
     assert torch.equal(y, y2) and torch.equal(hT, hT2) and torch.equal(H, H2)
 
 
+@pytest.mark.parametrize("io,chunks", [("f32", 3), ("bf16", 1)])
+def test_four_lane_sweep_reads_every_fourth_row_of_H(gpu, io, chunks):
+    """With four states per lane the sweep reads H only at rows r = 3 (mod 4) (the state
+    entering each four-step block) and at the last step, and re-forms the rows between
+    with the forward's own update: poisoning every other row with NaN must leave the
+    gradients bitwise unchanged (and they match the oracle in the parity tests)."""
+    B, T, D, DS = 2, 203, 70, 16
+    announce(f"four-lane sweep, poisoned H rows: B={B} T={T} D={D} DS={DS} io={io} chunks={chunks}")
+    w = workloads.custom(B, T, D, DS, io=io, seed=77, h0_std=0.3, delta_mu=-1.0, with_dy=True, with_dhT=True)
+    inp = workloads.make_inputs(w)
+    g = to_dev(inp, gpu)
+    y, hT, H = run_fwd(g, return_H=True)
+    plan = Plan(4, chunks)
+    ref = sscan_bwd(g["dy"], g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"], H, g["dhT"], plan=plan)
+    Hp = H.clone()
+    rows = torch.arange(T, device=gpu)
+    unread = (rows % 4 != 3) & (rows != T - 1)
+    Hp[:, unread] = float("nan")
+    got = sscan_bwd(g["dy"], g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"], Hp, g["dhT"], plan=plan)
+    torch.cuda.synchronize()
+    for name, a, b in zip(["gx", "gdelta", "gb", "gc", "gA", "gh0"], got, ref):
+        assert torch.equal(a, b), name
+
+
 def test_autograd_function(gpu):
     announce("SelectiveScan autograd 2x40x24x8")
     w = workloads.custom(2, 40, 24, 8, seed=9, h0_std=0.2, with_dy=True, with_dhT=True)
