@@ -1,20 +1,8 @@
-// Forward entry points without the wrapper, and the small helper kernels of the forward
-// (chunk carry, fills).
+// Forward entry points without the wrapper, and the small fill kernel.
 #include "fwd_kernel.h"
 
 namespace sscan {
 namespace {
-
-__global__ __launch_bounds__(kThreads) void carry_kernel(const CarryParams p) {
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= p.n) return;
-  float h = p.h0 != nullptr ? p.h0[i] : 0.f;
-  for (int k = 0; k < p.chunks - 1; ++k) {
-    const float2 pr = p.pairs[(int64_t)k * p.n + i];
-    h = fmaf(pr.x, h, pr.y);
-    p.hin[(int64_t)k * p.n + i] = h;
-  }
-}
 
 __global__ __launch_bounds__(kThreads) void fill_kernel(float* __restrict__ dst, const float* __restrict__ src, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -33,12 +21,6 @@ hipError_t launch_fwd(int io, int DS, int lanes, bool local_pass, bool mamba, co
                       hipStream_t s) {
   return mamba ? launch_fwd_mamba(io, DS, lanes, local_pass, p, grid, s)
                : launch_fwd_plain(io, DS, lanes, local_pass, p, grid, s);
-}
-
-hipError_t launch_carry(const CarryParams& p, hipStream_t s) {
-  const int64_t blocks = (p.n + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL(carry_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
-  return hipGetLastError();
 }
 
 hipError_t launch_fill(float* dst, int64_t n, hipStream_t s) {

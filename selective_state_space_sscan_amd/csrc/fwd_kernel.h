@@ -18,8 +18,8 @@
 // Two-level scan along T (used when B*D*L lanes cannot fill the GPU).  The local pass
 // runs chunks 0..C-2 from a zero state and records, per (b, d, n), the chunk's decay
 // product exp(A * sum(delta)) (the product of its per-step decays) and its end state.
-// The carry kernel composes these pairs left to right from h0, h_in[k+1] =
-// P_k * h_in[k] + hloc_k, and the full pass reruns every chunk from its true start
+// Each workgroup of the full pass composes the pairs of the chunks before its own, left
+// to right from h0 (h <- P_k h + hloc_k), and reruns its chunk from that true start
 // state.  The decomposition is the associativity of the affine maps h -> a*h + u.
 #pragma once
 #include "device_common.h"
@@ -106,10 +106,23 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(const FwdParams p) {
     if (LOCAL || (chunk == 0 && p.h0 == nullptr)) {
 #pragma unroll
       for (int i = 0; i < K; ++i) h[i] = 0.f;
-    } else if (chunk == 0) {
-      load_state<K>(p.h0 + soff, h);
     } else {
-      load_state<K>(p.hin + (int64_t)(chunk - 1) * nstate + soff, h);
+      // h0, then left to right the (decay product, local end state) pair of every chunk
+      // before this one: h <- P h + hloc
+      if (p.h0 != nullptr) {
+        load_state<K>(p.h0 + soff, h);
+      } else {
+#pragma unroll
+        for (int i = 0; i < K; ++i) h[i] = 0.f;
+      }
+      for (int k = 0; k < chunk; ++k) {
+        const float2* pr = p.pairs + (int64_t)k * nstate + soff;
+#pragma unroll
+        for (int i = 0; i < K; ++i) {
+          const float2 m = pr[i];
+          h[i] = fmaf(m.x, h[i], m.y);
+        }
+      }
     }
   } else {
 #pragma unroll

@@ -174,10 +174,23 @@ __global__ __launch_bounds__(64 * (DS / K) / (64 / CW)) void fwd_sg_kernel(const
     if (LOCAL || (chunk == 0 && p.h0 == nullptr)) {
 #pragma unroll
       for (int i = 0; i < K; ++i) h[i] = 0.f;
-    } else if (chunk == 0) {
-      lds_load_vec<K>(p.h0 + soff, h);
     } else {
-      lds_load_vec<K>(p.hin + (int64_t)(chunk - 1) * nstate + soff, h);
+      // h0, then left to right the (decay product, local end state) pair of every chunk
+      // before this one: h <- P h + hloc
+      if (p.h0 != nullptr) {
+        lds_load_vec<K>(p.h0 + soff, h);
+      } else {
+#pragma unroll
+        for (int i = 0; i < K; ++i) h[i] = 0.f;
+      }
+      for (int k = 0; k < chunk; ++k) {
+        const float2* pr = p.pairs + (int64_t)k * nstate + soff;
+#pragma unroll
+        for (int i = 0; i < K; ++i) {
+          const float2 m = pr[i];
+          h[i] = fmaf(m.x, h[i], m.y);
+        }
+      }
     }
   } else {
 #pragma unroll

@@ -188,17 +188,16 @@ int resolve_fwd_plan(const Resolved& r, const sscan_plan* plan, bool with_H, boo
 }
 
 struct FwdLayout {
-  size_t pairs_off, hin_off, bc_off, total;
+  size_t pairs_off, bc_off, total;
   int64_t tpad;  // state-group layout: steps of packed b/c per row
 };
 
 FwdLayout fwd_layout(const Resolved& r, int chunks, bool sg) {
-  FwdLayout L{0, 0, 0, 0, 0};
+  FwdLayout L{0, 0, 0, 0};
   const size_t nstate = (size_t)(r.B * r.D * r.DS);
   if (chunks > 1) {
     L.pairs_off = 0;
-    L.hin_off = align_up(L.pairs_off + (size_t)(chunks - 1) * nstate * sizeof(float2), 256);
-    L.total = align_up(L.hin_off + (size_t)(chunks - 1) * nstate * sizeof(float), 256);
+    L.total = align_up(L.pairs_off + (size_t)(chunks - 1) * nstate * sizeof(float2), 256);
   }
   if (sg) {
     L.tpad = ceil_div(r.T, sscan::kSgTile) * sscan::kSgTile;
@@ -353,17 +352,8 @@ int fwd_impl(bool mamba, const sscan_desc* desc, const sscan_plan* plan, const v
   };
   if (chunks > 1) {
     p.pairs = reinterpret_cast<float2*>(wsb + lay.pairs_off);
-    p.hin = reinterpret_cast<const float*>(wsb + lay.hin_off);
     e = pass(true, (unsigned)(ntiles_d * r.B * (chunks - 1)));
     if (e != hipSuccess) return hip_fail(e, "forward local pass");
-    sscan::CarryParams cp{};
-    cp.pairs = p.pairs;
-    cp.h0 = h0;
-    cp.hin = reinterpret_cast<float*>(wsb + lay.hin_off);
-    cp.n = r.B * r.D * r.DS;
-    cp.chunks = chunks;
-    e = sscan::launch_carry(cp, stream);
-    if (e != hipSuccess) return hip_fail(e, "chunk carry");
   }
   e = pass(false, (unsigned)(ntiles_d * r.B * chunks));
   if (e != hipSuccess) return hip_fail(e, "forward pass");

@@ -42,7 +42,6 @@ struct FwdParams {
   float* hT;           // may be null
   float* H;            // may be null
   float2* pairs;       // two-level scan: (decay product, local end state) per chunk, (C-1,B,D,DS)
-  const float* hin;    // two-level scan: start state of chunks 1..C-1, (C-1,B,D,DS)
   const float* Dskip;  // Mamba wrapper: per-channel skip weight (D,), may be null (no skip)
   float* hck;          // H-free path: state entering every kCkptSteps-step block, (B,nck,D,DS), or null
   int32_t nck;         // ceil(T / kCkptSteps)
@@ -56,14 +55,6 @@ struct FwdParams {
   int32_t chunks;      // number of chunks C
   int32_t ntiles_d;    // channel tiles per batch row
   int32_t xcd_group;   // consecutive channel tiles kept on one XCD
-};
-
-struct CarryParams {
-  const float2* pairs;  // (C-1,B,D,DS)
-  const float* h0;      // may be null
-  float* hin;           // (C-1,B,D,DS)
-  int64_t n;            // B*D*DS
-  int32_t chunks;
 };
 
 struct BwdParams {
@@ -135,7 +126,6 @@ hipError_t launch_fwd_plain(int io, int DS, int lanes, bool local_pass, const Fw
                             hipStream_t s);
 hipError_t launch_fwd_mamba(int io, int DS, int lanes, bool local_pass, const FwdParams& p, unsigned blocks,
                             hipStream_t s);
-hipError_t launch_carry(const CarryParams& p, hipStream_t s);
 // State-group forward (no H; DS in {4, 8, 16}, D a multiple of 4): the packing of b and c
 // into p.bcp, which must precede the passes, and a pass (local or full) over workgroups of
 // cw channels (64 or 32) and DS/kSgK state groups.
