@@ -240,6 +240,29 @@ def main() -> int:
     return 0
 
 
+def time_fwd_bwd(fwd, bwd, warmup, reps):
+    """Average forward and backward times of `reps` steps run back to back, as the main
+    step is timed: events between the calls, one synchronisation after the last step (so
+    the host's launch latency is not inside the events)."""
+    import torch
+
+    for k in range(warmup):
+        fwd(k)
+        bwd(k)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    for k in range(reps):
+        ev[k][0].record()
+        fwd(k)
+        ev[k][1].record()
+        bwd(k)
+        ev[k][2].record()
+    torch.cuda.synchronize()
+    f_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / reps
+    b_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / reps
+    return f_ms, b_ms
+
+
 def bench_hfree(sets, y, hT, outs, B, T, D, DS, warmup, reps):
     """The H-free path on the same workload: the forward keeps the state entering every
     32-step block instead of H, the backward recomputes each tile's states from them."""
@@ -258,23 +281,7 @@ def bench_hfree(sets, y, hT, outs, B, T, D, DS, warmup, reps):
         g = sets[k % NSETS]
         sscan_bwd_ckpt(g["dy"], g["x"], g["delta"], g["A"], g["b"], g["c"], hck, None, out=outs)
 
-    for k in range(warmup):
-        fwd(k)
-        bwd(k)
-    torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    f_ms = b_ms = 0.0
-    for k in range(reps):
-        ev[0].record()
-        fwd(k)
-        ev[1].record()
-        bwd(k)
-        ev[2].record()
-        torch.cuda.synchronize()
-        f_ms += ev[0].elapsed_time(ev[1])
-        b_ms += ev[1].elapsed_time(ev[2])
-    f_ms /= reps
-    b_ms /= reps
+    f_ms, b_ms = time_fwd_bwd(fwd, bwd, warmup, reps)
     print(f"bench: H-free fwd {f_ms:.4f} ms, bwd {b_ms:.4f} ms", file=sys.stderr, flush=True)
     return {"workload": f"fwd+bwd B={B} T={T} D={D} DS={DS} fp32 with boundary states every 32 steps instead of H "
                         "(1/32 of its memory); the backward recomputes each tile's states",
@@ -304,23 +311,7 @@ def bench_mamba(sets, y, hT, H, outs, B, T, D, warmup, reps):
         sscan_mamba_bwd(g["dy"], g["x"], g["delta_raw"], g["A_log"], g["b"], g["c"], g["Dskip"], g["h0"], H, None,
                         workspace=ws_b, out=mouts)
 
-    for k in range(warmup):
-        fwd(k)
-        bwd(k)
-    torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    f_ms = b_ms = 0.0
-    for k in range(reps):
-        ev[0].record()
-        fwd(k)
-        ev[1].record()
-        bwd(k)
-        ev[2].record()
-        torch.cuda.synchronize()
-        f_ms += ev[0].elapsed_time(ev[1])
-        b_ms += ev[1].elapsed_time(ev[2])
-    f_ms /= reps
-    b_ms /= reps
+    f_ms, b_ms = time_fwd_bwd(fwd, bwd, warmup, reps)
     print(f"bench: mamba wrapper fwd {f_ms:.4f} ms, bwd {b_ms:.4f} ms", file=sys.stderr, flush=True)
     return {"workload": f"Mamba-style wrapper on B={B} T={T} D={D}: softplus(delta_raw), -exp(A_log), Dskip*x; "
                         "fwd writes H, bwd returns 7 gradients",

@@ -169,6 +169,20 @@ int resolve_fwd_plan(const Resolved& r, const sscan_plan* plan, bool with_H, boo
   }
   int st = resolve_plan(r, plan, kPlanFwd, lanes, chunks);
   if (st != SSCAN_OK) return st;
+  if (with_ck && (plan == nullptr || plan->chunks == 0)) {
+    // The forward keeping boundary states is bound by its per-step latency below one wave
+    // per SIMD: split the sequence to three waves per SIMD, every chunk keeping at least 128
+    // steps (8x2048x768x16 fp32: 4 chunks 0.119 ms, 1 chunk 0.139 ms; the forward without
+    // boundary states gains under 4% there and keeps the rule above)
+    const int64_t lanes_total = r.B * r.D * *lanes;
+    if (lanes_total > 0 && lanes_total < kLanesOneWavePerSimd) {
+      int64_t want = ceil_div(3 * kLanesOneWavePerSimd, lanes_total);
+      const int64_t cap = r.T / 128;
+      if (want > cap) want = cap;
+      if (want > 16) want = 16;
+      if (want > *chunks) *chunks = (int)want;
+    }
+  }
   // channels per workgroup: 64 when that gives at least 256 workgroups per pass, else 32
   // (whose four-wave workgroups measured better from 128 workgroups up: 4x2048x2048x16
   // bf16 0.115 ms against 0.125 ms for lanes and 0.150 ms with 64 channels; 8x2048x768x16
@@ -510,9 +524,16 @@ int sscan_fwd_workspace(const sscan_desc* desc, const sscan_plan* plan, size_t* 
   int lanes, chunks;
   bool sg;
   int cw;
-  st = resolve_fwd_plan(r, plan, false, false, &lanes, &chunks, &sg, &cw);  // a call without H needs the most
-  if (st != SSCAN_OK) return st;
-  *bytes = (r.B == 0 || r.D == 0 || r.T == 0) ? 0 : fwd_layout(r, chunks, sg).total;
+  // the most that a call without H needs, with boundary states (more T-chunks) or without
+  // (the state-group layout's packed b/c)
+  size_t need = 0;
+  for (int ck = 0; ck < 2; ++ck) {
+    st = resolve_fwd_plan(r, plan, false, ck != 0, &lanes, &chunks, &sg, &cw);
+    if (st != SSCAN_OK) return st;
+    const size_t t = (r.B == 0 || r.D == 0 || r.T == 0) ? 0 : fwd_layout(r, chunks, sg).total;
+    if (t > need) need = t;
+  }
+  *bytes = need;
   return ok();
 }
 
