@@ -150,6 +150,25 @@ def test_layout_validation_and_choice(lib):
     assert n.value >= 16 * 4032 * 2 * 16 * 4
 
 
+def test_forward_workspace_covers_the_hfree_split(lib):
+    # 8x2048x768x16: the forward without H runs one pass in the state-group layout (packed
+    # b/c, 2 MB) while the forward keeping boundary states splits into 4 T-chunks (three
+    # carry-pair blocks of B*D*DS float2, 4.7 MB); one query serves both calls
+    d = desc(B=8, T=2048, D=768, DS=16)
+    n = ctypes.c_size_t()
+    assert lib.sscan_fwd_workspace(ctypes.byref(d), None, ctypes.byref(n)) == OK
+    assert n.value >= 3 * 8 * 768 * 16 * 8
+    assert n.value >= 8 * 2048 * 2 * 16 * 4
+    p = sscan_plan()
+    assert lib.sscan_plan_select(ctypes.byref(d), 0, ctypes.byref(p)) == OK
+    assert (p.layout, p.chunks) == (2, 1)  # the state-group layout, one pass
+    # a chunk count the caller fixes is used as given for both calls
+    p = sscan_plan()
+    p.lanes, p.chunks = 8, 2
+    assert lib.sscan_fwd_workspace(ctypes.byref(d), ctypes.byref(p), ctypes.byref(n)) == OK
+    assert 1 * 8 * 768 * 16 * 8 <= n.value < 3 * 8 * 768 * 16 * 8
+
+
 def test_forward_workspace_required_for_chunked_plan(lib):
     p = sscan_plan()
     p.lanes, p.chunks = 4, 4
