@@ -114,6 +114,9 @@ def main() -> int:
     ap.add_argument("--no-fwd-only", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (to scale HBM byte counters)")
+    ap.add_argument("--micro", action="store_true",
+                    help="only measure the ceilings the kernels are compared against (v_exp_f32 and FMA rates, "
+                         "the forward's per-state mix in registers, HBM read and write streams) and print them")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the scan runs on a single MI355X and this build has no multi-GPU "
@@ -131,6 +134,10 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": src.numel() * 4, "bytes_written": dst.numel() * 4,
                           "launches": 3}))
+        return 0
+
+    if args.micro:
+        print(json.dumps({"micro": micro_rates()}))
         return 0
 
     import workloads
@@ -238,6 +245,57 @@ def main() -> int:
     }
     print(json.dumps(line))
     return 0
+
+
+def micro_rates():
+    """Ceilings measured by the kernels of libsscan_micro.so (built with libsscan): per-CU-clock
+    figures use 256 CUs at 2.4 GHz."""
+    import ctypes
+
+    path = os.path.join(ROOT, "selective_state_space_sscan_amd", "libsscan_micro.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with python -m selective_state_space_sscan_amd.build")
+    lib = ctypes.CDLL(path)
+    lib.sscan_micro_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.POINTER(ctypes.c_double)]
+    lib.sscan_micro_rate.restype = ctypes.c_int
+
+    def rate(which, waves, nbytes=0):
+        r = ctypes.c_double()
+        if lib.sscan_micro_rate(which, waves, nbytes, ctypes.byref(r)) != 0:
+            raise RuntimeError(f"sscan_micro_rate({which}, {waves}, {nbytes}) failed")
+        return r.value
+
+    per_cu_clk = 256 * 2.4e9
+    out = {"exp2_per_s": {w: rate(0, w) for w in (1, 2, 4, 8)},
+           "fma_per_s": {w: rate(1, w) for w in (1, 2, 4, 8)},
+           "mix_states_per_cu_clk": {f"K{k} W{w}": round(rate(which, w) / per_cu_clk, 2)
+                                     for which, k in ((2, 1), (3, 2), (4, 4)) for w in (1, 2, 3, 4, 8)},
+           "write_stream_GBps": rate(5, 1, 2 << 30) / 1e9,
+           "write_stream_nontemporal_GBps": rate(7, 1, 2 << 30) / 1e9,
+           "read_stream_GBps": rate(6, 1, 2 << 30) / 1e9}
+    # torch's own fill and copy kernels on 2 GiB, for comparison with the plain streams above
+    import torch
+
+    buf = torch.empty(1 << 29, dtype=torch.float32, device="cuda")
+    src = torch.ones_like(buf)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    buf.fill_(1.0)
+    buf.copy_(src)
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(10):
+        buf.fill_(2.0)
+    ev[1].record()
+    for _ in range(10):
+        buf.copy_(src)
+    ev[2].record()
+    torch.cuda.synchronize()
+    out["torch_fill_GBps"] = buf.numel() * 4 / (ev[0].elapsed_time(ev[1]) / 10 * 1e-3) / 1e9
+    out["torch_copy_GBps_read_plus_written"] = 2 * buf.numel() * 4 / (ev[1].elapsed_time(ev[2]) / 10 * 1e-3) / 1e9
+    del buf, src
+    for k, v in out.items():
+        print(f"micro: {k}: {v}", file=sys.stderr, flush=True)
+    return out
 
 
 def time_fwd_bwd(fwd, bwd, warmup, reps):

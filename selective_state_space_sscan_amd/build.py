@@ -20,6 +20,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsscan.so")
+# microbenchmarks of the ceilings the kernels are measured against (bench.py --micro)
+MICRO_SOURCES = ["micro.hip"]
+MICRO_LIB = os.path.join(PKG, "libsscan_micro.so")
 
 ARCH = os.environ.get("SSCAN_OFFLOAD_ARCH", "gfx950")
 SOURCES = ["sscan_api.cpp", "fwd.hip", "fwd_mamba.hip", "fwd_sg.hip", "fwd_sg_mamba.hip", "bwd.hip", "bwd_mamba.hip",
@@ -56,16 +59,23 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every translation unit and link libsscan.so next to this file."""
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + f".tmp{os.getpid()}"
+def _link(objs, lib: str) -> None:
+    tmp = lib + f".tmp{os.getpid()}"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every translation unit and link libsscan.so (and the microbenchmark
+    library libsscan_micro.so) next to this file."""
+    srcs = SOURCES + MICRO_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], MICRO_LIB)
     return LIB
 
 
