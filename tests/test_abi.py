@@ -279,3 +279,22 @@ def test_ckpt_validation(lib):
                               None, ctypes.c_size_t(0), None) == E_ALIGN
     # backward: hck required
     assert lib.sscan_bwd_ckpt(ctypes.byref(d), None, 0, *([None] * 16), None, ctypes.c_size_t(0), None) == E_NULL
+
+
+def test_micro_library_rejects_bad_arguments_before_any_gpu_call():
+    # the microbenchmark library (bench.py --micro) is built with libsscan and checks its
+    # arguments on the host: these return 1 without touching a device
+    path = os.path.join(os.path.dirname(_lib.LIB_PATH), "libsscan_micro.so")
+    if not os.path.exists(path):
+        pytest.skip("libsscan_micro.so is not built")
+    m = ctypes.CDLL(path)
+    m.sscan_micro_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.POINTER(ctypes.c_double)]
+    m.sscan_micro_rate.restype = ctypes.c_int
+    r = ctypes.c_double()
+    assert m.sscan_micro_rate(0, 1, 0, None) == 1                         # no output
+    assert m.sscan_micro_rate(8, 1, 0, ctypes.byref(r)) == 1              # unknown kernel
+    assert m.sscan_micro_rate(0, 0, 0, ctypes.byref(r)) == 1              # waves per SIMD out of 1..8
+    assert m.sscan_micro_rate(0, 9, 0, ctypes.byref(r)) == 1
+    assert m.sscan_micro_rate(5, 1, 0, ctypes.byref(r)) == 1              # stream size missing
+    assert m.sscan_micro_rate(6, 1, 1000, ctypes.byref(r)) == 1           # not a multiple of 16
+    assert m.sscan_micro_rate(7, 1, (16 << 30) + 16, ctypes.byref(r)) == 1  # above 16 GiB
