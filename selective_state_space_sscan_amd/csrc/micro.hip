@@ -82,6 +82,22 @@ __global__ __launch_bounds__(kThreads) void write_stream_nt_kernel(f4_t* dst, in
     __builtin_nontemporal_store(q, dst + i);
 }
 
+// The store pattern of the forward writing H at B x T x D x DS = 8 x 2048 x 768 x 16 with
+// nothing else: a workgroup per (batch row, 32 channels), 8 lanes per channel holding two
+// states, each lane storing its 8 bytes of every step with the non-temporal policy.
+constexpr int kHB = 8, kHT = 2048, kHD = 768, kHDS = 16;
+typedef float f2_t __attribute__((ext_vector_type(2)));
+__global__ __launch_bounds__(kThreads) void h_pattern_kernel(float* H, float v) {
+  const int b = blockIdx.x / (kHD / 32);
+  const int d = (blockIdx.x % (kHD / 32)) * 32 + threadIdx.x / 8;
+  const int j = threadIdx.x % 8;
+  const f2_t q = {v, v + 1.f};
+  for (int t = 0; t < kHT; ++t) {
+    const int64_t off = ((int64_t)(b * kHT + t) * kHD + d) * kHDS + j * 2;
+    __builtin_nontemporal_store(q, reinterpret_cast<f2_t*>(H + off));
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void read_stream_kernel(const float4* src, int64_t n, float* out) {
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -128,13 +144,14 @@ extern "C" {
 
 // which: 0 = v_exp_f32 results/s, 1 = fp32 FMA results/s, 2/3/4 = forward-mix states/s with
 // 1/2/4 states per thread, 5 = write stream bytes/s, 6 = read stream bytes/s, 7 = write
-// stream with non-temporal stores, bytes/s.
+// stream with non-temporal stores, bytes/s, 8 = the forward's H store pattern at
+// 8x2048x768x16 alone, bytes/s (bytes and waves_per_simd are ignored).
 // waves_per_simd: 1..8, the grid size of the compute kernels (256 CUs x 4 SIMDs each);
 // bytes: buffer size of the stream kernels (a multiple of 16, at most 16 GiB).
 // Allocates its own device buffers and stream.  Returns 0 and the rate in *rate, else 1.
 int sscan_micro_rate(int which, int waves_per_simd, int64_t bytes, double* rate) {
-  if (rate == nullptr || which < 0 || which > 7 || waves_per_simd < 1 || waves_per_simd > 8) return 1;
-  if (which >= 5 && (bytes <= 0 || bytes % 16 != 0 || bytes > (int64_t(16) << 30))) return 1;
+  if (rate == nullptr || which < 0 || which > 8 || waves_per_simd < 1 || waves_per_simd > 8) return 1;
+  if (which >= 5 && which <= 7 && (bytes <= 0 || bytes % 16 != 0 || bytes > (int64_t(16) << 30))) return 1;
   Timer t;
   if (!t.ok) return 1;
   const int blocks = 256 * 4 * waves_per_simd * 64 / kThreads;  // waves_per_simd waves on each SIMD
@@ -167,6 +184,17 @@ int sscan_micro_rate(int which, int waves_per_simd, int64_t bytes, double* rate)
       if (rc == 0) *rate = (double)nthreads * steps * K / (ms * 1e-3);
     }
     (void)hipFree(out);
+    return rc;
+  }
+  if (which == 8) {
+    const int64_t hbytes = (int64_t)kHB * kHT * kHD * kHDS * 4;
+    float* H = nullptr;
+    if (hipMalloc(&H, hbytes) != hipSuccess) return 1;
+    rc = time_launches(t, 5, [&](hipStream_t s) {
+      hipLaunchKernelGGL(h_pattern_kernel, dim3(kHB * (kHD / 32)), dim3(kThreads), 0, s, H, 1.f);
+    }, &ms);
+    if (rc == 0) *rate = (double)hbytes / (ms * 1e-3);
+    (void)hipFree(H);
     return rc;
   }
   const int64_t n = bytes / 16;

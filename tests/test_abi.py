@@ -292,7 +292,8 @@ def test_micro_library_rejects_bad_arguments_before_any_gpu_call():
     m.sscan_micro_rate.restype = ctypes.c_int
     r = ctypes.c_double()
     assert m.sscan_micro_rate(0, 1, 0, None) == 1                         # no output
-    assert m.sscan_micro_rate(8, 1, 0, ctypes.byref(r)) == 1              # unknown kernel
+    assert m.sscan_micro_rate(9, 1, 0, ctypes.byref(r)) == 1              # unknown kernel
+    assert m.sscan_micro_rate(-1, 1, 0, ctypes.byref(r)) == 1
     assert m.sscan_micro_rate(0, 0, 0, ctypes.byref(r)) == 1              # waves per SIMD out of 1..8
     assert m.sscan_micro_rate(0, 9, 0, ctypes.byref(r)) == 1
     assert m.sscan_micro_rate(5, 1, 0, ctypes.byref(r)) == 1              # stream size missing
