@@ -214,8 +214,20 @@ int sscan_bwd_ckpt_workspace(const sscan_desc* desc, const sscan_plan* plan, int
 int sscan_decode(const sscan_desc* desc, const void* x, const void* delta, const float* A, const void* b,
                  const void* c, const float* state_in, float* state_out, void* y, hipStream_t stream);
 
-/* The plan the library picks for desc -> *plan: backward 0 for the forward entry points,
- * 2 for sscan_mamba_bwd, any other value for sscan_bwd.  Uses no GPU. */
+/* Entry points whose plan sscan_plan_select reports (its `backward` argument). */
+typedef enum sscan_plan_kind {
+  SSCAN_PLAN_FWD = 0,       /* sscan_fwd / sscan_mamba_fwd without H */
+  SSCAN_PLAN_BWD = 1,       /* sscan_bwd */
+  SSCAN_PLAN_MAMBA_BWD = 2, /* sscan_mamba_bwd */
+  SSCAN_PLAN_FWD_H = 3,     /* sscan_fwd / sscan_mamba_fwd writing H */
+  SSCAN_PLAN_FWD_CKPT = 4   /* sscan_fwd_ckpt (the forward keeping boundary states) */
+} sscan_plan_kind;
+
+/* The plan the library picks for desc -> *plan when the caller passes none, for the entry
+ * point named by `backward` (an sscan_plan_kind; any other value means sscan_bwd).  The
+ * forward's plan depends on what it stores: only the forward without H or boundary states
+ * runs the state-group layout, and the forward keeping boundary states splits T from below
+ * one wave per SIMD.  Uses no GPU. */
 int sscan_plan_select(const sscan_desc* desc, int backward, sscan_plan* plan);
 
 /* Static text for a status code. */

@@ -124,13 +124,18 @@ def sscan_version() -> int:
 
 
 def sscan_plan_select(B: int, T: int, D: int, DS: int, io: torch.dtype = torch.float32, backward: bool = False,
-                      mamba: bool = False) -> Plan:
-    """The plan the library picks: the forward's, or with ``backward`` the backward's (with
-    ``mamba`` that of the wrapper's backward)."""
+                      mamba: bool = False, with_H: bool = False, ckpt: bool = False) -> Plan:
+    """The plan the library picks: the forward's (without H; ``with_H`` for the forward
+    writing H, ``ckpt`` for the forward keeping boundary states), or with ``backward`` the
+    backward's (with ``mamba`` that of the wrapper's backward)."""
     lib = _lib.load()
     d = _desc(B, T, D, DS, _IO[io])
     p = sscan_plan()
-    _lib.check(lib.sscan_plan_select(ctypes.byref(d), (2 if mamba else 1) if backward else 0, ctypes.byref(p)))
+    if backward:
+        kind = 2 if mamba else 1
+    else:
+        kind = 3 if with_H else (4 if ckpt else 0)
+    _lib.check(lib.sscan_plan_select(ctypes.byref(d), kind, ctypes.byref(p)))
     return Plan(p.lanes, p.chunks, "state_groups" if p.layout == 2 else "lanes")
 
 

@@ -504,10 +504,11 @@ int sscan_plan_select(const sscan_desc* desc, int backward, sscan_plan* plan) {
   int lanes, chunks;
   bool sg = false;
   int cw;
-  if (backward == 0)
-    st = resolve_fwd_plan(r, nullptr, false, false, &lanes, &chunks, &sg, &cw);
+  if (backward == SSCAN_PLAN_FWD || backward == SSCAN_PLAN_FWD_H || backward == SSCAN_PLAN_FWD_CKPT)
+    st = resolve_fwd_plan(r, nullptr, backward == SSCAN_PLAN_FWD_H, backward == SSCAN_PLAN_FWD_CKPT, &lanes, &chunks,
+                          &sg, &cw);
   else
-    st = resolve_plan(r, nullptr, backward == 2 ? kPlanMambaBwd : kPlanBwd, &lanes, &chunks);
+    st = resolve_plan(r, nullptr, backward == SSCAN_PLAN_MAMBA_BWD ? kPlanMambaBwd : kPlanBwd, &lanes, &chunks);
   if (st != SSCAN_OK) return st;
   memset(plan, 0, sizeof(*plan));
   plan->lanes = lanes;

@@ -150,6 +150,27 @@ def test_layout_validation_and_choice(lib):
     assert n.value >= 16 * 4032 * 2 * 16 * 4
 
 
+def test_plan_select_per_forward_kind(lib):
+    # 8x2048x768x16 (0.75 waves per SIMD in one pass): the forward without H runs the
+    # state-group layout in one pass, the forward writing H the lanes layout in one pass,
+    # the forward keeping boundary states the lanes layout split into 4 T-chunks
+    d = desc(B=8, T=2048, D=768, DS=16)
+    want = {0: (2, 8, 1), 3: (1, 8, 1), 4: (1, 8, 4)}
+    for kind, (layout, lanes, chunks) in want.items():
+        p = sscan_plan()
+        assert lib.sscan_plan_select(ctypes.byref(d), kind, ctypes.byref(p)) == OK
+        assert (p.layout, p.lanes, p.chunks) == (layout, lanes, chunks), kind
+    # at two waves per SIMD or more nothing is split
+    d = desc(B=16, T=4096, D=1024, DS=16)
+    p = sscan_plan()
+    assert lib.sscan_plan_select(ctypes.byref(d), 4, ctypes.byref(p)) == OK
+    assert (p.layout, p.chunks) == (1, 1)
+    # short sequences keep at least 128 steps per chunk
+    d = desc(B=1, T=300, D=64, DS=16)
+    assert lib.sscan_plan_select(ctypes.byref(d), 4, ctypes.byref(p)) == OK
+    assert p.chunks == 2
+
+
 def test_forward_workspace_covers_the_hfree_split(lib):
     # 8x2048x768x16: the forward without H runs one pass in the state-group layout (packed
     # b/c, 2 MB) while the forward keeping boundary states splits into 4 T-chunks (three
