@@ -63,12 +63,16 @@ def _stream(device: torch.device):
 
 
 def _batch_stride(t: torch.Tensor, name: str) -> int:
-    """Batch stride of a (B, R, C) tensor whose trailing (R, C) block is contiguous."""
+    """Batch stride of a (B, R, C) tensor whose trailing (R, C) block is contiguous and
+    whose batch rows do not overlap.  A tensor broadcast over the batch dimension (stride
+    0, e.g. from ``expand``) is rejected: the C ABI reads a batch stride of 0 as R*C."""
     if t.dim() != 3:
         raise ValueError(f"{name} must be 3-D, got shape {tuple(t.shape)}")
     B, R, C = t.shape
     if C > 1 and t.stride(2) != 1 or R > 1 and t.stride(1) != C:
         raise ValueError(f"{name}: the last two dimensions must be contiguous")
+    if B > 1 and t.stride(0) < R * C:
+        raise ValueError(f"{name}: batch rows overlap (batch stride {t.stride(0)} < {R * C})")
     return t.stride(0) if B > 1 else R * C
 
 
@@ -117,6 +121,17 @@ def _f32_contig(t: Optional[torch.Tensor], shape, name):
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     return t.contiguous()
+
+
+def _f32_out(t: Optional[torch.Tensor], shape, name):
+    """A caller-supplied fp32 output: must already be float32, of ``shape`` and contiguous
+    (the kernels write exactly that many fp32 values at its address)."""
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 tensor of shape {tuple(shape)}, got "
+                         f"{t.dtype} {tuple(t.shape)}{'' if t.is_contiguous() else ' (not contiguous)'}")
+    return t
 
 
 def sscan_version() -> int:
@@ -245,18 +260,17 @@ def _fwd_call(mamba, x, delta, A, b, c, Dskip, h0, y, hT, H, return_H, plan, wor
     y_bs = _batch_stride(y, "y")
     if hT is None:
         hT = torch.empty((B, D, DS), dtype=torch.float32, device=device)
-    elif not hT.is_contiguous():
-        raise ValueError("hT must be contiguous")
+    else:
+        _f32_out(hT, (B, D, DS), "hT")
     if H is None and return_H:
         H = torch.empty((B, T, D, DS), dtype=torch.float32, device=device)
-    if H is not None and (not H.is_contiguous() or tuple(H.shape) != (B, T, D, DS) or H.dtype != torch.float32):
-        raise ValueError("H must be a contiguous (B,T,D,DS) float32 tensor")
+    _f32_out(H, (B, T, D, DS), "H")
     if ckpt:
         nck = (T + _lib.SSCAN_CKPT_STEPS - 1) // _lib.SSCAN_CKPT_STEPS
         if hck is None:
             hck = torch.empty((B, nck, D, DS), dtype=torch.float32, device=device)
-        elif not hck.is_contiguous() or tuple(hck.shape) != (B, nck, D, DS) or hck.dtype != torch.float32:
-            raise ValueError(f"hck must be a contiguous {(B, nck, D, DS)} float32 tensor")
+        else:
+            _f32_out(hck, (B, nck, D, DS), "hck")
     d = _desc(B, T, D, DS, _IO[x.dtype], x_bs, bc_bs, y_bs)
     pc, pp = _plan_ptr(plan)
     nws = ctypes.c_size_t(0)

@@ -10,8 +10,8 @@ import torch
 
 import oracle
 import workloads
-from parity import (TOL_BF16, TOL_F32, announce, assert_close, f64, oracle_rows, rel_err, sample_rows, to_dev,
-                    tol_for)
+from parity import TOL_BF16, TOL_F32, announce, assert_close, f64, rel_err, to_dev, tol_for
+from test_oracle_pins import gradient_identity_residuals
 
 pytestmark = pytest.mark.gpu
 
@@ -309,9 +309,15 @@ def test_fwd_bf16_full(gpu):
     print(f"fwd_bf16 full: y rel err {e_y:.2e}")
 
 
-def test_long_chunked_bf16_sampled(gpu):
+def test_long_chunked_bf16_full(gpu):
+    """4x16384x2048x16 bf16 run as 8 calls of 2048 steps with hT -> h0: every element of y
+    and hT against ONE unchunked oracle pass over the whole sequence (pssa_kernels.py page,
+    module docstring: h0 and hT carry the state across chunks), and against the GPU's own
+    single call over all 16384 steps.  The calls hand over the fp32 state exactly, and both
+    run the same kernel with the same per-step operations, so the two GPU results must be
+    bitwise equal."""
     w = workloads.get("long_chunked_bf16")
-    announce(f"{w.name}: {w.note}; sampled rows vs one unchunked oracle pass")
+    announce(f"{w.name}: {w.note}; every element vs one unchunked oracle pass and vs one GPU call")
     inp = workloads.make_inputs(w)
     g = to_dev(inp, gpu)
     y_all = torch.empty_like(g["x"])
@@ -319,17 +325,16 @@ def test_long_chunked_bf16_sampled(gpu):
     for t0, t1 in workloads.chunk_bounds(w.T, w.chunks):
         sl = slice(t0, t1)
         _, h = sscan_fwd(g["x"][:, sl], g["delta"][:, sl], g["A"], g["b"][:, sl], g["c"][:, sl], h, y=y_all[:, sl])
+    y1, h1 = run_fwd(g)  # one call over all T = 16384 steps
     torch.cuda.synchronize()
-    rows = sample_rows(w.B, w.D, 48)
-    ref = oracle_rows(inp, rows)
-    ys = y_all.cpu()
-    hs = h.cpu()
-    got_y = np.stack([f64(ys[b, :, d]) for b, d in rows])
-    ref_y = np.stack([ref[r][0] for r in rows])
-    got_h = np.stack([f64(hs[b, d]) for b, d in rows])
-    ref_h = np.stack([ref[r][1] for r in rows])
-    assert_close("y (sampled rows)", got_y, ref_y, TOL_BF16)
-    assert_close("hT (sampled rows)", got_h, ref_h, TOL_F32)
+    assert torch.equal(y_all, y1), "8 calls and one call differ in y"
+    assert torch.equal(h, h1), "8 calls and one call differ in hT"
+    del y1, h1, g
+    yr, hTr = oracle.fwd(inp["x"], inp["delta"], inp["A"], inp["b"], inp["c"], inp["h0"])
+    e_y = assert_close("y (all 4x16384x2048)", y_all, yr, TOL_BF16)
+    del yr
+    e_h = assert_close("hT", h, hTr, TOL_F32)
+    print(f"long_chunked_bf16 full: y rel err {e_y:.2e}, hT rel err {e_h:.2e}")
 
 
 def test_fwd_bwd_f32_full(gpu):
@@ -352,3 +357,11 @@ def test_fwd_bwd_f32_full(gpu):
     Hd = f64(H)
     gc_from_H = np.einsum("btd,btdn->btn", f64(inp["dy"]), Hd)
     assert_close("gc vs sum_d dy*H", grads[3], gc_from_H, 1e-5)
+    del Hd, gc_from_H
+    # the four exact relations between the gradients that invariances of the map give (they
+    # hold at any size), evaluated on the GPU's own outputs
+    e = {k: f64(inp[k]) for k in ("x", "delta", "A", "b", "c", "h0", "dy")}
+    e["dhT"] = None
+    res = gradient_identity_residuals(e, f64(y), f64(hT), [f64(t) for t in grads])
+    print("fwd_bwd full gradient identity residuals: " + " ".join(f"{r:.1e}" for r in res))
+    assert max(res) < 1e-5, res

@@ -95,7 +95,9 @@ def test_gradients_match_finite_differences():
 
 
 def _torch_wrapper_loop(x, raw, A_log, b, c, Dskip, h0):
-    # an independent plain loop in torch fp64 (torch's own softplus with threshold 20)
+    # the pssa_kernels.py page's scan_reference loop transcribed into torch fp64, with the
+    # wrapper's maps around it (torch's own softplus with threshold 20); a pin because the
+    # pages print it, its gradients from autograd
     delta = torch.nn.functional.softplus(raw, beta=1.0, threshold=20.0)
     A = -torch.exp(A_log)
     h = h0

@@ -250,7 +250,10 @@ def test_gradients_match_finite_differences():
 
 
 def _torch_plain_loop(x, delta, b, c, A, h0):
-    # an independent plain loop in torch fp64; its gradients come from autograd
+    # the plain loop the pssa_kernels.py page prints as scan_reference, transcribed into torch
+    # fp64 (a one-line recurrence in broadcasting form has essentially this one shape); it is
+    # a pin because the page prints it, and its gradients come from autograd, not from the
+    # oracle's adjoint sweep
     T = x.shape[1]
     h = h0
     ys = []
