@@ -33,7 +33,8 @@
  *    the state are fp32; y is rounded to bf16 with round-to-nearest-even.
  *  - Memory: every pointer is device memory owned by the caller.  The library
  *    allocates nothing; scratch space is the caller's workspace, sized by the
- *    *_workspace query.  Inputs are never written.  Outputs are overwritten,
+ *    *_workspace query (sscan_fwd_noalloc instead uses a static array of the
+ *    library).  Inputs are never written.  Outputs are overwritten,
  *    never accumulated into, and must not alias any input or each other.
  *  - A, h0, hT, H, dhT, gA and gh0 must be 16-byte aligned; every other tensor
  *    must be aligned to its element size (4 bytes for fp32, 2 for bf16); the
@@ -60,6 +61,9 @@ extern "C" {
 #endif
 
 #define SSCAN_VERSION 1
+
+/* Bytes of device scratch that sscan_fwd_noalloc has on each GPU (32 MiB). */
+#define SSCAN_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 /* Steps between the boundary states kept by the H-free path (sscan_fwd_ckpt). */
 #define SSCAN_CKPT_STEPS 32
@@ -122,6 +126,22 @@ int sscan_fwd(const sscan_desc* desc, const sscan_plan* plan, const void* x, con
 
 /* Bytes of workspace sscan_fwd needs for (desc, plan) -> *bytes. */
 int sscan_fwd_workspace(const sscan_desc* desc, const sscan_plan* plan, size_t* bytes);
+
+/* sscan_fwd for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Same arguments, results and
+ * errors as sscan_fwd, without the workspace: the scratch the forward needs (the two-level
+ * scan's carry pairs, the packed b/c of the state-group layout) lives in a static device
+ * array of SSCAN_NOALLOC_SCRATCH_BYTES per GPU, which the library holds from its load
+ * until the process ends.  This call allocates nothing (no hipMalloc, no torch).
+ *   A call whose forward needs more scratch than that (at most what sscan_fwd_workspace
+ *   reports for the same desc and plan) returns SSCAN_ERR_WORKSPACE before any GPU call.
+ *   Every call on one GPU shares its array: calls that overlap in time on one GPU (two
+ *   streams, or two threads) race and give undefined results; calls in one stream order are
+ *   safe.  Nothing in the array needs to start at zero: every call writes the scratch it
+ *   reads.  The GPU is the device of `stream` (the current device for NULL). */
+int sscan_fwd_noalloc(const sscan_desc* desc, const sscan_plan* plan, const void* x, const void* delta,
+                      const float* A, const void* b, const void* c, const float* h0, void* y, float* hT, float* H,
+                      hipStream_t stream);
 
 /* Backward: gradients of L = sum(dy*y) + sum(dhT*hT) for the forward with the same inputs.
  *   dy (B,T,D) io; dhT (B,D,DS) fp32 or NULL (zeros); x, delta, A, b, c, h0 as in sscan_fwd;

@@ -9,9 +9,10 @@ package is its Python binding.  Build it with
 """
 from .api import (MambaScan, Plan, SelectiveScan, SScanError, mamba_scan, selective_scan, sscan_bwd,
                   sscan_bwd_ckpt, sscan_bwd_workspace, sscan_decode, sscan_fwd, sscan_fwd_ckpt,
-                  sscan_fwd_workspace, sscan_mamba_bwd,
+                  sscan_fwd_noalloc, sscan_fwd_workspace, sscan_mamba_bwd,
                   sscan_mamba_bwd_workspace, sscan_mamba_fwd, sscan_plan_select, sscan_version)
 
 __all__ = ["MambaScan", "Plan", "SelectiveScan", "SScanError", "mamba_scan", "selective_scan", "sscan_bwd",
-           "sscan_bwd_ckpt", "sscan_fwd_ckpt", "sscan_bwd_workspace", "sscan_decode", "sscan_fwd", "sscan_fwd_workspace", "sscan_mamba_bwd",
+           "sscan_bwd_ckpt", "sscan_fwd_ckpt", "sscan_bwd_workspace", "sscan_decode", "sscan_fwd", "sscan_fwd_noalloc",
+           "sscan_fwd_workspace", "sscan_mamba_bwd",
            "sscan_mamba_bwd_workspace", "sscan_mamba_fwd", "sscan_plan_select", "sscan_version"]

@@ -27,11 +27,12 @@ STATUS_NAMES = {
 }
 
 # Every function include/sscan.h declares.
-EXPORTED = ("sscan_fwd", "sscan_fwd_workspace", "sscan_bwd", "sscan_bwd_workspace", "sscan_mamba_fwd",
+EXPORTED = ("sscan_fwd", "sscan_fwd_workspace", "sscan_fwd_noalloc", "sscan_bwd", "sscan_bwd_workspace", "sscan_mamba_fwd",
             "sscan_mamba_bwd", "sscan_mamba_bwd_workspace", "sscan_fwd_ckpt", "sscan_bwd_ckpt",
             "sscan_bwd_ckpt_workspace", "sscan_decode", "sscan_plan_select", "sscan_status_str",
             "sscan_last_error", "sscan_version")
 SSCAN_CKPT_STEPS = 32
+SSCAN_NOALLOC_SCRATCH_BYTES = 32 << 20
 SSCAN_WRAP_NONE = 0
 SSCAN_WRAP_MAMBA = 1
 SSCAN_LAYOUT_AUTO = 0
@@ -74,6 +75,8 @@ def load() -> ctypes.CDLL:
         pdesc, pplan = ctypes.POINTER(sscan_desc), ctypes.POINTER(sscan_plan)
         lib.sscan_fwd.argtypes = [pdesc, pplan] + [vp] * 9 + [vp, sz, vp]
         lib.sscan_fwd.restype = i32
+        lib.sscan_fwd_noalloc.argtypes = [pdesc, pplan] + [vp] * 9 + [vp]
+        lib.sscan_fwd_noalloc.restype = i32
         lib.sscan_fwd_workspace.argtypes = [pdesc, pplan, ctypes.POINTER(sz)]
         lib.sscan_fwd_workspace.restype = i32
         lib.sscan_bwd.argtypes = [pdesc, pplan] + [vp] * 15 + [vp, sz, vp]

@@ -15,7 +15,7 @@ import torch
 from . import _lib
 from ._lib import SScanError, sscan_desc, sscan_plan
 
-__all__ = ["sscan_fwd", "sscan_bwd", "sscan_mamba_fwd", "sscan_mamba_bwd", "sscan_fwd_ckpt", "sscan_bwd_ckpt",
+__all__ = ["sscan_fwd", "sscan_fwd_noalloc", "sscan_bwd", "sscan_mamba_fwd", "sscan_mamba_bwd", "sscan_fwd_ckpt", "sscan_bwd_ckpt",
            "sscan_decode", "sscan_fwd_workspace",
            "sscan_bwd_workspace", "sscan_mamba_bwd_workspace", "sscan_plan_select", "sscan_version",
            "SelectiveScan", "selective_scan", "MambaScan", "mamba_scan", "SScanError", "Plan"]
@@ -208,6 +208,17 @@ def sscan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, b: torch.Te
     return _fwd_call(False, x, delta, A, b, c, None, h0, y, hT, H, return_H, plan, workspace)
 
 
+def sscan_fwd_noalloc(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, b: torch.Tensor, c: torch.Tensor,
+                      h0: Optional[torch.Tensor] = None, *, y: Optional[torch.Tensor] = None,
+                      hT: Optional[torch.Tensor] = None, H: Optional[torch.Tensor] = None, return_H: bool = False,
+                      plan: Optional[Plan] = None):
+    """``sscan_fwd`` through the library's allocation-free entry point: its scratch is a
+    static device array of the library (32 MiB per GPU), so the call itself allocates no
+    device memory when ``y`` and ``hT`` (and ``H``) are supplied.  Calls that overlap in
+    time on one GPU race on that array.  Same arguments and returns as ``sscan_fwd``."""
+    return _fwd_call(False, x, delta, A, b, c, None, h0, y, hT, H, return_H, plan, None, noalloc=True)
+
+
 def sscan_mamba_fwd(x: torch.Tensor, delta_raw: torch.Tensor, A_log: torch.Tensor, b: torch.Tensor,
                     c: torch.Tensor, Dskip: Optional[torch.Tensor] = None, h0: Optional[torch.Tensor] = None, *,
                     y: Optional[torch.Tensor] = None, hT: Optional[torch.Tensor] = None,
@@ -231,7 +242,8 @@ def sscan_fwd_ckpt(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, b: tor
     return _fwd_call(mamba, x, delta, A, b, c, Dskip, h0, y, hT, None, False, plan, workspace, ckpt=True, hck=hck)
 
 
-def _fwd_call(mamba, x, delta, A, b, c, Dskip, h0, y, hT, H, return_H, plan, workspace, ckpt=False, hck=None):
+def _fwd_call(mamba, x, delta, A, b, c, Dskip, h0, y, hT, H, return_H, plan, workspace, ckpt=False, hck=None,
+              noalloc=False):
     lib = _lib.load()
     if x.dtype not in _IO:
         raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
@@ -273,6 +285,12 @@ def _fwd_call(mamba, x, delta, A, b, c, Dskip, h0, y, hT, H, return_H, plan, wor
             _f32_out(hck, (B, nck, D, DS), "hck")
     d = _desc(B, T, D, DS, _IO[x.dtype], x_bs, bc_bs, y_bs)
     pc, pp = _plan_ptr(plan)
+    if noalloc:
+        with torch.cuda.device(device):
+            st = lib.sscan_fwd_noalloc(ctypes.byref(d), pp, _ptr(x), _ptr(delta), _ptr(A), _ptr(b), _ptr(c),
+                                       _ptr(h0), _ptr(y), _ptr(hT), _ptr(H), _stream(device))
+        _lib.check(st)
+        return (y, hT, H) if (return_H or H is not None) else (y, hT)
     nws = ctypes.c_size_t(0)
     _lib.check(lib.sscan_fwd_workspace(ctypes.byref(d), pp, ctypes.byref(nws)))
     ws, wsn = _workspace(int(nws.value), device, workspace)

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <limits>
+#include <mutex>
 
 #include "sscan.h"
 #include "sscan_internal.h"
@@ -269,6 +270,40 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(SSCAN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Scratch of the allocation-free forward (sscan_fwd_noalloc): one array per GPU, held
+// from the library's load until the process ends.  On the host, `scratch` names a
+// host-side stand-in, not device memory: kernels are given the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per device.
+static __device__ __align__(256) unsigned char scratch[SSCAN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's `scratch` for work enqueued on `stream`.
+int scratch_address(hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return hip_fail(e, "device of the stream");
+  if (dev < 0 || dev >= kMaxDevices) return fail(SSCAN_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e, "current device");
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e, "selecting the stream's device");
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return hip_fail(e, "address of the scratch array");
+    if (e2 != hipSuccess) return hip_fail(e2, "restoring the current device");
+    if (ptr == nullptr) return fail(SSCAN_ERR_HIP, "the scratch array has no device address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SSCAN_OK;
+}
+
 // The forward, plain (mamba = false) or wrapped: delta holds delta_raw, A holds A_log and
 // Dskip (may be null) adds the skip term.
 // The H-free sweep takes one boundary block per tile: lanes with kCkptSteps-step tiles
@@ -293,9 +328,11 @@ int resolve_hf_plan(const Resolved& r, const sscan_plan* plan, int* lanes, int* 
 }
 
 // hck (not null): instead of H, keep the state entering every kCkptSteps-step block.
+// use_scratch: ws/ws_bytes are ignored and the workspace is this device's `scratch` array
+// (sscan_fwd_noalloc); a call needing more than it holds fails before any GPU call.
 int fwd_impl(bool mamba, const sscan_desc* desc, const sscan_plan* plan, const void* x, const void* delta,
              const float* A, const void* b, const void* c, const float* Dskip, const float* h0, void* y, float* hT,
-             float* H, float* hck, void* ws, size_t ws_bytes, hipStream_t stream) {
+             float* H, float* hck, void* ws, size_t ws_bytes, hipStream_t stream, bool use_scratch = false) {
   Resolved r;
   int st = resolve_desc(desc, &r);
   if (st != SSCAN_OK) return st;
@@ -322,6 +359,18 @@ int fwd_impl(bool mamba, const sscan_desc* desc, const sscan_plan* plan, const v
     return e == hipSuccess ? ok() : hip_fail(e, "hT <- h0");
   }
   const FwdLayout lay = fwd_layout(r, chunks, sg);
+  if (use_scratch) {
+    if (lay.total > SSCAN_NOALLOC_SCRATCH_BYTES)
+      return fail(SSCAN_ERR_WORKSPACE, "this forward needs %zu bytes of scratch; the allocation-free entry point has %zu",
+                  lay.total, (size_t)SSCAN_NOALLOC_SCRATCH_BYTES);
+    ws = nullptr;
+    ws_bytes = 0;
+    if (lay.total > 0) {
+      st = scratch_address(stream, &ws);
+      if (st != SSCAN_OK) return st;
+      ws_bytes = SSCAN_NOALLOC_SCRATCH_BYTES;
+    }
+  }
   if (lay.total > 0) {
     if (ws == nullptr || ws_bytes < lay.total)
       return fail(SSCAN_ERR_WORKSPACE, "forward needs %zu workspace bytes, got %zu", lay.total, ws_bytes);
@@ -566,6 +615,12 @@ int sscan_fwd(const sscan_desc* desc, const sscan_plan* plan, const void* x, con
               const void* b, const void* c, const float* h0, void* y, float* hT, float* H, void* ws, size_t ws_bytes,
               hipStream_t stream) {
   return fwd_impl(false, desc, plan, x, delta, A, b, c, nullptr, h0, y, hT, H, nullptr, ws, ws_bytes, stream);
+}
+
+int sscan_fwd_noalloc(const sscan_desc* desc, const sscan_plan* plan, const void* x, const void* delta,
+                      const float* A, const void* b, const void* c, const float* h0, void* y, float* hT, float* H,
+                      hipStream_t stream) {
+  return fwd_impl(false, desc, plan, x, delta, A, b, c, nullptr, h0, y, hT, H, nullptr, nullptr, 0, stream, true);
 }
 
 int sscan_mamba_fwd(const sscan_desc* desc, const sscan_plan* plan, const void* x, const void* delta_raw,

@@ -320,3 +320,30 @@ def test_micro_library_rejects_bad_arguments_before_any_gpu_call():
     assert m.sscan_micro_rate(5, 1, 0, ctypes.byref(r)) == 1              # stream size missing
     assert m.sscan_micro_rate(6, 1, 1000, ctypes.byref(r)) == 1           # not a multiple of 16
     assert m.sscan_micro_rate(7, 1, (16 << 30) + 16, ctypes.byref(r)) == 1  # above 16 GiB
+
+
+def noalloc(lib, d, plan=None, x=FAKE, delta=FAKE, A=FAKE, b=FAKE, c=FAKE, h0=None, y=FAKE, hT=FAKE, H=None):
+    v = lambda p: None if p is None else ctypes.c_void_p(p)
+    return lib.sscan_fwd_noalloc(ctypes.byref(d), None if plan is None else ctypes.byref(plan), v(x), v(delta),
+                                 v(A), v(b), v(c), v(h0), v(y), v(hT), v(H), None)
+
+
+def test_noalloc_forward_validates_before_any_gpu_call(lib):
+    """The allocation-free forward rejects, without a GPU, bad arguments and a problem whose
+    scratch exceeds its static array (the state-group layout packs B*T*2*DS floats of b, c:
+    64 x 65536 x 32 x 4 B = 512 MiB > 32 MiB)."""
+    assert noalloc(lib, desc(), x=None) == E_NULL
+    assert noalloc(lib, desc(), y=FAKE + 2) == E_ALIGN
+    assert noalloc(lib, desc(DS=3)) == E_UNSUP
+    big = desc(B=64, T=65536, D=4, DS=16)
+    plan = sscan_plan()
+    plan.layout = 2  # state groups
+    plan.chunks = 1
+    assert noalloc(lib, big, plan=plan) == E_WS
+    assert b"32 MiB" in lib.sscan_last_error() or b"33554432" in lib.sscan_last_error()
+    n = ctypes.c_size_t(0)
+    assert lib.sscan_fwd_workspace(ctypes.byref(big), ctypes.byref(plan), ctypes.byref(n)) == OK
+    assert n.value > _lib.SSCAN_NOALLOC_SCRATCH_BYTES
+    # problems with nothing to do need no scratch and no GPU
+    assert noalloc(lib, desc(B=0)) == OK
+    assert noalloc(lib, desc(D=0)) == OK
