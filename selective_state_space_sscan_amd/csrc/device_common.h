@@ -50,6 +50,23 @@ __device__ __forceinline__ float buf_load_elem(rsrc_t r, uint32_t off) {
   return buf_load_f32(r, off, static_cast<IO*>(nullptr));
 }
 
+// The raw bits of one element of type IO at byte offset `off` (a bf16 zero-extended), and
+// their fp32 value.  Split so that a tile loaded ahead can stay in registers as loaded and
+// be widened only where it is used: a widening next to the load makes the compiler wait
+// for the load right there.
+template <typename IO>
+__device__ __forceinline__ uint32_t buf_load_bits(rsrc_t r, uint32_t off) {
+  if constexpr (sizeof(IO) == 2) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  } else {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  }
+}
+template <typename IO>
+__device__ __forceinline__ float bits_to_f32(uint32_t v) {
+  return sizeof(IO) == 2 ? __uint_as_float(v << 16) : __uint_as_float(v);
+}
+
 __device__ __forceinline__ void buf_store_elem(rsrc_t r, uint32_t off, float v, float*) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
 }
