@@ -12,7 +12,11 @@ also carries:
 * ``roofline`` for the entry point that dominates the step, timed live with HIP
   events on the stream the library launches on (torch's current stream), and the
   HBM traffic per launch from the committed rocprofv3 counter summary;
-* ``cpu_baseline``: the fp64 CPU oracle timed on this host on the same workload;
+* ``cpu_baseline``: the fp64 CPU oracle timed on this host on the same workload
+  (the value), plus one forward of each forward workload (``per_config``), the CPU
+  model and the thread count;
+* ``detail``: forward and backward times; the backward's HBM fraction on the method's
+  bytes (every row of H read) and on the bytes the sweep as built moves;
 * ``mamba`` and ``hfree``: the same step through the Mamba-style wrapper, and
   with boundary states every 32 steps in place of H;
 * ``fwd_only``: forward-only throughput on the three forward workloads
@@ -96,10 +100,11 @@ def fwd_alg_bytes(B, T, D, DS, s, with_H=False):
     return byt
 
 
-def bwd_alg_bytes(B, T, D, DS, s, h_read=0.25):
+def bwd_alg_bytes(B, T, D, DS, s, h_read=1.0):
     """Bytes the backward must move: dy, x, delta in; H in; gx, gdelta out; b, c in; gb, gc out;
-    A in, gA out; h0 in, gh0 out.  h_read: the fraction of H's rows the sweep reads (with four
-    states per lane it reads every fourth row and forms the three after it, bitwise)."""
+    A in, gA out; h0 in, gh0 out.  h_read: the fraction of H's rows read; the method reads every
+    row (1.0, the algorithmic figure); the sweep as built with four states per lane reads every
+    fourth row and forms the three after it from it (0.25)."""
     n = B * T * D
     return (3 * s * n + int(h_read * 4 * n * DS) + 2 * 4 * n + 2 * s * B * T * DS + 2 * 4 * B * T * DS
             + 2 * 4 * D * DS + 2 * 4 * B * D * DS)
@@ -161,7 +166,7 @@ def main() -> int:
             torch.empty((B, T, DS), **f32), torch.empty((D, DS), **f32), torch.empty((B, D, DS), **f32))
     ws_f = torch.empty(max(1, sscan_fwd_workspace(B, T, D, DS)), dtype=torch.uint8, device=dev)
     ws_b = torch.empty(max(1, sscan_bwd_workspace(B, T, D, DS)), dtype=torch.uint8, device=dev)
-    plan_f = sscan_plan_select(B, T, D, DS)
+    plan_f = sscan_plan_select(B, T, D, DS, with_H=True)
     plan_b = sscan_plan_select(B, T, D, DS, backward=True)
 
     def fwd(k):
@@ -198,6 +203,7 @@ def main() -> int:
 
     fbytes = fwd_alg_bytes(B, T, D, DS, 4, with_H=True)
     bbytes = bwd_alg_bytes(B, T, D, DS, 4)
+    bbytes_built = bwd_alg_bytes(B, T, D, DS, 4, h_read=0.25)
     f_avg, b_avg = float(fwd_ms.mean()), float(bwd_ms.mean())
     # The dominant entry point is timed as one launch: sscan_bwd enqueues the local pass of
     # its two-level sweep, the sweep and the kernel that adds its partial sums, back to back
@@ -217,6 +223,9 @@ def main() -> int:
         "fwd_elems_per_s": elems / (f_avg * 1e-3), "bwd_elems_per_s": elems / (b_avg * 1e-3),
         "fwd_hbm_frac": round(fbytes / (f_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "bwd_hbm_frac": round(bbytes / (b_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "bwd_alg_bytes": int(bbytes),
+        "bwd_hbm_frac_as_built": round(bbytes_built / (b_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "bwd_bytes_as_built": int(bbytes_built),
         "plan_fwd": {"lanes": plan_f.lanes, "chunks": plan_f.chunks},
         "plan_bwd": {"lanes": plan_b.lanes, "chunks": plan_b.chunks},
         "wall_s_timed": round(wall, 4),
@@ -230,6 +239,8 @@ def main() -> int:
 
     cpu = None
     if not args.no_cpu_baseline:
+        del sets
+        torch.cuda.empty_cache()
         cpu = cpu_baseline(inp, w)
 
     line = {
@@ -500,9 +511,23 @@ def bench_fwd_only(dev, warmup, reps):
     return out
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp, w):
-    """The fp64 oracle, as it stands, on this host: one forward + backward of the whole workload."""
+    """The fp64 oracle, as it stands, on this host: one forward + backward of the whole bench
+    workload (the line's value), then one forward of each forward workload at full size (the
+    long one as a single unchunked pass over all its steps), and the smallest one on one core."""
     import oracle
+    import workloads
 
     n = oracle.default_threads()
     t0 = time.perf_counter()
@@ -511,9 +536,22 @@ def cpu_baseline(inp, w):
     oracle.bwd(inp["dy"], inp["x"], inp["delta"], inp["A"], inp["b"], inp["c"], inp["h0"], None, nthreads=n)
     t2 = time.perf_counter()
     elems = w.B * w.T * w.D
+    per = {f"{w.name}_fwd": {"s": round(t1 - t0, 4), "cores": n, "elems_per_s": elems / (t1 - t0)},
+           f"{w.name}_bwd": {"s": round(t2 - t1, 4), "cores": n, "elems_per_s": elems / (t2 - t1)}}
+    for name, threads in (("fwd_f32", n), ("fwd_f32", 1), ("fwd_bf16", n), ("long_chunked_bf16", n)):
+        wl = workloads.get(name)
+        x = workloads.make_inputs(wl)
+        a = time.perf_counter()
+        oracle.fwd(x["x"], x["delta"], x["A"], x["b"], x["c"], x["h0"], nthreads=threads)
+        dt = time.perf_counter() - a
+        del x
+        key = f"{name}_fwd" + ("" if threads == n else f"_{threads}core")
+        per[key] = {"s": round(dt, 4), "cores": threads, "elems_per_s": wl.elems / dt}
+        print(f"bench: oracle {key}: {dt:.3f} s on {threads} cores", file=sys.stderr, flush=True)
     return {"value": elems / (t2 - t0), "unit": "B*T*D elements/s (forward + backward)", "cores": n, "kind": "oracle",
             "sample": f"the whole {w.B}x{w.T}x{w.D}x{w.DS} workload, one forward (no H) + one backward "
-                      f"(which recomputes its states); fwd {t1 - t0:.3f} s, bwd {t2 - t1:.3f} s"}
+                      f"(which recomputes its states); fwd {t1 - t0:.3f} s, bwd {t2 - t1:.3f} s",
+            "cpu_model": cpu_model(), "per_config": per}
 
 
 if __name__ == "__main__":

@@ -51,8 +51,9 @@ def _load():
     global _lib
     with _lock:
         if _lib is None:
-            build()
-            lib = ctypes.CDLL(_LIB)
+            # SSCAN_ORACLE_LIBRARY: an instrumented build of sscan_oracle.c (the sanitizer test)
+            path = os.environ.get("SSCAN_ORACLE_LIBRARY") or build()
+            lib = ctypes.CDLL(path)
             i64, dp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
             lib.sscan_oracle_fwd.argtypes = [i64, i64, i64, i64] + [dp] * 9 + [ci]
             lib.sscan_oracle_fwd.restype = ci

@@ -10,7 +10,9 @@ import os
 import threading
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libsscan.so")
+# SSCAN_LIBRARY names another build of the same library (the host-sanitizer test loads one
+# whose host code is instrumented); by default the in-tree build.
+LIB_PATH = os.environ.get("SSCAN_LIBRARY") or os.path.join(PKG, "libsscan.so")
 
 SSCAN_F32 = 0
 SSCAN_BF16 = 1

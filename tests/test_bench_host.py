@@ -39,12 +39,13 @@ def test_backward_bytes_per_element():
     # written (16 B per (b, t, n)); A read, gA written; h0 read, gh0 written
     assert full == 84 * n + 16 * B * T * DS + 8 * D * DS + 8 * B * D * DS
     assert abs(full / 1e6 - 1062.0) < 0.1
+    assert bench.bwd_alg_bytes(B, T, D, DS, 4) == full  # the method's bytes are the default
     # the sweep as built reads every fourth row of H
-    got = bench.bwd_alg_bytes(B, T, D, DS, 4)
+    got = bench.bwd_alg_bytes(B, T, D, DS, 4, h_read=0.25)
     assert full - got == 48 * n
     assert abs(got / 1e6 - 458.1) < 0.1
     # bf16 I/O halves only the three (B,T,D) inputs and b, c
-    assert bench.bwd_alg_bytes(B, T, D, DS, 2) == got - 6 * n - 4 * B * T * DS
+    assert bench.bwd_alg_bytes(B, T, D, DS, 2, h_read=0.25) == got - 6 * n - 4 * B * T * DS
 
 
 def test_alu_peak_from_unit_counts():
