@@ -145,7 +145,12 @@ int sscan_fwd_noalloc(const sscan_desc* desc, const sscan_plan* plan, const void
 
 /* Backward: gradients of L = sum(dy*y) + sum(dhT*hT) for the forward with the same inputs.
  *   dy (B,T,D) io; dhT (B,D,DS) fp32 or NULL (zeros); x, delta, A, b, c, h0 as in sscan_fwd;
- *   H (B,T,D,DS) fp32, the states the forward materialised, required when T > 0.
+ *   H (B,T,D,DS) fp32, the states the forward materialised, required when T > 0.  With four
+ *   states per lane (the default plan for DS >= 4) the backward reads only rows 3, 7, 11, ...
+ *   and the last of H, and forms the three rows after each of them with the forward's own
+ *   update on the same inputs: bit for bit the stored rows when the forward ran as one pass,
+ *   within fp32 rounding of them where the forward split T into chunks (sscan_plan_select
+ *   with SSCAN_PLAN_FWD_H reports its chunks).  Other plans read every row.
  *   gx, gdelta (B,T,D) fp32; gb, gc (B,T,DS) fp32, summed over channels;
  *   gA (D,DS) fp32, summed over batch rows and steps; gh0 (B,D,DS) fp32 or NULL (not written).
  *   T == 0: gA = 0 and gh0 = dhT (zeros if NULL).  B == 0: gA = 0.

@@ -23,8 +23,10 @@
 // consecutive addresses of each step row; H is read once, and kept out of the caches
 // it would otherwise flush), parked in a per-wave LDS block when their sub-block starts
 // (with four states per lane each lane's load is exactly its own states, which stay in
-// registers; then only every other row is read, and the row between is formed from it by
-// the forward's own update, bitwise equal to the stored row), and read back by each lane
+// registers; then only the first row of each block is read, and the rows after it are formed
+// from it by the forward's own update -- bit for bit the stored rows when the forward ran
+// as one pass, within fp32 rounding of them where a split forward started a chunk inside
+// the block), and read back by each lane
 // for its own states; H_t is kept from the step before.  Sums over a channel's states
 // use DPP; sums over channels use DPP row rotations, the gfx950 row-swap permutes and
 // one LDS slot per wave, and each workgroup writes one (gb, gc) partial per (step,
@@ -331,8 +333,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DS == 
   constexpr bool HDIRECT = !HF && K == 4 && DB == 16;
   static_assert(!HDIRECT || NQ == HB, "one load per step row");
   // With one step per batch, only the first row of each HB-row block is read; the rows
-  // after it are formed from it with the forward's own operations on the same inputs, so
-  // they are bitwise the rows the forward stored: a quarter of the H traffic at HB = 4.
+  // after it are formed from it with the forward's own operations on the same inputs: a
+  // quarter of the H traffic at HB = 4.  They are bit for bit the rows a single-pass
+  // forward stored; where the forward split the sequence (its two-level scan), the state
+  // it started a chunk from was composed from the chunk pairs rather than read from the
+  // row before, so rows formed across such a chunk start agree with the stored ones only
+  // to fp32 rounding (well inside the tolerance; the gradients are still exact adjoints
+  // of states within rounding of the forward's).
   constexpr bool HFIRST = HDIRECT && S == 1;
   float hq[NQ][DB / 4];
   float hb[HDIRECT ? NQ : 1][DB / 4];
