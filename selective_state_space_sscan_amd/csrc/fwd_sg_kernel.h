@@ -13,14 +13,14 @@
 // over steps; each row loads its group's block of them (lane q holds floats 4q .. 4q+3 of
 // a 64-float block), and every use reads the value it needs from the lane that holds it
 // with a DPP row broadcast folded into the multiply (row_newbcast), so b and c cost
-// neither LDS traffic nor extra instructions.  The workgroup stages (delta, delta*x) of a
-// tile once in LDS (each element converted by one thread, the softplus of the wrapper
-// applied there), and every lane reads its channel's from it.  Each group leaves its
-// partial sum over its K states of h * c per (step, channel) in LDS, and after the tile
-// the workgroup adds the NG partials and stores y coalesced.  Per (step, state) a lane
-// does one v_exp_f32 and four fp32 operations, with no other cross-lane traffic: about 5.7
-// instructions per state against 7 for the lane-split forward, which spends 1.5 on DPP
-// sums over a channel's lanes.
+// neither LDS traffic nor extra instructions.  Separate reducer waves of the workgroup stage
+// (delta, delta*x) of a tile once in LDS (each element converted by one thread, the softplus
+// of the wrapper applied there), and every lane reads its channel's from it.  Each group
+// leaves its partial sum over its K states of h * c per (step, channel) in LDS, and the
+// reducer waves add the NG partials and store y coalesced while the next tile computes.
+// Per (step, state) a compute lane does one v_exp_f32 and four fp32 operations, with no
+// other cross-lane traffic: about 5.7 instructions per state against 7 for the lane-split
+// forward, which spends 1.5 on DPP sums over a channel's lanes.
 //
 // Steps past the end of the chunk load delta = 0 and b = c = 0 (buffer range checks),
 // which leaves the state bit-for-bit unchanged.
@@ -100,55 +100,68 @@ __device__ __forceinline__ void fmac_bcast_rt(float& acc, float c, float h, int 
 #undef SSCAN_FMAC_CASE
 }
 
+// Reducer waves per workgroup of the state-group forward, and (step, channel) elements of
+// one tile: 32 steps of 64 channels or 64 of 32.
+constexpr int kSgReducerWaves = 4;
+constexpr int kSgTileElems = 2048;
+
+template <int DS, int K, int CW>
+__host__ __device__ constexpr int sg_threads() {
+  return 64 * ((DS / K) / (64 / CW) + kSgReducerWaves);
+}
+
 // MODE: 0 the two-level scan's local pass (only the chunk pair leaves the kernel), 1 y and
 // hT, 2 y, hT and the H-free path's boundary states.  CW: channels per wave (64 or 32); a
 // wave holds 64/CW state groups, one per CW/16 rows, so every 16-lane row belongs to a
 // single group and its DPP row broadcasts stay within it.
 //
-// Tile pipeline (per tile of TB steps, one workgroup barrier at each end): after the first
-// barrier the workgroup issues the global loads of the next tile (x and delta as raw bits,
-// widened only when they are parked after the second barrier, so that no wait for a load
-// in flight lands in the step code) and the next b/c blocks into the other of two register
-// sets.  The step code runs batches of S = 4 steps, reading the next batch's (delta,
-// delta*x) from LDS while it computes the current one, and leaves each batch's four partial
-// readouts as one 16-byte LDS store.  After the second barrier every thread sums the state
-// groups of (channel, 4-step) items and stores y.  Measured at 16x4096x1024x16 and
-// 4x2048x2048x16 bf16 against the previous version of this kernel (one batch read at a
-// time, one LDS store per step, channel-vector items, a nop before each DPP readout, b/c
-// copied between register sets): 331 -> 302 us and 110 -> 91 us, bitwise the same hT and y.
+// Two kinds of wave.  The compute waves (one per state group pair: NW of them) run only the
+// step code: per batch of S = 4 steps, the decays and injections, the serial update, and
+// the partial readouts of their K states, left as one 16-byte LDS store per lane.  The
+// kSgReducerWaves reducer waves stage the inputs of the next tile (global loads of x and
+// delta as raw bits, widened -- and passed through the softplus of the wrapper -- when they
+// are parked in LDS) and sum the previous tile's partial readouts over the state groups into
+// y.  Staged inputs and partial sums are double-buffered, so the two kinds meet at one
+// barrier per tile: at tile it the compute waves read inputs buffer it % 2 and write partial
+// buffer it % 2 while the reducers sum partial buffer (it-1) % 2 and fill inputs buffer
+// (it+1) % 2.  The compute waves load the next tile's b/c blocks into the other of two
+// register sets, so every DPP source is written by a buffer load only.  Measured against the
+// same kernel with the staging and the sum over groups done by the compute waves between
+// two barriers per tile: 16x4096x1024x16 bf16 292 -> 270 us, 4x2048x2048x16 bf16 90 -> 73 us
+// per call, bitwise the same y and hT.
 template <typename IO, int DS, int K, int CW, int MODE, bool MAMBA>
-__global__ __launch_bounds__(64 * (DS / K) / (64 / CW)) void fwd_sg_kernel(const FwdParams p) {
+__global__ __launch_bounds__((sg_threads<DS, K, CW>())) void fwd_sg_kernel(const FwdParams p) {
   constexpr bool LOCAL = MODE == 0;
-  constexpr int NG = DS / K;        // state groups
-  constexpr int GPW = 64 / CW;      // state groups per wave
-  constexpr int NW = NG / GPW;      // waves per workgroup
-  constexpr int NT = 64 * NW;
-  constexpr int TB = kSgTile;
+  constexpr int NG = DS / K;            // state groups
+  constexpr int GPW = 64 / CW;          // state groups per wave
+  constexpr int NW = NG / GPW;          // compute waves
+  constexpr int NTC = 64 * NW;          // compute threads
+  constexpr int NTR = 64 * kSgReducerWaves;  // reducer threads
+  constexpr int TB = kSgTileElems / CW;  // steps per tile
   constexpr int S = 4;  // steps per batch: one 16-byte store of partial readouts
   constexpr int E2 = 2 * K;
   constexpr uint32_t ES = sizeof(IO);
-  constexpr int TILE = TB * CW;     // (step, channel) elements of a tile
-  constexpr int PER = TILE / NT;    // elements each thread stages
-  constexpr int NB = TB * E2 / 64;  // 64-float blocks of packed b/c per tile
+  constexpr int TILE = TB * CW;         // (step, channel) elements of a tile
+  constexpr int PER = TILE / NTR;       // elements each reducer thread stages
+  constexpr int NB = TB * E2 / 64;      // 64-float blocks of packed b/c per tile
   constexpr int ITEMS = CW * (TB / 4);  // (channel, 4-step) items of a tile's readout
-  // partial readouts: s_y[group][channel][step], the 4-step blocks of a channel's row
-  // permuted by its low channel bits so that a wave's 16-byte stores and loads spread over
-  // all banks
+  // partial readouts: [group][channel][step], the 4-step blocks of a channel's row permuted
+  // by its low channel bits so that a wave's 16-byte stores and loads spread over all banks
   constexpr int QM = (TB / 4 < 16 ? TB / 4 : 16) - 1;
+  constexpr int PSZ = NG * CW * TB / 4;  // float4 of one partial buffer
   static_assert(CW % 16 == 0 && NG % GPW == 0 && NW >= 1, "rows of one state group");
-  static_assert(TILE % NT == 0 && TB % S == 0 && TB % kCkptSteps == 0 && kCkptSteps % S == 0 && (TB * E2) % 64 == 0,
+  static_assert(TILE % NTR == 0 && TB % S == 0 && TB % kCkptSteps == 0 && kCkptSteps % S == 0 &&
+                    (TB * E2) % 64 == 0 && kSgTile % TB == 0,
                 "tile shape");
 
-  // (delta, delta*x) at [step*CW + channel]; with the wrapper (delta, x), so that the
-  // first state group can add the skip term Dskip * x to its partial sums
-  __shared__ float2 s_dw[TILE];
-  __shared__ float4 s_y[LOCAL ? 1 : NG * CW * TB / 4];
+  // (delta, delta*x) at [buffer][step*CW + channel]; with the wrapper (delta, x), so that
+  // the first state group can add the skip term Dskip * x to its partial sums
+  __shared__ float2 s_dw[2 * TILE];
+  __shared__ float4 s_y[LOCAL ? 1 : 2 * PSZ];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c = lane % CW;             // this lane's channel within the workgroup
-  const int grp = w * GPW + lane / CW;  // this lane's state group
   const int lin = blockIdx.x;
   const int dtile = lin % p.ntiles_d;
   const int rest = lin / p.ntiles_d;
@@ -156,14 +169,107 @@ __global__ __launch_bounds__(64 * (DS / K) / (64 / CW)) void fwd_sg_kernel(const
   const int chunk = rest / p.B;
   const int D = p.D;
   const int d0 = dtile * CW;
-  const int d = d0 + c;
-  const bool dvalid = d < D;
   const int t_begin = chunk * p.chunk_len;
   const int t_end = min(p.T, t_begin + p.chunk_len);
+  const int nsteps_total = t_end - t_begin;
+  const int ntiles = nsteps_total > 0 ? (nsteps_total + TB - 1) / TB : 0;
 
-  const IO* xrow = static_cast<const IO*>(p.x) + (int64_t)bb * p.x_bs;
-  const IO* drow = static_cast<const IO*>(p.delta) + (int64_t)bb * p.x_bs;
-  IO* yrow = static_cast<IO*>(p.y) + (int64_t)bb * p.y_bs;
+  if (w >= NW) {
+    // ---- reducer waves: stage the next tile, sum the previous one's partials into y
+    const int rt = tid - NTC;
+    const IO* xrow = static_cast<const IO*>(p.x) + (int64_t)bb * p.x_bs;
+    const IO* drow = static_cast<const IO*>(p.delta) + (int64_t)bb * p.x_bs;
+    IO* yrow = static_cast<IO*>(p.y) + (int64_t)bb * p.y_bs;
+    // staged elements: idx = rt + e*NTR is (step idx / CW, channel idx % CW); columns past D
+    // are forced out of range, rows past the chunk fall outside the resource
+    uint32_t xoff[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int idx = rt + e * NTR;
+      const int dd = d0 + (idx % CW);
+      xoff[e] = dd < D ? static_cast<uint32_t>((idx / CW) * D + dd) * ES : kOutOfRange;
+    }
+    uint32_t rx[PER], rd[PER];  // raw bits of the tile loaded last
+    int pend_rows = 0;
+    auto load_tile = [&](int ts) {
+      const int rows = tile_rows(t_end, ts, TB);
+      pend_rows = rows;
+      const rsrc_t rX = make_rsrc(xrow + (int64_t)ts * D, static_cast<uint32_t>(rows * D) * ES);
+      const rsrc_t rD = make_rsrc(drow + (int64_t)ts * D, static_cast<uint32_t>(rows * D) * ES);
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        rx[e] = buf_load_bits<IO>(rX, xoff[e]);
+        rd[e] = buf_load_bits<IO>(rD, xoff[e]);
+      }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const float xv = bits_to_f32<IO>(rx[e]);
+        const float dv = bits_to_f32<IO>(rd[e]);
+        // padded steps and channels keep delta = 0 (a multiply by a 0/1 mask: a select
+        // lets the compiler branch around the softplus)
+        const float keep = (((rt + e * NTR) / CW) < pend_rows && xoff[e] != kOutOfRange) ? 1.f : 0.f;
+        const float dl = MAMBA ? softplus_th(dv) * keep : dv;
+        s_dw[buf * TILE + rt + e * NTR] = make_float2(dl, MAMBA ? xv : dl * xv);
+      }
+    };
+    auto reduce_tile = [&](int it) {
+      const int ts = t_begin + it * TB;
+      const int rows = min(TB, t_end - ts);
+      const rsrc_t rY = make_rsrc(yrow + (int64_t)ts * D, static_cast<uint32_t>(rows * D) * ES);
+      const float* P = reinterpret_cast<const float*>(s_y + (it & 1) * PSZ);
+#pragma unroll
+      for (int i0 = 0; i0 < ITEMS; i0 += NTR) {
+        // every thread stores (out of range when it has no item), so the number of
+        // stores in flight does not depend on the thread
+        const int item = i0 + rt;
+        const bool act = ITEMS % NTR == 0 || item < ITEMS;
+        const int cc = item % CW;            // channel
+        const int q4 = act ? item / CW : 0;  // 4-step block
+        const float* src = P + cc * TB + 4 * (q4 ^ (cc & QM));
+        float4 acc = *reinterpret_cast<const float4*>(src);
+#pragma unroll
+        for (int gg = 1; gg < NG; ++gg) {
+          const float4 v = *reinterpret_cast<const float4*>(src + gg * CW * TB);
+          acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        }
+        // one value per step row; lanes hold consecutive channels, so each store is
+        // coalesced; rows past the tile fall outside the resource
+        const int dd = d0 + cc;
+        const uint32_t off = (act && dd < D) ? static_cast<uint32_t>(4 * q4 * D + dd) * ES : kOutOfRange;
+        const uint32_t row = static_cast<uint32_t>(D) * ES;
+        buf_store_io<IO>(rY, off, acc.x);
+        buf_store_io<IO>(rY, off == kOutOfRange ? off : off + row, acc.y);
+        buf_store_io<IO>(rY, off == kOutOfRange ? off : off + 2 * row, acc.z);
+        buf_store_io<IO>(rY, off == kOutOfRange ? off : off + 3 * row, acc.w);
+      }
+    };
+    if (ntiles > 0) {
+      load_tile(t_begin);
+      store_tile(0);
+      load_tile(t_begin + TB);  // zeros past the end of the chunk
+    }
+    for (int it = 0; it < ntiles; ++it) {
+      __syncthreads();  // tile `it` staged; its partial buffer's previous contents summed
+      if constexpr (!LOCAL) {
+        if (it > 0) reduce_tile(it - 1);
+      }
+      store_tile((it + 1) & 1);
+      load_tile(t_begin + (it + 2) * TB);
+    }
+    if (ntiles > 0) {
+      __syncthreads();  // the last tile's partials
+      if constexpr (!LOCAL) reduce_tile(ntiles - 1);
+    }
+    return;
+  }
+
+  // ---- compute waves
+  const int c = lane % CW;              // this lane's channel within the workgroup
+  const int grp = w * GPW + lane / CW;  // this lane's state group
+  const int d = d0 + c;
+  const bool dvalid = d < D;
   // the packed b/c rows of this batch row; lane q of each 16-lane row loads floats
   // 4q .. 4q+3 of every 64-float block of its group's row
   const rsrc_t rBC = make_rsrc(p.bcp + (int64_t)bb * NG * p.tpad * E2, static_cast<uint32_t>(NG * p.tpad * E2) * 4u);
@@ -206,44 +312,9 @@ __global__ __launch_bounds__(64 * (DS / K) / (64 / CW)) void fwd_sg_kernel(const
     for (int i = 0; i < K; ++i) { A2[i] = 0.f; h[i] = 0.f; }
   }
   double dsum = 0.0;  // local pass: sum of delta over the chunk
-
-  // staged elements: idx = tid + e*NT is (step idx / CW, channel idx % CW); columns past D
-  // are forced out of range, rows past the chunk fall outside the resource
-  uint32_t xoff[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const int idx = tid + e * NT;
-    const int dd = d0 + (idx % CW);
-    xoff[e] = dd < D ? static_cast<uint32_t>((idx / CW) * D + dd) * ES : kOutOfRange;
-  }
   // the skip weight of this lane's channel (used by the first state group)
   const float dskip = (MAMBA && !LOCAL && grp == 0 && p.Dskip != nullptr && dvalid) ? p.Dskip[d] : 0.f;
-  uint32_t rx[PER], rd[PER];  // raw bits of the next tile's x and delta
-  int pend_rows = 0;
-  auto load_tile = [&](int ts) {
-    const int rows = tile_rows(t_end, ts, TB);
-    pend_rows = rows;
-    const rsrc_t rX = make_rsrc(xrow + (int64_t)ts * D, static_cast<uint32_t>(rows * D) * ES);
-    const rsrc_t rD = make_rsrc(drow + (int64_t)ts * D, static_cast<uint32_t>(rows * D) * ES);
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      rx[e] = buf_load_bits<IO>(rX, xoff[e]);
-      rd[e] = buf_load_bits<IO>(rD, xoff[e]);
-    }
-  };
-  auto store_tile = [&]() {
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const float xv = bits_to_f32<IO>(rx[e]);
-      const float dv = bits_to_f32<IO>(rd[e]);
-      // padded steps and channels keep delta = 0 (a multiply by a 0/1 mask: a select
-      // lets the compiler branch around the softplus)
-      const float keep = (((tid + e * NT) / CW) < pend_rows && xoff[e] != kOutOfRange) ? 1.f : 0.f;
-      const float dl = MAMBA ? softplus_th(dv) * keep : dv;
-      s_dw[tid + e * NT] = make_float2(dl, MAMBA ? xv : dl * xv);
-    }
-  };
+
   auto load_bc = [&](int ts, float (&dst)[NB][4]) {
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
@@ -255,36 +326,29 @@ __global__ __launch_bounds__(64 * (DS / K) / (64 / CW)) void fwd_sg_kernel(const
       dst[k][2] = __uint_as_float(t[2]); dst[k][3] = __uint_as_float(t[3]);
     }
   };
-
-  const int nsteps_total = t_end - t_begin;
-  const int ntiles = nsteps_total > 0 ? (nsteps_total + TB - 1) / TB : 0;
   float bcA[NB][4], bcB[NB][4];  // b/c blocks: the current tile's and the next one's, alternating
-  if (ntiles > 0) {
-    load_tile(t_begin);
-    load_bc(t_begin, bcA);
-    store_tile();
-  }
-  float* const sy = reinterpret_cast<float*>(s_y) + (grp * CW + c) * TB;  // this lane's row of partials
+  if (ntiles > 0) load_bc(t_begin, bcA);
 
   auto do_tile = [&](int it, const float (&bcv)[NB][4], float (&bcw)[NB][4]) {
     const int ts = t_begin + it * TB;
-    const int rows = min(TB, t_end - ts);
+    const int buf = it & 1;
     const int kb0 = ts / kCkptSteps;  // first boundary block of the tile
     const rsrc_t rCk = make_rsrc(MODE == 2 ? ckrow + (int64_t)kb0 * D * DS : nullptr,
                                  MODE == 2 ? static_cast<uint32_t>(min(p.nck - kb0, kCkBlocks) * D * DS) * 4u : 0u);
-    __syncthreads();  // this tile's inputs are in LDS; the previous tile's partial sums are read
-    load_tile(ts + TB);  // zeros past the end of the chunk
+    __syncthreads();  // this tile's inputs are staged; the partial buffer it writes is free
     load_bc(ts + TB, bcw);
+    const float2* DW = s_dw + buf * TILE;
+    float* const sy = reinterpret_cast<float*>(s_y + (LOCAL ? 0 : buf * PSZ)) + (grp * CW + c) * TB;
 
     float2 dwc[S];
 #pragma unroll
-    for (int s = 0; s < S; ++s) dwc[s] = s_dw[s * CW + c];
+    for (int s = 0; s < S; ++s) dwc[s] = DW[s * CW + c];
 #pragma unroll
     for (int s0 = 0; s0 < TB; s0 += S) {
       float2 dwn[S];  // the next batch's inputs, read while this one computes
       if (s0 + S < TB) {
 #pragma unroll
-        for (int s = 0; s < S; ++s) dwn[s] = s_dw[(s0 + S + s) * CW + c];
+        for (int s = 0; s < S; ++s) dwn[s] = DW[(s0 + S + s) * CW + c];
       }
       if constexpr (MODE == 2) {
         // the state entering every kCkptSteps-step block: tiles start on multiples of the
@@ -347,43 +411,13 @@ __global__ __launch_bounds__(64 * (DS / K) / (64 / CW)) void fwd_sg_kernel(const
         for (int s = 0; s < S; ++s) dwc[s] = dwn[s];
       }
     }
-
-    __syncthreads();  // every wave is done with this tile's inputs and has left its partials
-    if constexpr (!LOCAL) {
-      const rsrc_t rY = make_rsrc(yrow + (int64_t)ts * D, static_cast<uint32_t>(rows * D) * ES);
-#pragma unroll
-      for (int i0 = 0; i0 < ITEMS; i0 += NT) {
-        // every thread stores (out of range when it has no item), so the number of
-        // stores in flight does not depend on the thread
-        const int item = i0 + tid;
-        const bool act = ITEMS % NT == 0 || item < ITEMS;
-        const int cc = item % CW;            // channel
-        const int q4 = act ? item / CW : 0;  // 4-step block
-        const float* src = reinterpret_cast<const float*>(s_y) + cc * TB + 4 * (q4 ^ (cc & QM));
-        float4 acc = *reinterpret_cast<const float4*>(src);
-#pragma unroll
-        for (int gg = 1; gg < NG; ++gg) {
-          const float4 v = *reinterpret_cast<const float4*>(src + gg * CW * TB);
-          acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-        }
-        // one value per step row; lanes hold consecutive channels, so each store is
-        // coalesced; rows past the tile fall outside the resource
-        const int dd = d0 + cc;
-        const uint32_t off = (act && dd < D) ? static_cast<uint32_t>(4 * q4 * D + dd) * ES : kOutOfRange;
-        const uint32_t row = static_cast<uint32_t>(D) * ES;
-        buf_store_io<IO>(rY, off, acc.x);
-        buf_store_io<IO>(rY, off == kOutOfRange ? off : off + row, acc.y);
-        buf_store_io<IO>(rY, off == kOutOfRange ? off : off + 2 * row, acc.z);
-        buf_store_io<IO>(rY, off == kOutOfRange ? off : off + 3 * row, acc.w);
-      }
-    }
-    store_tile();  // the next tile's inputs (zeros past the end of the chunk)
   };
 
   for (int it = 0; it < ntiles; it += 2) {
     do_tile(it, bcA, bcB);
     if (it + 1 < ntiles) do_tile(it + 1, bcB, bcA);
   }
+  if (ntiles > 0) __syncthreads();  // the reducers' last barrier: this tile's partials are complete
 
   if (!dvalid) return;
   if constexpr (LOCAL) {
@@ -408,7 +442,7 @@ hipError_t launch_bc_pack_t(const FwdParams& p, hipStream_t s) {
 
 template <typename IO, int DS, int K, int CW, bool MAMBA>
 hipError_t launch_fwd_sg_t(bool local_pass, const FwdParams& p, unsigned blocks, hipStream_t s) {
-  constexpr int NT = 64 * (DS / K) / (64 / CW);
+  constexpr int NT = sg_threads<DS, K, CW>();
   if (local_pass)
     hipLaunchKernelGGL((fwd_sg_kernel<IO, DS, K, CW, 0, MAMBA>), dim3(blocks), dim3(NT), 0, s, p);
   else if (p.hck != nullptr)
