@@ -152,9 +152,10 @@ int resolve_plan(const Resolved& r, const sscan_plan* plan, PlanKind kind, int* 
 // The forward's plan: lanes, T-chunks, whether the state-group layout runs and its
 // channels per workgroup (cw).  That layout needs DS in {4, 8, 16}, D a multiple of 4,
 // T < 2^24 and no H (with_H).  Chosen by itself for a single pass with at least 256
-// 64-channel or 128 32-channel workgroups (16x4096x1024x16 bf16: 0.321 ms against 0.333 ms
-// for lanes, warm inputs); split sequences gain nothing (8x1024x256x16 fp32: 0.034 ms
-// against 0.031 ms).
+// 64-channel or 128 32-channel workgroups, with or without boundary states
+// (16x4096x1024x16 bf16: 0.278 ms against 0.32 ms for lanes; 8x2048x768x16 fp32: 73 us
+// against 137 us); split sequences gain nothing (8x1024x256x16 fp32 in 8 chunks: 28.0 us
+// against 27.5 us for lanes).
 int resolve_fwd_plan(const Resolved& r, const sscan_plan* plan, bool with_H, bool with_ck, int* lanes, int* chunks,
                      bool* sg, int* cw) {
   const bool sg_ok = !with_H && (r.DS == 4 || r.DS == 8 || r.DS == 16) && r.D % 4 == 0 && r.T < (1 << 24);
@@ -170,7 +171,14 @@ int resolve_fwd_plan(const Resolved& r, const sscan_plan* plan, bool with_H, boo
   }
   int st = resolve_plan(r, plan, kPlanFwd, lanes, chunks);
   if (st != SSCAN_OK) return st;
-  if (with_ck && (plan == nullptr || plan->chunks == 0)) {
+  // a single pass of the state-group layout with enough workgroups beats every split of the
+  // forward keeping boundary states (8x2048x768x16 fp32: 78 us against 110 us for the lanes
+  // layout in 4 chunks; 16x4096x1024x16 bf16: 264 against 321-355 us), so that forward
+  // splits only when the state-group layout cannot fill the GPU in one pass
+  const bool sg_single = sg_ok && *lanes == sg_lanes && want != SSCAN_LAYOUT_LANES && (plan == nullptr || plan->chunks <= 1) &&
+                         (plan == nullptr || plan->lanes == 0 || plan->lanes == sg_lanes) &&
+                         (r.B * ceil_div(r.D, 64) >= 256 || r.B * ceil_div(r.D, 32) >= 128);
+  if (with_ck && !sg_single && (plan == nullptr || plan->chunks == 0)) {
     // The forward keeping boundary states is bound by its per-step latency below one wave
     // per SIMD: split the sequence to three waves per SIMD, every chunk keeping at least 128
     // steps (8x2048x768x16 fp32: 4 chunks 0.119 ms, 1 chunk 0.139 ms; the forward without
@@ -193,9 +201,7 @@ int resolve_fwd_plan(const Resolved& r, const sscan_plan* plan, bool with_H, boo
   *sg = false;
   if (want == SSCAN_LAYOUT_STATE_GROUPS) {
     *sg = true;
-  } else if (want == SSCAN_LAYOUT_AUTO && sg_ok && !with_ck && *lanes == sg_lanes) {
-    // (its boundary-state stores, two floats per lane with lanes 16 floats apart, do not coalesce:
-    // the H-free forward runs the lanes layout)
+  } else if (want == SSCAN_LAYOUT_AUTO && sg_ok && *lanes == sg_lanes) {
     *sg = *chunks == 1 && (wgs64 >= 256 || wgs32 >= 128);
   }
   if (*sg) *lanes = sg_lanes;

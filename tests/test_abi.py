@@ -151,38 +151,48 @@ def test_layout_validation_and_choice(lib):
 
 
 def test_plan_select_per_forward_kind(lib):
-    # 8x2048x768x16 (0.75 waves per SIMD in one pass): the forward without H runs the
-    # state-group layout in one pass, the forward writing H the lanes layout in one pass,
-    # the forward keeping boundary states the lanes layout split into 4 T-chunks
+    # 8x2048x768x16 (0.75 waves per SIMD in one pass): the forwards without H, with or
+    # without boundary states, run the state-group layout in one pass (192 workgroups of 32
+    # channels); the forward writing H the lanes layout in one pass
     d = desc(B=8, T=2048, D=768, DS=16)
-    want = {0: (2, 8, 1), 3: (1, 8, 1), 4: (1, 8, 4)}
+    want = {0: (2, 8, 1), 3: (1, 8, 1), 4: (2, 8, 1)}
     for kind, (layout, lanes, chunks) in want.items():
         p = sscan_plan()
         assert lib.sscan_plan_select(ctypes.byref(d), kind, ctypes.byref(p)) == OK
         assert (p.layout, p.lanes, p.chunks) == (layout, lanes, chunks), kind
+    # where the state-group layout cannot run (D not a multiple of 4), the forward keeping
+    # boundary states splits the lanes layout to three waves per SIMD
+    d = desc(B=8, T=2048, D=770, DS=16)
+    p = sscan_plan()
+    assert lib.sscan_plan_select(ctypes.byref(d), 4, ctypes.byref(p)) == OK
+    assert (p.layout, p.lanes, p.chunks) == (1, 8, 4)
     # at two waves per SIMD or more nothing is split
     d = desc(B=16, T=4096, D=1024, DS=16)
     p = sscan_plan()
     assert lib.sscan_plan_select(ctypes.byref(d), 4, ctypes.byref(p)) == OK
-    assert (p.layout, p.chunks) == (1, 1)
-    # short sequences keep at least 128 steps per chunk
+    assert (p.layout, p.chunks) == (2, 1)
+    # too few workgroups for one state-group pass: short sequences keep at least 128 steps
+    # per chunk
     d = desc(B=1, T=300, D=64, DS=16)
     assert lib.sscan_plan_select(ctypes.byref(d), 4, ctypes.byref(p)) == OK
-    assert p.chunks == 2
+    assert (p.layout, p.chunks) == (1, 2)
 
 
 def test_forward_workspace_covers_the_hfree_split(lib):
-    # 8x2048x768x16: the forward without H runs one pass in the state-group layout (packed
-    # b/c, 2 MB) while the forward keeping boundary states splits into 4 T-chunks (three
-    # carry-pair blocks of B*D*DS float2, 4.7 MB); one query serves both calls
-    d = desc(B=8, T=2048, D=768, DS=16)
+    # 8x2048x770x16: the forward without H runs one pass in the lanes layout (no workspace)
+    # while the forward keeping boundary states splits into 4 T-chunks (three carry-pair
+    # blocks of B*D*DS float2); one query serves both calls
+    d = desc(B=8, T=2048, D=770, DS=16)
     n = ctypes.c_size_t()
     assert lib.sscan_fwd_workspace(ctypes.byref(d), None, ctypes.byref(n)) == OK
-    assert n.value >= 3 * 8 * 768 * 16 * 8
-    assert n.value >= 8 * 2048 * 2 * 16 * 4
+    assert n.value >= 3 * 8 * 770 * 16 * 8
     p = sscan_plan()
     assert lib.sscan_plan_select(ctypes.byref(d), 0, ctypes.byref(p)) == OK
-    assert (p.layout, p.chunks) == (2, 1)  # the state-group layout, one pass
+    assert (p.layout, p.chunks) == (1, 1)  # the lanes layout, one pass
+    # 8x2048x768x16: both forwards run one state-group pass (packed b/c, 2 MB)
+    d = desc(B=8, T=2048, D=768, DS=16)
+    assert lib.sscan_fwd_workspace(ctypes.byref(d), None, ctypes.byref(n)) == OK
+    assert n.value >= 8 * 2048 * 2 * 16 * 4
     # a chunk count the caller fixes is used as given for both calls
     p = sscan_plan()
     p.lanes, p.chunks = 8, 2
