@@ -32,8 +32,9 @@ def test_tiny_workload_matches_golden(gpu):
     y, hT = run_fwd(to_dev(inp, gpu))
     with open(os.path.join(os.path.dirname(__file__), "golden", "tiny_fwd_oracle.json")) as f:
         doc = json.load(f)
-    assert_close("y", y, np.array(doc["y"]).reshape(w.B, w.T, w.D), TOL_F32)
-    assert_close("hT", hT, np.array(doc["hT"]).reshape(w.B, w.D, w.DS), TOL_F32)
+    e_y = assert_close("y", y, np.array(doc["y"]).reshape(w.B, w.T, w.D), TOL_F32)
+    e_h = assert_close("hT", hT, np.array(doc["hT"]).reshape(w.B, w.D, w.DS), TOL_F32)
+    print(f"tiny_fwd: y rel err {e_y:.2e}, hT rel err {e_h:.2e}")
 
 
 def test_selftest_shape_forward_backward(gpu):
@@ -294,8 +295,9 @@ def test_fwd_f32_full(gpu):
     inp = workloads.make_inputs(w)
     y, hT = run_fwd(to_dev(inp, gpu))
     yr, hTr = oracle.fwd(inp["x"], inp["delta"], inp["A"], inp["b"], inp["c"], inp["h0"])
-    assert_close("y", y, yr, TOL_F32)
-    assert_close("hT", hT, hTr, TOL_F32)
+    e_y = assert_close("y", y, yr, TOL_F32)
+    e_h = assert_close("hT", hT, hTr, TOL_F32)
+    print(f"fwd_f32 full: y rel err {e_y:.2e}, hT rel err {e_h:.2e}")
 
 
 def test_fwd_bf16_full(gpu):
@@ -305,8 +307,8 @@ def test_fwd_bf16_full(gpu):
     y, hT = run_fwd(to_dev(inp, gpu))
     yr, hTr = oracle.fwd(inp["x"], inp["delta"], inp["A"], inp["b"], inp["c"], inp["h0"])
     e_y = assert_close("y", y, yr, TOL_BF16)
-    assert_close("hT", hT, hTr, TOL_F32)
-    print(f"fwd_bf16 full: y rel err {e_y:.2e}")
+    e_h = assert_close("hT", hT, hTr, TOL_F32)
+    print(f"fwd_bf16 full: y rel err {e_y:.2e}, hT rel err {e_h:.2e}")
 
 
 def test_long_chunked_bf16_full(gpu):
@@ -345,9 +347,12 @@ def test_fwd_bwd_f32_full(gpu):
     y, hT, H = run_fwd(g, return_H=True)
     grads = sscan_bwd(g["dy"], g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"], H, None)
     torch.cuda.synchronize()
-    yr, hTr = oracle.fwd(inp["x"], inp["delta"], inp["A"], inp["b"], inp["c"], inp["h0"])
-    assert_close("y", y, yr, TOL_F32)
-    assert_close("hT", hT, hTr, TOL_F32)
+    yr, hTr, Hr = oracle.fwd(inp["x"], inp["delta"], inp["A"], inp["b"], inp["c"], inp["h0"], return_H=True)
+    e_y = assert_close("y", y, yr, TOL_F32)
+    e_h = assert_close("hT", hT, hTr, TOL_F32)
+    e_H = assert_close("H", H, Hr, TOL_F32)  # every state of every step
+    print(f"fwd_bwd full: y rel err {e_y:.2e}, hT rel err {e_h:.2e}, H rel err {e_H:.2e}")
+    del Hr
     ref = oracle.bwd(inp["dy"], inp["x"], inp["delta"], inp["A"], inp["b"], inp["c"], inp["h0"], None)
     errs = {}
     for name, a, r in zip(["gx", "gdelta", "gb", "gc", "gA", "gh0"], grads, ref):
