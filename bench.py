@@ -284,6 +284,8 @@ def micro_rates():
            "write_stream_GBps": rate(5, 1, 2 << 30) / 1e9,
            "write_stream_nontemporal_GBps": rate(7, 1, 2 << 30) / 1e9,
            "h_store_pattern_8x2048x768x16_GBps": rate(8, 1) / 1e9,
+           "fwd_h_memory_pattern_8x2048x768x16_GBps": rate(9, 1) / 1e9,
+           "fwd_h_memory_pattern_8x2048x768x16_cold_inputs_GBps": rate(10, 1) / 1e9,
            "read_stream_GBps": rate(6, 1, 2 << 30) / 1e9}
     # torch's own fill and copy kernels on 2 GiB, for comparison with the plain streams above
     import torch

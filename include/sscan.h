@@ -100,10 +100,11 @@ typedef struct sscan_desc {
 } sscan_desc;
 
 /* Forward layouts.  LANES: a 64-lane wave holds 64/lanes channels, the states of a channel
- * split over `lanes` consecutive lanes (the only layout of the backward and of a forward
- * that writes H).  STATE_GROUPS: a workgroup holds 64 (or 32) channels, one per lane, and
- * the states of a channel in pairs across its waves (DS in {4, 8, 16}, D a multiple of 4,
- * T < 2^24, no H; its plan.lanes, the threads per channel, is DS/2). */
+ * split over `lanes` consecutive lanes (the only layout of the backward).  STATE_GROUPS: a
+ * workgroup holds 64 (or 32) channels, one per lane, and the states of a channel in pairs
+ * across its waves (DS in {4, 8, 16}, D a multiple of 4, T < 2^24; writing H, DS = 16 and
+ * 32 channels; its plan.lanes, the threads per channel, is DS/2).  Both layouts form every
+ * state with the same operations, so hT, H and the boundary states agree bit for bit. */
 typedef enum sscan_layout { SSCAN_LAYOUT_AUTO = 0, SSCAN_LAYOUT_LANES = 1, SSCAN_LAYOUT_STATE_GROUPS = 2 } sscan_layout;
 
 /* Launch plan.  Pass NULL wherever a plan is accepted to let the library choose. */
@@ -133,8 +134,11 @@ int sscan_fwd_workspace(const sscan_desc* desc, const sscan_plan* plan, size_t* 
  * scan's carry pairs, the packed b/c of the state-group layout) lives in a static device
  * array of SSCAN_NOALLOC_SCRATCH_BYTES per GPU, which the library holds from its load
  * until the process ends.  This call allocates nothing (no hipMalloc, no torch).
- *   A call whose forward needs more scratch than that (at most what sscan_fwd_workspace
- *   reports for the same desc and plan) returns SSCAN_ERR_WORKSPACE before any GPU call.
+ *   Where the state-group layout's packed b/c would not fit (B*T > 262144 at DS = 16) and
+ *   the plan leaves the layout to the library, the call runs the lanes layout instead.  A
+ *   call whose forward still needs more scratch than the array holds (at most what
+ *   sscan_fwd_workspace reports for the same desc and plan) returns SSCAN_ERR_WORKSPACE
+ *   before any GPU call.
  *   Every call on one GPU shares its array: calls that overlap in time on one GPU (two
  *   streams, or two threads) race and give undefined results; calls in one stream order are
  *   safe.  Nothing in the array needs to start at zero: every call writes the scratch it

@@ -104,14 +104,17 @@ __device__ __forceinline__ void fmac_bcast_rt(float& acc, float c, float h, int 
 // one tile: 32 steps of 64 channels or 64 of 32.
 constexpr int kSgReducerWaves = 4;
 constexpr int kSgTileElems = 2048;
+// store waves of the forward writing H (MODE 3)
+constexpr int kSgStoreWaves = 4;
 
-template <int DS, int K, int CW>
+template <int DS, int K, int CW, int MODE>
 __host__ __device__ constexpr int sg_threads() {
-  return 64 * ((DS / K) / (64 / CW) + kSgReducerWaves);
+  return 64 * ((DS / K) / (64 / CW) + kSgReducerWaves + (MODE == 3 ? kSgStoreWaves : 0));
 }
 
 // MODE: 0 the two-level scan's local pass (only the chunk pair leaves the kernel), 1 y and
-// hT, 2 y, hT and the H-free path's boundary states.  CW: channels per wave (64 or 32); a
+// hT, 2 y, hT and the H-free path's boundary states, 3 y, hT and every state H (DS = 16,
+// CW = 32, two states per lane only; see below).  CW: channels per wave (64 or 32); a
 // wave holds 64/CW state groups, one per CW/16 rows, so every 16-lane row belongs to a
 // single group and its DPP row broadcasts stay within it.
 //
@@ -129,20 +132,39 @@ __host__ __device__ constexpr int sg_threads() {
 // same kernel with the staging and the sum over groups done by the compute waves between
 // two barriers per tile: 16x4096x1024x16 bf16 292 -> 270 us, 4x2048x2048x16 bf16 90 -> 73 us
 // per call, bitwise the same y and hT.
+//
+// MODE 3 writes H through LDS: a lane's two states of a step land 64 bytes from the next
+// lane's in H, and stores of that shape run at a fraction of the HBM write rate, so each
+// compute lane parks its states in a per-step row laid out as H's (the workgroup's 32
+// channels x 16 states, 2 KB), and after the tile's barrier kSgStoreWaves store waves copy
+// the rows to H with 16-byte stores, each wave's covering 1 KB of one row: the same
+// protocol as the partial readouts, on a double buffer of 16-step tiles (104 KB of LDS in
+// all).  The store waves issue no loads: a wave's memory counter retires loads and stores
+// in issue order, so a wave that also loads (the reducers' next tiles) waits for every
+// store issued before the load it needs, which held the H stream to one tile in flight.
+// Within a row a channel's four 16-byte blocks of states are rotated by the channel's bits
+// 2-3, so that a wave's 8-byte parking stores, which all fall in the same block of 32
+// channels, spread over all 64 banks.
 template <typename IO, int DS, int K, int CW, int MODE, bool MAMBA>
-__global__ __launch_bounds__((sg_threads<DS, K, CW>())) void fwd_sg_kernel(const FwdParams p) {
+__global__ __launch_bounds__((sg_threads<DS, K, CW, MODE>())) void fwd_sg_kernel(const FwdParams p) {
   constexpr bool LOCAL = MODE == 0;
+  constexpr bool WH = MODE == 3;        // every state to H, through LDS
   constexpr int NG = DS / K;            // state groups
   constexpr int GPW = 64 / CW;          // state groups per wave
   constexpr int NW = NG / GPW;          // compute waves
   constexpr int NTC = 64 * NW;          // compute threads
   constexpr int NTR = 64 * kSgReducerWaves;  // reducer threads
-  constexpr int TB = kSgTileElems / CW;  // steps per tile
+  constexpr int TB = (WH ? kSgTileElems / 4 : kSgTileElems) / CW;  // steps per tile
   constexpr int S = 4;  // steps per batch: one 16-byte store of partial readouts
   constexpr int E2 = 2 * K;
   constexpr uint32_t ES = sizeof(IO);
   constexpr int TILE = TB * CW;         // (step, channel) elements of a tile
-  constexpr int PER = TILE / NTR;       // elements each reducer thread stages
+  // x and delta are staged in tiles of GS tiles (64 steps in every mode): MODE 3's 16-step
+  // tiles would otherwise fetch them in pieces a quarter the size, which, interleaved
+  // with the H stream, cut its HBM write rate by about 40%
+  constexpr int GS = WH ? 4 : 1;
+  constexpr int TILE_S = GS * TILE;     // (step, channel) elements of a staging tile
+  constexpr int PER = TILE_S / NTR;     // elements each reducer thread stages
   constexpr int NB = TB * E2 / 64;      // 64-float blocks of packed b/c per tile
   constexpr int ITEMS = CW * (TB / 4);  // (channel, 4-step) items of a tile's readout
   // partial readouts: [group][channel][step], the 4-step blocks of a channel's row permuted
@@ -150,14 +172,24 @@ __global__ __launch_bounds__((sg_threads<DS, K, CW>())) void fwd_sg_kernel(const
   constexpr int QM = (TB / 4 < 16 ? TB / 4 : 16) - 1;
   constexpr int PSZ = NG * CW * TB / 4;  // float4 of one partial buffer
   static_assert(CW % 16 == 0 && NG % GPW == 0 && NW >= 1, "rows of one state group");
-  static_assert(TILE % NTR == 0 && TB % S == 0 && TB % kCkptSteps == 0 && kCkptSteps % S == 0 &&
+  static_assert(TILE % NTR == 0 && TB % S == 0 && (MODE != 2 || (TB % kCkptSteps == 0 && kCkptSteps % S == 0)) &&
                     (TB * E2) % 64 == 0 && kSgTile % TB == 0,
                 "tile shape");
+  static_assert(!WH || (DS == 16 && K == 2 && CW == 32), "H is written for DS = 16, two states per lane, 32 channels");
+  constexpr int HROW4 = CW * DS / 4;    // 16-byte blocks of one step's row of H (per workgroup)
+  constexpr int NTS = 64 * kSgStoreWaves;  // store threads (MODE 3)
+  // Prefetch depth of the compute waves' b/c blocks: RB - 1 tiles, 48-64 steps in every
+  // mode (a load issued one 16-step tile ahead arrives after the tile that needs it started)
+  constexpr int RB = WH ? 4 : 2;
+  static_assert(!WH || (TB * HROW4) % NTS == 0, "a tile's rows of H are whole rounds of the store threads");
+  static_assert(!WH || (GS == RB && RB * TB == kSgTile), "MODE 3's added tiles stay within the b/c padding");
 
   // (delta, delta*x) at [buffer][step*CW + channel]; with the wrapper (delta, x), so that
   // the first state group can add the skip term Dskip * x to its partial sums
-  __shared__ float2 s_dw[2 * TILE];
+  __shared__ float2 s_dw[2 * TILE_S];
   __shared__ float4 s_y[LOCAL ? 1 : 2 * PSZ];
+  // MODE 3: the tile's states, [buffer][step][16-byte block], blocks rotated per channel
+  __shared__ float4 s_h[WH ? 2 * TB * HROW4 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -172,8 +204,51 @@ __global__ __launch_bounds__((sg_threads<DS, K, CW>())) void fwd_sg_kernel(const
   const int t_begin = chunk * p.chunk_len;
   const int t_end = min(p.T, t_begin + p.chunk_len);
   const int nsteps_total = t_end - t_begin;
-  const int ntiles = nsteps_total > 0 ? (nsteps_total + TB - 1) / TB : 0;
+  // MODE 3 runs a whole number of prefetch rings: its unrolled tile loops then have no
+  // per-tile condition, which would make the compiler wait for every load in flight where
+  // the paths merge, the prefetched ones included.  The tiles added past the end (at most
+  // 48 steps, within the 64-step padding of the packed b/c) read delta = 0 and b = c = 0,
+  // which leaves the state bit-for-bit unchanged, and store nothing (no rows in range).
+  const int ntiles_used = nsteps_total > 0 ? (nsteps_total + TB - 1) / TB : 0;
+  const int ntiles = WH ? (ntiles_used + RB - 1) / RB * RB : ntiles_used;
 
+  if constexpr (WH) {
+    if (w >= NW + kSgReducerWaves) {
+      // ---- store waves: copy each tile's parked states to H after the tile's barrier
+      const int rt = tid - NTC - NTR;
+      // copy tile `it`'s parked states to H.  Block q of the tile is step q / HROW4 and
+      // position q % HROW4 of its row: channel cc = pos / 4 and, undoing the rotation, state
+      // block (pos - cc / 4) % 4.  Rows past the chunk fall outside the resource, channels
+      // past D are forced out of range.
+      auto store_h = [&](int it) {
+        const int ts = t_begin + it * TB;
+        const int rows = tile_rows(t_end, ts, TB);  // 0 for a tile past the end
+        float* Hrow = p.H + ((int64_t)bb * p.T + ts) * D * DS;
+        const rsrc_t rH = make_rsrc(Hrow, static_cast<uint32_t>(rows * D * DS) * 4u);
+        const float4* src = s_h + (it & 1) * (TB * HROW4);
+#pragma unroll
+        for (int e = 0; e < TB * HROW4 / NTS; ++e) {
+          const int q = rt + e * NTS;
+          const int r = q / HROW4, pos = q % HROW4;
+          const int cc = pos >> 2, blk = (pos - (cc >> 2)) & 3;
+          const float4 v4 = src[q];
+          const float v[4] = {v4.x, v4.y, v4.z, v4.w};
+          const uint32_t off =
+              d0 + cc < D ? (static_cast<uint32_t>(r * D + d0 + cc) * DS + blk * 4) * 4u : kOutOfRange;
+          buf_store_vec<4, kNonTemporal>(rH, off, v);
+        }
+      };
+      for (int it = 0; it < ntiles; ++it) {
+        __syncthreads();  // tile `it` computed into its buffer; tile it-1's is complete
+        if (it > 0) store_h(it - 1);
+      }
+      if (ntiles > 0) {
+        __syncthreads();
+        store_h(ntiles - 1);
+      }
+      return;
+    }
+  }
   if (w >= NW) {
     // ---- reducer waves: stage the next tile, sum the previous one's partials into y
     const int rt = tid - NTC;
@@ -189,34 +264,34 @@ __global__ __launch_bounds__((sg_threads<DS, K, CW>())) void fwd_sg_kernel(const
       const int dd = d0 + (idx % CW);
       xoff[e] = dd < D ? static_cast<uint32_t>((idx / CW) * D + dd) * ES : kOutOfRange;
     }
-    uint32_t rx[PER], rd[PER];  // raw bits of the tile loaded last
+    uint32_t rx[PER], rd[PER];  // raw bits of the staging tile loaded last
     int pend_rows = 0;
-    auto load_tile = [&](int ts) {
-      const int rows = tile_rows(t_end, ts, TB);
-      pend_rows = rows;
+    auto load_tile = [&](int ts, uint32_t (&lx)[PER], uint32_t (&ld)[PER], int& prow) {
+      const int rows = tile_rows(t_end, ts, GS * TB);
+      prow = rows;
       const rsrc_t rX = make_rsrc(xrow + (int64_t)ts * D, static_cast<uint32_t>(rows * D) * ES);
       const rsrc_t rD = make_rsrc(drow + (int64_t)ts * D, static_cast<uint32_t>(rows * D) * ES);
 #pragma unroll
       for (int e = 0; e < PER; ++e) {
-        rx[e] = buf_load_bits<IO>(rX, xoff[e]);
-        rd[e] = buf_load_bits<IO>(rD, xoff[e]);
+        lx[e] = buf_load_bits<IO>(rX, xoff[e]);
+        ld[e] = buf_load_bits<IO>(rD, xoff[e]);
       }
     };
-    auto store_tile = [&](int buf) {
+    auto store_tile = [&](int buf, const uint32_t (&lx)[PER], const uint32_t (&ld)[PER], int prow) {
 #pragma unroll
       for (int e = 0; e < PER; ++e) {
-        const float xv = bits_to_f32<IO>(rx[e]);
-        const float dv = bits_to_f32<IO>(rd[e]);
+        const float xv = bits_to_f32<IO>(lx[e]);
+        const float dv = bits_to_f32<IO>(ld[e]);
         // padded steps and channels keep delta = 0 (a multiply by a 0/1 mask: a select
         // lets the compiler branch around the softplus)
-        const float keep = (((rt + e * NTR) / CW) < pend_rows && xoff[e] != kOutOfRange) ? 1.f : 0.f;
+        const float keep = (((rt + e * NTR) / CW) < prow && xoff[e] != kOutOfRange) ? 1.f : 0.f;
         const float dl = MAMBA ? softplus_th(dv) * keep : dv;
-        s_dw[buf * TILE + rt + e * NTR] = make_float2(dl, MAMBA ? xv : dl * xv);
+        s_dw[buf * TILE_S + rt + e * NTR] = make_float2(dl, MAMBA ? xv : dl * xv);
       }
     };
     auto reduce_tile = [&](int it) {
       const int ts = t_begin + it * TB;
-      const int rows = min(TB, t_end - ts);
+      const int rows = tile_rows(t_end, ts, TB);  // 0 for a tile past the end
       const rsrc_t rY = make_rsrc(yrow + (int64_t)ts * D, static_cast<uint32_t>(rows * D) * ES);
       const float* P = reinterpret_cast<const float*>(s_y + (it & 1) * PSZ);
 #pragma unroll
@@ -246,17 +321,28 @@ __global__ __launch_bounds__((sg_threads<DS, K, CW>())) void fwd_sg_kernel(const
       }
     };
     if (ntiles > 0) {
-      load_tile(t_begin);
-      store_tile(0);
-      load_tile(t_begin + TB);  // zeros past the end of the chunk
+      load_tile(t_begin, rx, rd, pend_rows);
+      store_tile(0, rx, rd, pend_rows);
+      load_tile(t_begin + GS * TB, rx, rd, pend_rows);  // zeros past the end of the chunk
     }
-    for (int it = 0; it < ntiles; ++it) {
-      __syncthreads();  // tile `it` staged; its partial buffer's previous contents summed
-      if constexpr (!LOCAL) {
-        if (it > 0) reduce_tile(it - 1);
+    // unrolled by GS: the staging tile j + 1 is parked during the last tile of staging tile j
+    // (a condition known at compile time, so the loads' waits stay exact)
+    for (int it0 = 0; it0 < ntiles; it0 += GS) {
+#pragma unroll
+      for (int u = 0; u < GS; ++u) {
+        const int it = it0 + u;
+        if (WH || it < ntiles) {  // WH: ntiles is a multiple of GS
+          __syncthreads();  // tile `it` staged; its partial buffer's previous contents summed
+          if constexpr (!LOCAL) {
+            if (it > 0) reduce_tile(it - 1);
+          }
+          if (u == GS - 1) {
+            const int j = it0 / GS + 1;  // the staging tile after the current one
+            store_tile(j & 1, rx, rd, pend_rows);
+            load_tile(t_begin + (j + 1) * GS * TB, rx, rd, pend_rows);
+          }
+        }
       }
-      store_tile((it + 1) & 1);
-      load_tile(t_begin + (it + 2) * TB);
     }
     if (ntiles > 0) {
       __syncthreads();  // the last tile's partials
@@ -326,8 +412,12 @@ __global__ __launch_bounds__((sg_threads<DS, K, CW>())) void fwd_sg_kernel(const
       dst[k][2] = __uint_as_float(t[2]); dst[k][3] = __uint_as_float(t[3]);
     }
   };
-  float bcA[NB][4], bcB[NB][4];  // b/c blocks: the current tile's and the next one's, alternating
-  if (ntiles > 0) load_bc(t_begin, bcA);
+  // b/c blocks: a ring of RB register sets, tile j in set j % RB; each tile loads tile
+  // it + RB - 1 into the set tile it - 1 used (only buffer loads write these registers)
+  float bcr[RB][NB][4];
+#pragma unroll
+  for (int k = 0; k + 1 < RB; ++k)
+    if (ntiles > 0) load_bc(t_begin + k * TB, bcr[k]);
 
   auto do_tile = [&](int it, const float (&bcv)[NB][4], float (&bcw)[NB][4]) {
     const int ts = t_begin + it * TB;
@@ -336,9 +426,11 @@ __global__ __launch_bounds__((sg_threads<DS, K, CW>())) void fwd_sg_kernel(const
     const rsrc_t rCk = make_rsrc(MODE == 2 ? ckrow + (int64_t)kb0 * D * DS : nullptr,
                                  MODE == 2 ? static_cast<uint32_t>(min(p.nck - kb0, kCkBlocks) * D * DS) * 4u : 0u);
     __syncthreads();  // this tile's inputs are staged; the partial buffer it writes is free
-    load_bc(ts + TB, bcw);
-    const float2* DW = s_dw + buf * TILE;
+    load_bc(ts + (RB - 1) * TB, bcw);
+    const float2* DW = s_dw + ((it / GS) & 1) * TILE_S + (it % GS) * TILE;
     float* const sy = reinterpret_cast<float*>(s_y + (LOCAL ? 0 : buf * PSZ)) + (grp * CW + c) * TB;
+    float* const shw = reinterpret_cast<float*>(s_h + (WH ? buf * (TB * HROW4) : 0)) +
+                       (WH ? c * DS + ((((grp >> 1) + (c >> 2)) & 3) << 2) + ((grp & 1) << 1) : 0);
 
     float2 dwc[S];
 #pragma unroll
@@ -386,6 +478,13 @@ __global__ __launch_bounds__((sg_threads<DS, K, CW>())) void fwd_sg_kernel(const
           a[s][i] = h[i];
         }
       }
+      if constexpr (WH) {
+        // the batch's states into the tile's rows of H (block grp / 2 of the channel,
+        // rotated by its bits 2-3; the half grp % 2 of the block)
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+          *reinterpret_cast<float2*>(shw + (s0 + s) * (HROW4 * 4)) = make_float2(a[s][0], a[s][1]);
+      }
       if constexpr (LOCAL) {
         float dls[S];
 #pragma unroll
@@ -413,9 +512,10 @@ __global__ __launch_bounds__((sg_threads<DS, K, CW>())) void fwd_sg_kernel(const
     }
   };
 
-  for (int it = 0; it < ntiles; it += 2) {
-    do_tile(it, bcA, bcB);
-    if (it + 1 < ntiles) do_tile(it + 1, bcB, bcA);
+  for (int it = 0; it < ntiles; it += RB) {
+#pragma unroll
+    for (int u = 0; u < RB; ++u)
+      if (WH || it + u < ntiles) do_tile(it + u, bcr[u], bcr[(u + RB - 1) % RB]);  // WH: ntiles % RB == 0
   }
   if (ntiles > 0) __syncthreads();  // the reducers' last barrier: this tile's partials are complete
 
@@ -442,10 +542,16 @@ hipError_t launch_bc_pack_t(const FwdParams& p, hipStream_t s) {
 
 template <typename IO, int DS, int K, int CW, bool MAMBA>
 hipError_t launch_fwd_sg_t(bool local_pass, const FwdParams& p, unsigned blocks, hipStream_t s) {
-  constexpr int NT = sg_threads<DS, K, CW>();
+  constexpr int NT = sg_threads<DS, K, CW, 0>();
   if (local_pass)
     hipLaunchKernelGGL((fwd_sg_kernel<IO, DS, K, CW, 0, MAMBA>), dim3(blocks), dim3(NT), 0, s, p);
-  else if (p.hck != nullptr)
+  else if (p.H != nullptr) {
+    if constexpr (DS == 16 && K == 2 && CW == 32)
+      hipLaunchKernelGGL((fwd_sg_kernel<IO, DS, K, CW, 3, MAMBA>), dim3(blocks), dim3(sg_threads<DS, K, CW, 3>()), 0,
+                         s, p);
+    else
+      return hipErrorInvalidValue;
+  } else if (p.hck != nullptr)
     hipLaunchKernelGGL((fwd_sg_kernel<IO, DS, K, CW, 2, MAMBA>), dim3(blocks), dim3(NT), 0, s, p);
   else
     hipLaunchKernelGGL((fwd_sg_kernel<IO, DS, K, CW, 1, MAMBA>), dim3(blocks), dim3(NT), 0, s, p);

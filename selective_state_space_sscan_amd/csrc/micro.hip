@@ -98,6 +98,49 @@ __global__ __launch_bounds__(kThreads) void h_pattern_kernel(float* H, float v) 
   }
 }
 
+// The whole memory traffic of the forward writing H at 8x2048x768x16 fp32, without its
+// arithmetic: the same workgroups (a batch row and 32 channels each), x and delta loaded
+// cooperatively one 64-step tile ahead, y written for the tile's elements, and H stored by 8
+// lanes per channel, 8 bytes per lane and step, non-temporal.  The stored values depend on
+// the tile's loads, so the loads complete before the tile's stores, as in the forward.
+__global__ __launch_bounds__(kThreads) void fwd_pattern_kernel(const float* x, const float* dl, float* y, float* H) {
+  constexpr int TB = 64, PER = TB * 32 / kThreads;
+  const int b = blockIdx.x / (kHD / 32);
+  const int d0 = (blockIdx.x % (kHD / 32)) * 32;
+  const int d = d0 + threadIdx.x / 8;
+  const int j = threadIdx.x % 8;
+  float rx[PER], rd[PER];
+  auto load = [&](int ts) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int e = threadIdx.x + k * kThreads;
+      const int64_t off = ((int64_t)b * kHT + ts + e / 32) * kHD + d0 + e % 32;
+      rx[k] = x[off];
+      rd[k] = dl[off];
+    }
+  };
+  load(0);
+  for (int ts = 0; ts < kHT; ts += TB) {
+    float cx[PER], cd[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) { cx[k] = rx[k]; cd[k] = rd[k]; }
+    if (ts + TB < kHT) load(ts + TB);
+    float sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) sum = fmaf(cx[k], cd[k], sum);
+    for (int t = ts; t < ts + TB; ++t) {
+      const f2_t q = {sum, sum + (float)t};
+      const int64_t off = ((int64_t)(b * kHT + t) * kHD + d) * kHDS + j * 2;
+      __builtin_nontemporal_store(q, reinterpret_cast<f2_t*>(H + off));
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int e = threadIdx.x + k * kThreads;
+      y[((int64_t)b * kHT + ts + e / 32) * kHD + d0 + e % 32] = cx[k] + cd[k];
+    }
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void read_stream_kernel(const float4* src, int64_t n, float* out) {
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -145,12 +188,15 @@ extern "C" {
 // which: 0 = v_exp_f32 results/s, 1 = fp32 FMA results/s, 2/3/4 = forward-mix states/s with
 // 1/2/4 states per thread, 5 = write stream bytes/s, 6 = read stream bytes/s, 7 = write
 // stream with non-temporal stores, bytes/s, 8 = the forward's H store pattern at
-// 8x2048x768x16 alone, bytes/s (bytes and waves_per_simd are ignored).
+// 8x2048x768x16 alone, bytes/s, 9 = the whole memory traffic of the forward writing H at
+// that size (x, delta read; y, H written) without its arithmetic, bytes/s, 10 = the same
+// with x, delta and y taken from three copies in turn, so that no launch finds its inputs
+// in the last-level cache (for 8-10 bytes and waves_per_simd are ignored).
 // waves_per_simd: 1..8, the grid size of the compute kernels (256 CUs x 4 SIMDs each);
 // bytes: buffer size of the stream kernels (a multiple of 16, at most 16 GiB).
 // Allocates its own device buffers and stream.  Returns 0 and the rate in *rate, else 1.
 int sscan_micro_rate(int which, int waves_per_simd, int64_t bytes, double* rate) {
-  if (rate == nullptr || which < 0 || which > 8 || waves_per_simd < 1 || waves_per_simd > 8) return 1;
+  if (rate == nullptr || which < 0 || which > 10 || waves_per_simd < 1 || waves_per_simd > 8) return 1;
   if (which >= 5 && which <= 7 && (bytes <= 0 || bytes % 16 != 0 || bytes > (int64_t(16) << 30))) return 1;
   Timer t;
   if (!t.ok) return 1;
@@ -194,6 +240,27 @@ int sscan_micro_rate(int which, int waves_per_simd, int64_t bytes, double* rate)
       hipLaunchKernelGGL(h_pattern_kernel, dim3(kHB * (kHD / 32)), dim3(kThreads), 0, s, H, 1.f);
     }, &ms);
     if (rc == 0) *rate = (double)hbytes / (ms * 1e-3);
+    (void)hipFree(H);
+    return rc;
+  }
+  if (which == 9 || which == 10) {
+    const int64_t n = (int64_t)kHB * kHT * kHD;
+    const int64_t hbytes = n * kHDS * 4;
+    const int copies = which == 10 ? 3 : 1;
+    float *H = nullptr, *io = nullptr;
+    if (hipMalloc(&H, hbytes) != hipSuccess) return 1;
+    if (hipMalloc(&io, copies * 3 * n * sizeof(float)) != hipSuccess) {
+      (void)hipFree(H);
+      return 1;
+    }
+    (void)hipMemsetAsync(io, 0, copies * 3 * n * sizeof(float), t.s);
+    int k = 0;
+    rc = time_launches(t, 6, [&](hipStream_t s) {
+      float* c = io + (int64_t)(k++ % copies) * 3 * n;
+      hipLaunchKernelGGL(fwd_pattern_kernel, dim3(kHB * (kHD / 32)), dim3(kThreads), 0, s, c, c + n, c + 2 * n, H);
+    }, &ms);
+    if (rc == 0) *rate = (double)(hbytes + 3 * n * sizeof(float)) / (ms * 1e-3);
+    (void)hipFree(io);
     (void)hipFree(H);
     return rc;
   }

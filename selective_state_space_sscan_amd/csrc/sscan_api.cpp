@@ -150,21 +150,22 @@ int resolve_plan(const Resolved& r, const sscan_plan* plan, PlanKind kind, int* 
 }
 
 // The forward's plan: lanes, T-chunks, whether the state-group layout runs and its
-// channels per workgroup (cw).  That layout needs DS in {4, 8, 16}, D a multiple of 4,
-// T < 2^24 and no H (with_H).  Chosen by itself for a single pass with at least 256
-// 64-channel or 128 32-channel workgroups, with or without boundary states
-// (16x4096x1024x16 bf16: 0.278 ms against 0.32 ms for lanes; 8x2048x768x16 fp32: 73 us
-// against 137 us); split sequences gain nothing (8x1024x256x16 fp32 in 8 chunks: 28.0 us
-// against 27.5 us for lanes).
+// channels per workgroup (cw).  That layout needs DS in {4, 8, 16}, D a multiple of 4 and
+// T < 2^24, and DS = 16 when it writes H (with_H; then cw = 32).  Chosen by itself for a
+// single pass with at least 256 64-channel or 128 32-channel workgroups, with or without
+// boundary states or H (16x4096x1024x16 bf16: 0.278 ms against 0.32 ms for lanes;
+// 8x2048x768x16 fp32: 73 us against 137 us); split sequences gain nothing (8x1024x256x16
+// fp32 in 8 chunks: 28.0 us against 27.5 us for lanes).
 int resolve_fwd_plan(const Resolved& r, const sscan_plan* plan, bool with_H, bool with_ck, int* lanes, int* chunks,
                      bool* sg, int* cw) {
-  const bool sg_ok = !with_H && (r.DS == 4 || r.DS == 8 || r.DS == 16) && r.D % 4 == 0 && r.T < (1 << 24);
+  const bool sg_ok = (r.DS == 4 || r.DS == 8 || r.DS == 16) && (!with_H || r.DS == 16) && r.D % 4 == 0 &&
+                     r.T < (1 << 24);
   const int sg_lanes = (int)(r.DS / sscan::kSgK);
   const int want = plan != nullptr ? plan->layout : SSCAN_LAYOUT_AUTO;
   if (want == SSCAN_LAYOUT_STATE_GROUPS) {
     if (!sg_ok)
-      return fail(SSCAN_ERR_UNSUPPORTED, "the state-group layout needs DS in {4, 8, 16}, D a multiple of 4, "
-                                         "T < 2^24 and no H");
+      return fail(SSCAN_ERR_UNSUPPORTED, "the state-group layout needs DS in {4, 8, 16} (16 when it writes H), "
+                                         "D a multiple of 4 and T < 2^24");
     if (plan->lanes != 0 && plan->lanes != sg_lanes)
       return fail(SSCAN_ERR_UNSUPPORTED, "the state-group layout runs DS/2 = %d threads per channel, not %d", sg_lanes,
                   plan->lanes);
@@ -195,14 +196,14 @@ int resolve_fwd_plan(const Resolved& r, const sscan_plan* plan, bool with_H, boo
   // channels per workgroup: 64 when that gives at least 256 workgroups per pass, else 32
   // (whose four-wave workgroups measured better from 128 workgroups up: 4x2048x2048x16
   // bf16 0.115 ms against 0.125 ms for lanes and 0.150 ms with 64 channels; 8x2048x768x16
-  // fp32 0.113 against 0.120 and 0.149 ms)
+  // fp32 0.113 against 0.120 and 0.149 ms); the forward writing H runs 32 channels
   const int64_t wgs64 = r.B * ceil_div(r.D, 64) * *chunks, wgs32 = r.B * ceil_div(r.D, 32) * *chunks;
-  *cw = wgs64 >= 256 ? 64 : 32;
+  *cw = (wgs64 >= 256 && !with_H) ? 64 : 32;
   *sg = false;
   if (want == SSCAN_LAYOUT_STATE_GROUPS) {
     *sg = true;
   } else if (want == SSCAN_LAYOUT_AUTO && sg_ok && *lanes == sg_lanes) {
-    *sg = *chunks == 1 && (wgs64 >= 256 || wgs32 >= 128);
+    *sg = *chunks == 1 && (with_H ? wgs32 >= 128 : (wgs64 >= 256 || wgs32 >= 128));
   }
   if (*sg) *lanes = sg_lanes;
   return SSCAN_OK;
@@ -364,7 +365,17 @@ int fwd_impl(bool mamba, const sscan_desc* desc, const sscan_plan* plan, const v
     const hipError_t e = sscan::launch_copy_or_zero(hT, h0, r.B * r.D * r.DS, stream);
     return e == hipSuccess ? ok() : hip_fail(e, "hT <- h0");
   }
-  const FwdLayout lay = fwd_layout(r, chunks, sg);
+  FwdLayout lay = fwd_layout(r, chunks, sg);
+  if (use_scratch && lay.total > SSCAN_NOALLOC_SCRATCH_BYTES && sg &&
+      (plan == nullptr || plan->layout == SSCAN_LAYOUT_AUTO)) {
+    // the state-group layout's packed b/c does not fit the static scratch: the lanes
+    // layout, which packs nothing, keeps such a call within it
+    sscan_plan lp = plan != nullptr ? *plan : sscan_plan{};
+    lp.layout = SSCAN_LAYOUT_LANES;
+    st = resolve_fwd_plan(r, &lp, H != nullptr, hck != nullptr, &lanes, &chunks, &sg, &cw);
+    if (st != SSCAN_OK) return st;
+    lay = fwd_layout(r, chunks, sg);
+  }
   if (use_scratch) {
     if (lay.total > SSCAN_NOALLOC_SCRATCH_BYTES)
       return fail(SSCAN_ERR_WORKSPACE, "this forward needs %zu bytes of scratch; the allocation-free entry point has %zu",
@@ -580,11 +591,13 @@ int sscan_fwd_workspace(const sscan_desc* desc, const sscan_plan* plan, size_t* 
   int lanes, chunks;
   bool sg;
   int cw;
-  // the most that a call without H needs, with boundary states (more T-chunks) or without
-  // (the state-group layout's packed b/c)
+  // the most that any forward needs: without H, with boundary states (more T-chunks) or
+  // without, or writing H (the state-group layout's packed b/c)
   size_t need = 0;
-  for (int ck = 0; ck < 2; ++ck) {
-    st = resolve_fwd_plan(r, plan, false, ck != 0, &lanes, &chunks, &sg, &cw);
+  for (int kind = 0; kind < 3; ++kind) {
+    // a plan forcing the state-group layout below DS = 16 has no call writing H to size
+    if (kind == 2 && plan != nullptr && plan->layout == SSCAN_LAYOUT_STATE_GROUPS && r.DS != 16) continue;
+    st = resolve_fwd_plan(r, plan, kind == 2, kind == 1, &lanes, &chunks, &sg, &cw);
     if (st != SSCAN_OK) return st;
     const size_t t = (r.B == 0 || r.D == 0 || r.T == 0) ? 0 : fwd_layout(r, chunks, sg).total;
     if (t > need) need = t;

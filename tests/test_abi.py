@@ -126,7 +126,8 @@ def test_layout_validation_and_choice(lib):
     p.layout = 3
     assert fwd(lib, desc(), plan=p) == E_UNSUP
     p.layout = SG
-    assert fwd(lib, desc(DS=16), plan=p, H=FAKE) == E_UNSUP   # the state-group layout writes no H
+    assert fwd(lib, desc(DS=8), plan=p, H=FAKE) == E_UNSUP    # it writes H only at DS = 16
+    assert fwd(lib, desc(DS=16), plan=p, H=FAKE) == E_WS      # valid; b/c packing needs workspace
     assert fwd(lib, desc(DS=2), plan=p) == E_UNSUP            # DS in {4, 8, 16}
     assert fwd(lib, desc(DS=16, D=18), plan=p) == E_UNSUP     # D a multiple of 4
     p.lanes = 4                                                # it runs DS/2 = 8 threads per channel
@@ -135,7 +136,7 @@ def test_layout_validation_and_choice(lib):
     assert fwd(lib, desc(DS=16), plan=p) == E_WS               # valid plan; b/c packing needs workspace
     assert bwd(lib, desc(DS=16), plan=p) == E_UNSUP           # the backward runs the lanes layout only
     # the library's choice: state groups for a single pass with 256 or more 64-channel or 128
-    # or more 32-channel workgroups, lanes otherwise (a call with H always runs lanes)
+    # or more 32-channel workgroups, lanes otherwise
     for (B, T, D, DS), (layout, lanes, chunks) in {(16, 4096, 1024, 16): (SG, 8, 1), (8, 1024, 256, 16): (LANES, 8, 8),
                                                    (4, 2048, 2048, 16): (SG, 8, 1), (8, 2048, 768, 16): (SG, 8, 1),
                                                    (2, 4096, 1024, 16): (LANES, 8, 8)}.items():
@@ -151,11 +152,11 @@ def test_layout_validation_and_choice(lib):
 
 
 def test_plan_select_per_forward_kind(lib):
-    # 8x2048x768x16 (0.75 waves per SIMD in one pass): the forwards without H, with or
-    # without boundary states, run the state-group layout in one pass (192 workgroups of 32
-    # channels); the forward writing H the lanes layout in one pass
+    # 8x2048x768x16 (0.75 waves per SIMD in one pass): every forward, without H, keeping
+    # boundary states or writing H, runs the state-group layout in one pass (192 workgroups
+    # of 32 channels)
     d = desc(B=8, T=2048, D=768, DS=16)
-    want = {0: (2, 8, 1), 3: (1, 8, 1), 4: (2, 8, 1)}
+    want = {0: (2, 8, 1), 3: (2, 8, 1), 4: (2, 8, 1)}
     for kind, (layout, lanes, chunks) in want.items():
         p = sscan_plan()
         assert lib.sscan_plan_select(ctypes.byref(d), kind, ctypes.byref(p)) == OK
@@ -166,6 +167,12 @@ def test_plan_select_per_forward_kind(lib):
     p = sscan_plan()
     assert lib.sscan_plan_select(ctypes.byref(d), 4, ctypes.byref(p)) == OK
     assert (p.layout, p.lanes, p.chunks) == (1, 8, 4)
+    # the forward writing H runs the state-group layout only at DS = 16, with 32-channel
+    # workgroups from 128 of them up: 8x2048x768x8 and 2x2048x768x16 (48 workgroups) run lanes
+    for B, DS in ((8, 8), (2, 16)):
+        d = desc(B=B, T=2048, D=768, DS=DS)
+        assert lib.sscan_plan_select(ctypes.byref(d), 3, ctypes.byref(p)) == OK
+        assert p.layout == 1, (B, DS)
     # at two waves per SIMD or more nothing is split
     d = desc(B=16, T=4096, D=1024, DS=16)
     p = sscan_plan()
@@ -357,3 +364,15 @@ def test_noalloc_forward_validates_before_any_gpu_call(lib):
     # problems with nothing to do need no scratch and no GPU
     assert noalloc(lib, desc(B=0)) == OK
     assert noalloc(lib, desc(D=0)) == OK
+
+
+def test_forward_workspace_with_a_state_group_plan_below_ds16(lib):
+    # a plan forcing the state-group layout at DS = 8 is valid for the forwards without H
+    # (the query sizes them) and not for one writing H (which the query then leaves out)
+    p = sscan_plan()
+    p.layout, p.chunks = 2, 2
+    d = desc(B=2, T=63, D=4, DS=8)
+    n = ctypes.c_size_t()
+    assert lib.sscan_fwd_workspace(ctypes.byref(d), ctypes.byref(p), ctypes.byref(n)) == OK
+    assert n.value >= 2 * 64 * 2 * 8 * 4
+    assert fwd(lib, d, plan=p, H=FAKE) == E_UNSUP

@@ -2,7 +2,7 @@
 per lane, a channel's states across the waves of its workgroup, 64 or 32 channels per
 workgroup by the workgroup count) against the fp64 oracle on
 the same seeded inputs, and against the lanes layout: its states come from the same
-operations in the same order, so hT and the boundary states of the H-free path agree bit
+operations in the same order, so hT, H and the boundary states of the H-free path agree bit
 for bit on a single pass; y differs only in the order of the sum over states.
 Tolerances: 1e-4 (fp32 I/O), 2e-2 (bf16 I/O), norm-wise per tensor."""
 import pytest
@@ -95,6 +95,57 @@ def test_state_groups_mamba_wrapper(gpu, B, T, D, DS, io, with_D):
     assert_close("hT", hT, hTr, TOL_F32)
 
 
+H_CASES = [
+    # B, T, D, io, h0, chunks (DS = 16: 32-channel workgroups, 16-step tiles)
+    (2, 100, 64, "f32", True, 1),       # ragged T: the last tile partly past the end
+    (3, 77, 100, "bf16", True, 1),      # ragged D: a partial 32-channel tile
+    (2, 1000, 68, "f32", True, 4),      # two-level scan: chunks of whole 64-step tiles
+    (1, 16, 32, "f32", False, 1),       # exactly one tile
+    (1, 1, 4, "f32", True, 1),
+    (4, 300, 1024, "bf16", False, 1),   # 128 workgroups, the size class the library picks it for
+]
+
+
+@pytest.mark.parametrize("B,T,D,io,h0,chunks", H_CASES)
+def test_state_groups_write_H(gpu, B, T, D, io, h0, chunks):
+    DS = 16
+    announce(f"state-group fwd writing H B={B} T={T} D={D} DS={DS} io={io} h0={h0} chunks={chunks}")
+    inp = inputs(B, T, D, DS, io, h0, seed=91 + T + D)
+    g = to_dev(inp, gpu)
+    y, hT, H = sscan_fwd(g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"], return_H=True,
+                         plan=Plan(0, chunks, SG))
+    torch.cuda.synchronize()
+    yr, hTr, Hr = oracle.fwd(inp["x"], inp["delta"], inp["A"], inp["b"], inp["c"], inp["h0"], return_H=True)
+    assert_close("y", y, yr, tol_for(io))
+    assert_close("hT", hT, hTr, TOL_F32)
+    assert_close("H", H, Hr, TOL_F32)
+    y1, hT1, H1 = sscan_fwd(g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"], return_H=True,
+                            plan=Plan(0, chunks, "lanes"))
+    torch.cuda.synchronize()
+    assert rel_err(y.float(), y1.float()) < (1e-6 if io == "f32" else 1e-2)
+    if chunks == 1:
+        assert torch.equal(H, H1) and torch.equal(hT, hT1)  # the same fma chain per state
+    else:  # the layouts split the sequence at different steps
+        assert rel_err(H, H1) < 1e-6 and rel_err(hT, hT1) < 1e-6
+
+
+def test_state_groups_write_H_mamba_wrapper(gpu):
+    B, T, D, DS = 2, 150, 96, 16
+    announce(f"state-group mamba fwd writing H B={B} T={T} D={D} DS={DS}")
+    w = workloads.custom(B, T, D, DS, io="f32", seed=17, h0_std=0.3, delta_mu=-1.0)
+    inp = workloads.make_inputs(w)
+    g = to_dev(inp, gpu)
+    args = (g["x"], g["delta_raw"], g["A_log"], g["b"], g["c"], g["Dskip"], g["h0"])
+    y, hT, H = sscan_mamba_fwd(*args, return_H=True, plan=Plan(0, 1, SG))
+    y1, hT1, H1 = sscan_mamba_fwd(*args, return_H=True, plan=Plan(0, 1, "lanes"))
+    torch.cuda.synchronize()
+    yr, hTr = oracle.mamba_fwd(inp["x"], inp["delta_raw"], inp["A_log"], inp["b"], inp["c"], inp["Dskip"], inp["h0"])
+    assert_close("y", y, yr, TOL_F32)
+    assert_close("hT", hT, hTr, TOL_F32)
+    assert torch.equal(H, H1) and torch.equal(hT, hT1)
+    assert rel_err(y, y1) < 1e-6
+
+
 def test_default_plan_picks_state_groups_for_many_channels(gpu):
     announce("default plan: 16x512x1024x16 bf16 runs the state-group layout")
     inp = inputs(16, 512, 1024, 16, "bf16", True, seed=3)
@@ -103,3 +154,14 @@ def test_default_plan_picks_state_groups_for_many_channels(gpu):
     y1, hT1 = sscan_fwd(g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"], plan=Plan(0, 1, SG))
     torch.cuda.synchronize()
     assert torch.equal(y, y1) and torch.equal(hT, hT1)
+
+
+def test_default_plan_writes_H_in_state_groups(gpu):
+    announce("default plan: 8x256x768x16 fp32 writing H runs the state-group layout")
+    inp = inputs(8, 256, 768, 16, "f32", True, seed=4)
+    g = to_dev(inp, gpu)
+    out = sscan_fwd(g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"], return_H=True)
+    out1 = sscan_fwd(g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"], return_H=True, plan=Plan(0, 1, SG))
+    torch.cuda.synchronize()
+    for a, b in zip(out, out1):
+        assert torch.equal(a, b)

@@ -62,3 +62,30 @@ def test_noalloc_forward_rejects_more_than_its_scratch(gpu):
     A = -torch.ones(D, DS, device=gpu)
     with pytest.raises(SScanError, match="SSCAN_ERR_WORKSPACE"):
         sscan_fwd_noalloc(x, x, A, bc, bc, plan=Plan(0, 1, "state_groups"))
+
+
+def test_noalloc_forward_writing_H_beyond_its_scratch_runs_the_lanes_layout(gpu):
+    # 128 x 2100 x 64 x 16 writing H: the library's plan, one state-group pass (256
+    # workgroups of 32 channels), would pack 128 * 2100 * 128 B = 34.4 MB of b and c, more
+    # than the 32 MiB array; the allocation-free call runs the lanes layout instead, whose
+    # states and outputs are those of sscan_fwd with a lanes plan, bit for bit
+    B, T, D, DS = 128, 2100, 64, 16
+    announce(f"noalloc fwd writing H, B={B} T={T} D={D} DS={DS}: lanes layout within the scratch")
+    w = workloads.custom(B, T, D, DS, io="f32", seed=71, h0_std=0.3, delta_mu=-1.0)
+    inp = workloads.make_inputs(w)
+    g = to_dev(inp, gpu)
+    assert sscan_fwd_workspace(B, T, D, DS, g["x"].dtype, None) > _lib.SSCAN_NOALLOC_SCRATCH_BYTES
+    ref = sscan_fwd(g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"], plan=Plan(0, 0, "lanes"), return_H=True)
+    y = torch.full_like(g["x"], float("nan"))
+    hT = torch.full((B, D, DS), float("nan"), device=gpu)
+    H = torch.full((B, T, D, DS), float("nan"), device=gpu)
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_allocated(gpu)
+    got = sscan_fwd_noalloc(g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"], y=y, hT=hT, H=H)
+    torch.cuda.synchronize()
+    assert torch.cuda.memory_allocated(gpu) == before
+    for name, a, r in zip(["y", "hT", "H"], got, ref):
+        assert torch.equal(a, r), name
+    yr, hTr = oracle.fwd(inp["x"], inp["delta"], inp["A"], inp["b"], inp["c"], inp["h0"])
+    assert_close("y", got[0], yr, TOL_F32)
+    assert_close("hT", got[1], hTr, TOL_F32)
