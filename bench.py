@@ -58,7 +58,8 @@ def alu_peak_states_per_s() -> float:
 
 PROFILE = os.path.join(ROOT, "profiles", "fwd_bwd_f32_B8_T2048_D768_DS16.md")
 NSETS = 3  # input copies the step-type lines take in turn
-KERNEL_SOURCES = ("fwd_kernel.h", "fwd.hip", "bwd_kernel.h", "bwd.hip", "device_common.h", "sscan_internal.h",
+KERNEL_SOURCES = ("fwd_kernel.h", "fwd.hip", "fwd_sg_kernel.h", "fwd_sg.hip", "bwd_kernel.h", "bwd.hip",
+                  "device_common.h", "sscan_internal.h",
                   "sscan_api.cpp")
 
 
@@ -212,7 +213,9 @@ def main() -> int:
         dom, entry, dom_bytes, dom_ms = ("sscan_bwd (bwd_local_kernel + bwd_kernel sweep + bwd_reduce_kernel)",
                                          "sscan_bwd", bbytes, b_avg)
     else:
-        dom, entry, dom_bytes, dom_ms = "sscan_fwd (fwd_kernel writing H)", "sscan_fwd", fbytes, f_avg
+        kern = ("bc_pack_kernel + fwd_sg_kernel writing H through LDS" if plan_f.layout == "state_groups"
+                else "fwd_kernel writing H")
+        dom, entry, dom_bytes, dom_ms = f"sscan_fwd ({kern})", "sscan_fwd", fbytes, f_avg
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic = committed_traffic(entry)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -226,7 +229,7 @@ def main() -> int:
         "bwd_alg_bytes": int(bbytes),
         "bwd_hbm_frac_as_built": round(bbytes_built / (b_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "bwd_bytes_as_built": int(bbytes_built),
-        "plan_fwd": {"lanes": plan_f.lanes, "chunks": plan_f.chunks},
+        "plan_fwd": {"lanes": plan_f.lanes, "chunks": plan_f.chunks, "layout": plan_f.layout},
         "plan_bwd": {"lanes": plan_b.lanes, "chunks": plan_b.chunks},
         "wall_s_timed": round(wall, 4),
     }
