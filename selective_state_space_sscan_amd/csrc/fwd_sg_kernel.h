@@ -138,8 +138,8 @@ __host__ __device__ constexpr int sg_threads() {
 // compute lane parks its states in a per-step row laid out as H's (the workgroup's 32
 // channels x 16 states, 2 KB), and after the tile's barrier kSgStoreWaves store waves copy
 // the rows to H with 16-byte stores, each wave's covering 1 KB of one row: the same
-// protocol as the partial readouts, on a double buffer of 16-step tiles (104 KB of LDS in
-// all).  The store waves issue no loads: a wave's memory counter retires loads and stores
+// protocol as the partial readouts, on a double buffer of 16-step tiles (with the
+// 128-step x/delta staging, 160 KB of LDS in all).  The store waves issue no loads: a wave's memory counter retires loads and stores
 // in issue order, so a wave that also loads (the reducers' next tiles) waits for every
 // store issued before the load it needs, which held the H stream to one tile in flight.
 // Within a row a channel's four 16-byte blocks of states are rotated by the channel's bits
@@ -159,10 +159,10 @@ __global__ __launch_bounds__((sg_threads<DS, K, CW, MODE>())) void fwd_sg_kernel
   constexpr int E2 = 2 * K;
   constexpr uint32_t ES = sizeof(IO);
   constexpr int TILE = TB * CW;         // (step, channel) elements of a tile
-  // x and delta are staged in tiles of GS tiles (64 steps in every mode): MODE 3's 16-step
-  // tiles would otherwise fetch them in pieces a quarter the size, which, interleaved
-  // with the H stream, cut its HBM write rate by about 40%
-  constexpr int GS = WH ? 4 : 1;
+  // x and delta are staged in tiles of GS tiles (64 or 32 steps in modes 0-2, 128 in
+  // MODE 3, the 160 KB of LDS in all): fetched in MODE 3's 16-step pieces, those reads,
+  // interleaved with the H stream, cut its HBM write rate by about 40%
+  constexpr int GS = WH ? 8 : 1;
   constexpr int TILE_S = GS * TILE;     // (step, channel) elements of a staging tile
   constexpr int PER = TILE_S / NTR;     // elements each reducer thread stages
   constexpr int NB = TB * E2 / 64;      // 64-float blocks of packed b/c per tile
@@ -182,7 +182,7 @@ __global__ __launch_bounds__((sg_threads<DS, K, CW, MODE>())) void fwd_sg_kernel
   // mode (a load issued one 16-step tile ahead arrives after the tile that needs it started)
   constexpr int RB = WH ? 4 : 2;
   static_assert(!WH || (TB * HROW4) % NTS == 0, "a tile's rows of H are whole rounds of the store threads");
-  static_assert(!WH || (GS == RB && RB * TB == kSgTile), "MODE 3's added tiles stay within the b/c padding");
+  static_assert(!WH || (GS % RB == 0 && RB * TB == kSgTile), "whole rings per staging tile");
 
   // (delta, delta*x) at [buffer][step*CW + channel]; with the wrapper (delta, x), so that
   // the first state group can add the skip term Dskip * x to its partial sums
@@ -204,13 +204,15 @@ __global__ __launch_bounds__((sg_threads<DS, K, CW, MODE>())) void fwd_sg_kernel
   const int t_begin = chunk * p.chunk_len;
   const int t_end = min(p.T, t_begin + p.chunk_len);
   const int nsteps_total = t_end - t_begin;
-  // MODE 3 runs a whole number of prefetch rings: its unrolled tile loops then have no
+  // MODE 3 runs a whole number of staging tiles: its unrolled tile loops then have no
   // per-tile condition, which would make the compiler wait for every load in flight where
   // the paths merge, the prefetched ones included.  The tiles added past the end (at most
-  // 48 steps, within the 64-step padding of the packed b/c) read delta = 0 and b = c = 0,
-  // which leaves the state bit-for-bit unchanged, and store nothing (no rows in range).
+  // 112 steps) read delta = 0 (their x/delta rows fall outside the resource) and, for b
+  // and c, the packing's zero padding, the next state group's packed values or zeros past
+  // the buffer: finite values times delta = 0, which leaves the state bit-for-bit
+  // unchanged; they store nothing (no rows of y or H in range).
   const int ntiles_used = nsteps_total > 0 ? (nsteps_total + TB - 1) / TB : 0;
-  const int ntiles = WH ? (ntiles_used + RB - 1) / RB * RB : ntiles_used;
+  const int ntiles = WH ? (ntiles_used + GS - 1) / GS * GS : ntiles_used;
 
   if constexpr (WH) {
     if (w >= NW + kSgReducerWaves) {
