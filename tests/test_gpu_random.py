@@ -1,11 +1,13 @@
 """GPU parity over seeded random problem shapes and launch plans: the forward (with and
-without H, either layout where it applies) and the backward (any lane count and T-chunk
+without H, either layout where it applies; at DS = 16 also H through the state-group
+layout, bitwise the lanes layout's on one pass) and the backward (any lane count and T-chunk
 count), and the H-free pair where DS >= 8, against the fp64 oracle; then the same for the
 Mamba-style wrapper against its oracle.  The shapes are small
 (the oracle finishes in well under a second each) but cover ragged T and D, single steps
 and channels, every DS and both I/O dtypes."""
 import numpy as np
 import pytest
+import torch
 
 import oracle
 import workloads
@@ -65,6 +67,19 @@ def test_random_shape_and_plan(gpu, i):
                            plan=Plan(fplan[0] if fplan[2] != "state_groups" else 0, fplan[1]))
     assert_close("y (with H)", y2, yr, tol_for(io))
     assert_close("H", H, Hr, TOL_F32)
+    if DS == 16 and D % 4 == 0:
+        # H through the state-group layout (LDS rows copied out by store waves), whatever
+        # the library would pick: its states are the lanes layout's bit for bit on one pass
+        fch = fplan[1]
+        y3, hT3, H3 = sscan_fwd(g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"], return_H=True,
+                                plan=Plan(0, fch, "state_groups"))
+        assert_close("y (state groups, with H)", y3, yr, tol_for(io))
+        assert_close("hT (state groups, with H)", hT3, hTr, TOL_F32)
+        assert_close("H (state groups)", H3, Hr, TOL_F32)
+        if fch == 1:
+            _, hT1, H1 = sscan_fwd(g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"], return_H=True,
+                                   plan=Plan(0, 1, "lanes"))
+            assert torch.equal(H3, H1) and torch.equal(hT3, hT1)
 
     ref = oracle.bwd(inp["dy"], inp["x"], inp["delta"], inp["A"], inp["b"], inp["c"], inp["h0"], inp["dhT"])
     grads = sscan_bwd(g["dy"], g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"], H, g["dhT"], plan=Plan(*bplan))
