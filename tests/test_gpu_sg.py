@@ -165,3 +165,24 @@ def test_default_plan_writes_H_in_state_groups(gpu):
     torch.cuda.synchronize()
     for a, b in zip(out, out1):
         assert torch.equal(a, b)
+
+
+def test_state_groups_write_H_full_size_bitwise(gpu):
+    """At the fwd+bwd workload's full size (8x2048x768x16 fp32, 805 MB of H) the state-group
+    forward writing H, the library's choice there, gives every state and hT bit for bit as
+    the lanes layout, and y within fp32 rounding of it (the sum over states runs in another
+    order); both are checked against the fp64 oracle by the full-size parity test."""
+    w = workloads.get("fwd_bwd_f32")
+    announce(f"{w.name}: state groups vs lanes, H bitwise at full size")
+    inp = workloads.make_inputs(w)
+    g = to_dev(inp, gpu)
+    args = (g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"])
+    y, hT, H = sscan_fwd(*args, return_H=True, plan=Plan(0, 1, SG))
+    torch.cuda.synchronize()
+    H_sg = H.cpu()
+    del H
+    y1, hT1, H1 = sscan_fwd(*args, return_H=True, plan=Plan(0, 1, "lanes"))
+    torch.cuda.synchronize()
+    assert torch.equal(hT, hT1)
+    assert torch.equal(H_sg, H1.cpu())
+    assert rel_err(y, y1) < 1e-6
