@@ -138,10 +138,10 @@ __host__ __device__ constexpr int sg_threads() {
 // compute lane parks its states in a per-step row laid out as H's (the workgroup's 32
 // channels x 16 states, 2 KB), and after the tile's barrier kSgStoreWaves store waves copy
 // the rows to H with 16-byte stores, each wave's covering 1 KB of one row: the same
-// protocol as the partial readouts, on a double buffer of 16-step tiles (with the
-// 128-step x/delta staging, 160 KB of LDS in all).  The store waves issue no loads: a wave's memory counter retires loads and stores
-// in issue order, so a wave that also loads (the reducers' next tiles) waits for every
-// store issued before the load it needs, which held the H stream to one tile in flight.
+// protocol as the partial readouts, on a double buffer of 16-step tiles (with the 128-step
+// x/delta staging, 160 KB of LDS in all).  The store waves issue no loads, so nothing they
+// store is waited for before a load is used (a wave's memory counter retires loads and
+// stores in issue order): the reducers' prefetches stay independent of the H stream.
 // Within a row a channel's four 16-byte blocks of states are rotated by the channel's bits
 // 2-3, so that a wave's 8-byte parking stores, which all fall in the same block of 32
 // channels, spread over all 64 banks.
@@ -178,7 +178,7 @@ __global__ __launch_bounds__((sg_threads<DS, K, CW, MODE>())) void fwd_sg_kernel
   static_assert(!WH || (DS == 16 && K == 2 && CW == 32), "H is written for DS = 16, two states per lane, 32 channels");
   constexpr int HROW4 = CW * DS / 4;    // 16-byte blocks of one step's row of H (per workgroup)
   constexpr int NTS = 64 * kSgStoreWaves;  // store threads (MODE 3)
-  // Prefetch depth of the compute waves' b/c blocks: RB - 1 tiles, 48-64 steps in every
+  // Prefetch depth of the compute waves' b/c blocks: RB - 1 tiles, 32-64 steps in every
   // mode (a load issued one 16-step tile ahead arrives after the tile that needs it started)
   constexpr int RB = WH ? 4 : 2;
   static_assert(!WH || (TB * HROW4) % NTS == 0, "a tile's rows of H are whole rounds of the store threads");
@@ -207,10 +207,9 @@ __global__ __launch_bounds__((sg_threads<DS, K, CW, MODE>())) void fwd_sg_kernel
   // MODE 3 runs a whole number of staging tiles: its unrolled tile loops then have no
   // per-tile condition, which would make the compiler wait for every load in flight where
   // the paths merge, the prefetched ones included.  The tiles added past the end (at most
-  // 112 steps) read delta = 0 (their x/delta rows fall outside the resource) and, for b
-  // and c, the packing's zero padding, the next state group's packed values or zeros past
-  // the buffer: finite values times delta = 0, which leaves the state bit-for-bit
-  // unchanged; they store nothing (no rows of y or H in range).
+  // 112 steps) read delta = 0 (their x/delta rows fall outside the resource) and b = c = 0
+  // (the packing's zero padding, or zeros past the padded row), which leaves the state
+  // bit-for-bit unchanged; they store nothing (no rows of y or H in range).
   const int ntiles_used = nsteps_total > 0 ? (nsteps_total + TB - 1) / TB : 0;
   const int ntiles = WH ? (ntiles_used + GS - 1) / GS * GS : ntiles_used;
 
@@ -406,10 +405,12 @@ __global__ __launch_bounds__((sg_threads<DS, K, CW, MODE>())) void fwd_sg_kernel
   auto load_bc = [&](int ts, float (&dst)[NB][4]) {
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
-      // past the end of the row a load reads the next group's (or no) data: such a tile
-      // is never processed
-      const auto t = __builtin_amdgcn_raw_buffer_load_b128(rBC, bcrow + static_cast<uint32_t>(ts) * E2 * 4u + k * 256u,
-                                                           0, 0);
+      // blocks at or past the padded row length load zeros (not the next group's values,
+      // which MODE 3's added tiles would otherwise multiply by delta = 0: a non-finite b
+      // there would make the state NaN)
+      const bool in_row = ts + k * (64 / E2) < p.tpad;
+      const uint32_t off = in_row ? bcrow + static_cast<uint32_t>(ts) * E2 * 4u + k * 256u : kOutOfRange;
+      const auto t = __builtin_amdgcn_raw_buffer_load_b128(rBC, off, 0, 0);
       dst[k][0] = __uint_as_float(t[0]); dst[k][1] = __uint_as_float(t[1]);
       dst[k][2] = __uint_as_float(t[2]); dst[k][3] = __uint_as_float(t[3]);
     }

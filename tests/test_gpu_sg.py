@@ -186,3 +186,24 @@ def test_state_groups_write_H_full_size_bitwise(gpu):
     assert torch.equal(hT, hT1)
     assert torch.equal(H_sg, H1.cpu())
     assert rel_err(y, y1) < 1e-6
+
+
+def test_state_groups_write_H_added_tiles_read_zeros(gpu):
+    """MODE 3 rounds its 16-step tiles up to whole 128-step staging tiles: at T = 130 the packed
+    b/c rows hold 192 steps and the added tiles run to step 256.  Those tiles must read zeros
+    for b and c, not the next state group's packed values: with b infinite in state 2 (state
+    group 1) at step 5, states 0 and 1 (group 0) stay finite and bitwise the lanes layout's."""
+    B, T, D, DS = 1, 130, 32, 16
+    announce(f"state-group fwd writing H, B={B} T={T} D={D}: added tiles past the packed rows")
+    inp = inputs(B, T, D, DS, "f32", True, seed=23)
+    b = inp["b"].clone()
+    b[0, 5, 2] = float("inf")
+    inp["b"] = b
+    g = to_dev(inp, gpu)
+    args = (g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"])
+    _, hT, H = sscan_fwd(*args, return_H=True, plan=Plan(0, 1, SG))
+    _, hT1, H1 = sscan_fwd(*args, return_H=True, plan=Plan(0, 1, "lanes"))
+    torch.cuda.synchronize()
+    assert torch.isfinite(hT[..., :2]).all() and torch.isfinite(H[..., :2]).all()
+    assert torch.equal(hT[..., :2], hT1[..., :2]) and torch.equal(H[..., :2], H1[..., :2])
+    assert not torch.isfinite(hT[..., 2]).all()  # the state the infinite b feeds
