@@ -460,6 +460,12 @@ def bench_fwd_only(dev, warmup, reps):
 
     out = {}
     peak = alu_peak_states_per_s()
+    # what bounds each workload, from the kernel traces and vector-ALU counters (profiles/)
+    bound = {"fwd_f32": "latency: 3.4e7 state updates and 26 MB, run as two passes over 128-step chunks "
+                        "(local pass, full pass)",
+             "fwd_bf16": "VALU issue: the SIMDs issue ~84% of cycles at ~5.8 instructions per state "
+                         "(floor 5 without packed FP32)",
+             "long_chunked_bf16": "VALU latency: one compute wave per SIMD, ~63% of SIMD cycles issuing"}
     for name in ("fwd_f32", "fwd_bf16", "long_chunked_bf16"):
         w = workloads.get(name)
         inp = workloads.make_inputs(w)
@@ -508,7 +514,8 @@ def bench_fwd_only(dev, warmup, reps):
                      "plan": {"lanes": plan.lanes, "chunks": plan.chunks, "layout": plan.layout},
                      "ms": round(ms, 5), "elems_per_s": elems / (ms * 1e-3),
                      "alu_frac": round(states / (ms * 1e-3) / peak, 4),
-                     "hbm_frac": round(fwd_alg_bytes(w.B, w.T, w.D, w.DS, s) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                     "hbm_frac": round(fwd_alg_bytes(w.B, w.T, w.D, w.DS, s) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "bound": bound[name]}
         print(f"bench: fwd-only {name}: {ms:.4f} ms, {elems / (ms * 1e-3):.3e} elem/s", file=sys.stderr, flush=True)
         del sets
         torch.cuda.empty_cache()
