@@ -444,6 +444,13 @@ __global__ __launch_bounds__((sg_threads<DS, K, CW, MODE>())) void fwd_sg_kernel
       if (s0 + S < TB) {
 #pragma unroll
         for (int s = 0; s < S; ++s) dwn[s] = DW[(s0 + S + s) * CW + c];
+        // With 32-channel workgroups (chosen below 256 workgroups of 64, so at most about
+        // one compute wave per SIMD) keep these reads at the top of the batch: left to
+        // itself the compiler issues them at its end, just before their use, and the LDS
+        // latency then stalls a SIMD that has no other compute wave (4x2048x2048 bf16 per
+        // call -4.5%, the forward keeping boundary states -3%).  With two waves per SIMD,
+        // and in MODE 3, the fence costs more than it gains (+3-4%).
+        if constexpr (CW == 32 && !WH) __builtin_amdgcn_sched_barrier(0);
       }
       if constexpr (MODE == 2) {
         // the state entering every kCkptSteps-step block: tiles start on multiples of the
