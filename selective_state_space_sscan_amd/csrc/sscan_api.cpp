@@ -149,13 +149,36 @@ int resolve_plan(const Resolved& r, const sscan_plan* plan, PlanKind kind, int* 
   return SSCAN_OK;
 }
 
+// T-chunks of the plain forward in the state-group layout, or 0 to leave the plan to the
+// lanes layout: one pass from 512 compute waves (B * D * DS/2 lanes / 64) up; below that,
+// enough chunks for about 2048 waves (two per SIMD), a power of two up to 16, as long as
+// the chunks keep at least 256 steps (shorter ones, where the lanes layout's two launches
+// without a packing pass are as fast or faster, go to that layout).  Measured against
+// every chunk count of both layouts: 1x8192x2048x16 bf16 (256 waves per pass) 8 chunks 128
+// us against 199 us for the lanes layout's choice; 4x4096x1536x8 bf16 (384) 8 chunks 118 us
+// against 270; 2x8192x512x8 bf16 (64) 16 chunks 54 us against 92; 8x2048x1024x8 fp32
+// (512) one pass 72 us against 114; within 8% of the fastest plan on every shape tried.
+// 8x1024x256x16 fp32 (it would take 128-step chunks) stays in the lanes layout, as fast
+// there (8 chunks 30 us, 8 state-group chunks 30 us) without the packing pass.
+int sg_plain_chunks(const Resolved& r) {
+  const int64_t waves = ceil_div(r.B * r.D * (r.DS / sscan::kSgK), 64);
+  if (waves >= 512) return 1;
+  int64_t c = 1;
+  while (c < 16 && waves * c < 2048) c *= 2;
+  const int64_t cap = r.T / 128;
+  if (c > cap) c = cap;
+  if (c < 2 || r.T / c < 256) return 0;
+  return (int)c;
+}
+
 // The forward's plan: lanes, T-chunks, whether the state-group layout runs and its
 // channels per workgroup (cw).  That layout needs DS in {4, 8, 16}, D a multiple of 4 and
 // T < 2^24, and DS = 16 when it writes H (with_H; then cw = 32).  Chosen by itself for a
 // single pass with at least 256 64-channel or 128 32-channel workgroups, with or without
 // boundary states or H (16x4096x1024x16 bf16: 0.278 ms against 0.32 ms for lanes;
-// 8x2048x768x16 fp32: 73 us against 137 us); split sequences gain nothing (8x1024x256x16
-// fp32 in 8 chunks: 28.0 us against 27.5 us for lanes).
+// 8x2048x768x16 fp32: 73 us against 137 us).  The plain forward (neither H nor boundary
+// states) runs it wherever it applies unless a split into short T-chunks would be needed
+// (sg_plain_chunks).
 int resolve_fwd_plan(const Resolved& r, const sscan_plan* plan, bool with_H, bool with_ck, int* lanes, int* chunks,
                      bool* sg, int* cw) {
   const bool sg_ok = (r.DS == 4 || r.DS == 8 || r.DS == 16) && (!with_H || r.DS == 16) && r.D % 4 == 0 &&
@@ -172,6 +195,17 @@ int resolve_fwd_plan(const Resolved& r, const sscan_plan* plan, bool with_H, boo
   }
   int st = resolve_plan(r, plan, kPlanFwd, lanes, chunks);
   if (st != SSCAN_OK) return st;
+  const int plain_chunks = (!with_H && !with_ck && sg_ok && want == SSCAN_LAYOUT_AUTO &&
+                            (plan == nullptr || plan->lanes == 0 || plan->lanes == sg_lanes))
+                               ? (plan != nullptr && plan->chunks != 0 ? *chunks : sg_plain_chunks(r))
+                               : 0;
+  if (plain_chunks > 0) {
+    *lanes = sg_lanes;
+    *chunks = plain_chunks;
+    *cw = r.B * ceil_div(r.D, 64) * *chunks >= 256 ? 64 : 32;
+    *sg = true;
+    return SSCAN_OK;
+  }
   // a single pass of the state-group layout with enough workgroups beats every split of the
   // forward keeping boundary states (8x2048x768x16 fp32: 78 us against 110 us for the lanes
   // layout in 4 chunks; 16x4096x1024x16 bf16: 264 against 321-355 us), so that forward

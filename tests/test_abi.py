@@ -135,11 +135,16 @@ def test_layout_validation_and_choice(lib):
     p.lanes = 0
     assert fwd(lib, desc(DS=16), plan=p) == E_WS               # valid plan; b/c packing needs workspace
     assert bwd(lib, desc(DS=16), plan=p) == E_UNSUP           # the backward runs the lanes layout only
-    # the library's choice: state groups for a single pass with 256 or more 64-channel or 128
-    # or more 32-channel workgroups, lanes otherwise
+    # the library's choice for the plain forward: state groups wherever they apply, one pass
+    # from 512 compute waves (B*D*DS/2 lanes / 64) up, else T-chunks towards 2048 waves (a
+    # power of two up to 16) if the chunks keep 256 steps; the lanes layout otherwise
     for (B, T, D, DS), (layout, lanes, chunks) in {(16, 4096, 1024, 16): (SG, 8, 1), (8, 1024, 256, 16): (LANES, 8, 8),
                                                    (4, 2048, 2048, 16): (SG, 8, 1), (8, 2048, 768, 16): (SG, 8, 1),
-                                                   (2, 4096, 1024, 16): (LANES, 8, 8)}.items():
+                                                   (2, 4096, 1024, 16): (SG, 8, 8), (1, 8192, 2048, 16): (SG, 8, 8),
+                                                   (4, 4096, 1536, 8): (SG, 4, 8), (8, 2048, 1024, 8): (SG, 4, 1),
+                                                   (2, 8192, 512, 8): (SG, 4, 16), (16, 2048, 2048, 4): (SG, 2, 1),
+                                                   (8, 1024, 256, 2): (LANES, 2, 8), (8, 1024, 258, 16): (LANES, 8, 8),
+                                                   (1, 300, 64, 16): (LANES, 8, 2), (1, 4096, 1024, 16): (SG, 8, 16)}.items():
         d = desc(B=B, T=T, D=D, DS=DS)
         q = sscan_plan()
         assert lib.sscan_plan_select(ctypes.byref(d), 0, ctypes.byref(q)) == OK
@@ -204,7 +209,8 @@ def test_forward_workspace_covers_the_hfree_split(lib):
     p = sscan_plan()
     p.lanes, p.chunks = 8, 2
     assert lib.sscan_fwd_workspace(ctypes.byref(d), ctypes.byref(p), ctypes.byref(n)) == OK
-    assert 1 * 8 * 768 * 16 * 8 <= n.value < 3 * 8 * 768 * 16 * 8
+    # (one block of carry pairs, plus the state-group layout's packed b/c for the plain forward)
+    assert 1 * 8 * 768 * 16 * 8 <= n.value < 3 * 8 * 768 * 16 * 8 + 8 * 2048 * 2 * 16 * 4 + 4096
 
 
 def test_forward_workspace_required_for_chunked_plan(lib):
@@ -252,7 +258,8 @@ def test_empty_problems_need_no_pointers(lib):
 
 
 def test_plan_select_and_workspace_sizes(lib):
-    cases = {(16, 4096, 1024, 16): 8, (4, 2048, 2048, 16): 8, (8, 2048, 768, 16): 8, (1, 64, 16, 4): 4}
+    cases = {(16, 4096, 1024, 16): 8, (4, 2048, 2048, 16): 8, (8, 2048, 768, 16): 8, (1, 64, 16, 4): 4,
+             (16, 2048, 2048, 4): 2}  # state groups run DS/2 threads per channel
     for (B, T, D, DS), lanes in cases.items():
         d = desc(B=B, T=T, D=D, DS=DS)
         p = sscan_plan()
