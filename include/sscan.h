@@ -105,9 +105,9 @@ typedef struct sscan_desc {
  * across its waves (DS in {4, 8, 16}, D a multiple of 4, T < 2^24; writing H, DS = 16 and
  * 32 channels; its plan.lanes, the threads per channel, is DS/2).  Both layouts form every
  * state with the same operations, so hT, H and the boundary states agree bit for bit.
- * AUTO: the forward without H or boundary states takes state groups wherever they apply,
- * split into T-chunks (of at least 256 steps) when one pass has under 512 compute waves;
- * the forwards writing H or boundary states take them for a single pass with enough
+ * AUTO: the forwards without H (keeping boundary states or not) take state groups wherever
+ * they apply, split into T-chunks (of at least 256 steps) when one pass has under 512
+ * compute waves; the forward writing H takes them at DS = 16 for a single pass with enough
  * workgroups; the lanes layout otherwise (sscan_plan_select reports the choice). */
 typedef enum sscan_layout { SSCAN_LAYOUT_AUTO = 0, SSCAN_LAYOUT_LANES = 1, SSCAN_LAYOUT_STATE_GROUPS = 2 } sscan_layout;
 

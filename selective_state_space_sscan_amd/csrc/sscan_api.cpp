@@ -149,7 +149,7 @@ int resolve_plan(const Resolved& r, const sscan_plan* plan, PlanKind kind, int* 
   return SSCAN_OK;
 }
 
-// T-chunks of the plain forward in the state-group layout, or 0 to leave the plan to the
+// T-chunks of a forward without H in the state-group layout, or 0 to leave the plan to the
 // lanes layout: one pass from 512 compute waves (B * D * DS/2 lanes / 64) up; below that,
 // enough chunks for about 2048 waves (two per SIMD), a power of two up to 16, as long as
 // the chunks keep at least 256 steps (shorter ones, where the lanes layout's two launches
@@ -176,9 +176,10 @@ int sg_plain_chunks(const Resolved& r) {
 // T < 2^24, and DS = 16 when it writes H (with_H; then cw = 32).  Chosen by itself for a
 // single pass with at least 256 64-channel or 128 32-channel workgroups, with or without
 // boundary states or H (16x4096x1024x16 bf16: 0.278 ms against 0.32 ms for lanes;
-// 8x2048x768x16 fp32: 73 us against 137 us).  The plain forward (neither H nor boundary
-// states) runs it wherever it applies unless a split into short T-chunks would be needed
-// (sg_plain_chunks).
+// 8x2048x768x16 fp32: 73 us against 137 us).  The forwards without H (with boundary states
+// or not) run it wherever it applies unless a split into short T-chunks would be needed
+// (sg_plain_chunks; keeping boundary states: 4x4096x1536x8 bf16 8 chunks 116 us against 210
+// us for the lanes layout's choice, 8x2048x1024x8 fp32 one pass 77 against 120 us).
 int resolve_fwd_plan(const Resolved& r, const sscan_plan* plan, bool with_H, bool with_ck, int* lanes, int* chunks,
                      bool* sg, int* cw) {
   const bool sg_ok = (r.DS == 4 || r.DS == 8 || r.DS == 16) && (!with_H || r.DS == 16) && r.D % 4 == 0 &&
@@ -195,7 +196,7 @@ int resolve_fwd_plan(const Resolved& r, const sscan_plan* plan, bool with_H, boo
   }
   int st = resolve_plan(r, plan, kPlanFwd, lanes, chunks);
   if (st != SSCAN_OK) return st;
-  const int plain_chunks = (!with_H && !with_ck && sg_ok && want == SSCAN_LAYOUT_AUTO &&
+  const int plain_chunks = (!with_H && sg_ok && want == SSCAN_LAYOUT_AUTO &&
                             (plan == nullptr || plan->lanes == 0 || plan->lanes == sg_lanes))
                                ? (plan != nullptr && plan->chunks != 0 ? *chunks : sg_plain_chunks(r))
                                : 0;

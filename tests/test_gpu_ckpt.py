@@ -65,7 +65,7 @@ def test_ckpt_gradients_equal_the_H_path_bitwise(gpu, lanes, chunks):
     announce(f"ckpt bitwise vs H path, bwd plan ({lanes},{chunks})")
     inp = case(B, T, D, DS, "f32", seed=931)
     g = to_dev(inp, gpu)
-    one = Plan(8, 1)  # single-chunk forwards: the same states whether kept or not
+    one = Plan(8, 1, "lanes")  # single-chunk forwards in one layout: the same states and y whether kept or not
     y1, hT1, H = sscan_fwd(g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"], return_H=True, plan=one)
     y2, hT2, hck = sscan_fwd_ckpt(g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"], plan=one)
     gH = sscan_bwd(g["dy"], g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"], H, g["dhT"], plan=Plan(lanes, chunks))
@@ -134,12 +134,13 @@ def test_ckpt_workload_size(gpu):
         assert_close(name, a, r, TOL_F32)
 
 
+@pytest.mark.parametrize("layout", ["lanes", "state_groups"])
 @pytest.mark.parametrize("T", [31, 257, 100])
-def test_ckpt_forward_writes_no_block_past_the_end(gpu, T):
+def test_ckpt_forward_writes_no_block_past_the_end(gpu, T, layout):
     """The tail tile's padded batches must not store boundary states: blocks past ceil(T/32)
     would land in the next batch row's blocks, or past the array."""
     B, D, DS = 3, 40, 16
-    announce(f"ckpt guard region T={T}")
+    announce(f"ckpt guard region T={T} layout={layout}")
     inp = case(B, T, D, DS, "f32", seed=970 + T)
     g = to_dev(inp, gpu)
     nck = (T + CK - 1) // CK
@@ -147,7 +148,7 @@ def test_ckpt_forward_writes_no_block_past_the_end(gpu, T):
     guard = 4 * D * DS
     buf = torch.full((n + guard,), 12345.0, dtype=torch.float32, device=gpu)
     hck = buf[:n].view(B, nck, D, DS)
-    sscan_fwd_ckpt(g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"], hck=hck, plan=Plan(8, 1))
+    sscan_fwd_ckpt(g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"], hck=hck, plan=Plan(0, 1, layout))
     torch.cuda.synchronize()
     assert bool((buf[n:] == 12345.0).all()), "a boundary state was written past the array"
     assert torch.equal(hck[:, 0], g["h0"])  # block 0 of every row is h0 itself
