@@ -98,13 +98,23 @@ int resolve_plan(const Resolved& r, const sscan_plan* plan, PlanKind kind, int* 
   // lane: a quarter of the per-workgroup gb/gc partials of one state per lane, and fewer
   // cross-lane sums), split along T for occupancy (8x2048x768x16: 4 lanes and 8 chunks
   // 0.268 ms, 16 lanes and 2 chunks 0.304 ms; the wrapper's 0.273 and 0.302 ms).
+  // Below DS = 16 the backward also keeps four states per lane (DS/4 lanes per channel)
+  // unless that leaves fewer than three waves per SIMD at 16 T-chunks, in which case it
+  // takes more lanes per channel, up to DS (16x2048x2048x4 fp32: one lane and 8 chunks
+  // 416 us against 519 us for four lanes and 2; 2x8192x512x8: eight lanes 125 us against
+  // 166 us for four; 32x1024x1024x8 bf16: two lanes 302 against 334 us).
   int l;
   if (plan != nullptr && plan->lanes != 0) {
     l = plan->lanes;
   } else if (kind == kPlanFwd) {
     l = (int)(r.DS < 8 ? r.DS : 8);
+  } else if (r.DS >= 16) {
+    l = 4;
+  } else if (r.DS >= 4) {
+    l = (int)(r.DS / 4);
+    while (l < r.DS && r.B * r.D * l * 16 < 3 * kLanesOneWavePerSimd) l *= 2;
   } else {
-    l = (int)(r.DS < 4 ? r.DS : 4);
+    l = (int)r.DS;
   }
   int c = 1;
   if (backward) {

@@ -275,6 +275,13 @@ def test_plan_select_and_workspace_sizes(lib):
     d = desc(B=8, T=2048, D=768, DS=16)
     assert lib.sscan_plan_select(ctypes.byref(d), 1, ctypes.byref(p)) == OK
     assert p.lanes == 4 and p.chunks == 8  # 0.375 -> 3 waves per SIMD
+    # below DS = 16: four states per lane, more lanes per channel where 16 chunks would still
+    # leave under three waves per SIMD
+    for (B, T, D, DS), lanes in {(16, 2048, 2048, 4): 1, (32, 1024, 1024, 8): 2, (2, 8192, 512, 8): 8,
+                                 (8, 4096, 256, 4): 4, (2, 50, 7, 2): 2}.items():
+        dd = desc(B=B, T=T, D=D, DS=DS)
+        assert lib.sscan_plan_select(ctypes.byref(dd), 1, ctypes.byref(p)) == OK
+        assert p.lanes == lanes, (B, T, D, DS, p.lanes)
     assert lib.sscan_plan_select(ctypes.byref(d), 2, ctypes.byref(p)) == OK  # the wrapper's backward
     assert p.lanes == 4 and p.chunks == 8
     # backward partial buffers: one (gb, gc) pair per channel tile, step and state, plus gA per batch row
