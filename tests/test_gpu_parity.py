@@ -370,3 +370,46 @@ def test_fwd_bwd_f32_full(gpu):
     res = gradient_identity_residuals(e, f64(y), f64(hT), [f64(t) for t in grads])
     print("fwd_bwd full gradient identity residuals: " + " ".join(f"{r:.1e}" for r in res))
     assert max(res) < 1e-5, res
+
+
+# Shapes where the library's own plans take the branches of its plan rules: the forward in
+# the state-group layout split into T-chunks (one pass would have under 512 compute waves),
+# the forward keeping boundary states likewise, and the backward's four states per lane
+# below DS = 16.  Whole-tensor parity of every output against the oracle.
+AUTO_PLAN_CASES = [
+    # B, T, D, DS, io, (fwd layout, fwd chunks), bwd lanes
+    (1, 4096, 256, 16, "f32", ("state_groups", 16), 4),
+    (2, 4096, 128, 8, "bf16", ("state_groups", 16), 8),
+    (8, 256, 2048, 4, "f32", ("state_groups", 1), 1),
+    (8, 256, 1024, 8, "f32", ("state_groups", 1), 2),
+]
+
+
+@pytest.mark.parametrize("B,T,D,DS,io,fplan,blanes", AUTO_PLAN_CASES)
+def test_library_plans_at_their_rule_branches(gpu, B, T, D, DS, io, fplan, blanes):
+    from selective_state_space_sscan_amd import sscan_bwd_ckpt, sscan_fwd_ckpt, sscan_plan_select
+    w = workloads.custom(B, T, D, DS, io=io, seed=400 + DS, h0_std=0.2, delta_mu=-1.0, with_dy=True, with_dhT=True)
+    inp = workloads.make_inputs(w)
+    g = to_dev(inp, gpu)
+    dt = g["x"].dtype
+    pf, pk, pb = (sscan_plan_select(B, T, D, DS, dt), sscan_plan_select(B, T, D, DS, dt, ckpt=True),
+                  sscan_plan_select(B, T, D, DS, dt, backward=True))
+    announce(f"library plans B={B} T={T} D={D} DS={DS} {io}: fwd {pf} ckpt {pk} bwd {pb}")
+    assert (pf.layout, pf.chunks) == fplan and (pk.layout, pk.chunks) == fplan and pb.lanes == blanes
+    y, hT = sscan_fwd(g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"])
+    yk, hTk, hck = sscan_fwd_ckpt(g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"])
+    _, _, H = sscan_fwd(g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"], return_H=True)
+    grads = sscan_bwd(g["dy"], g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"], H, g["dhT"])
+    gk = sscan_bwd_ckpt(g["dy"], g["x"], g["delta"], g["A"], g["b"], g["c"], hck, g["dhT"]) if DS >= 8 else None
+    torch.cuda.synchronize()
+    yr, hTr = oracle.fwd(inp["x"], inp["delta"], inp["A"], inp["b"], inp["c"], inp["h0"])
+    assert_close("y", y, yr, tol_for(io))
+    assert_close("hT", hT, hTr, TOL_F32)
+    assert_close("y (boundary states kept)", yk, yr, tol_for(io))
+    assert torch.equal(hTk, hT)  # the same layout and chunks: the same states
+    ref = oracle.bwd(inp["dy"], inp["x"], inp["delta"], inp["A"], inp["b"], inp["c"], inp["h0"], inp["dhT"])
+    for name, a, r in zip(["gx", "gdelta", "gb", "gc", "gA", "gh0"], grads, ref):
+        assert_close(name, a, r, TOL_F32)
+    if gk is not None:
+        for name, a, r in zip(["gx", "gdelta", "gb", "gc", "gA", "gh0"], gk, ref):
+            assert_close(name + " (H-free)", a, r, TOL_F32)
