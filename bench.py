@@ -129,7 +129,7 @@ def main() -> int:
                          "the forward's per-state mix in registers, HBM read and write streams) and print them")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: the scan runs on a single MI355X and this build has no multi-GPU "
+        print(f"bench.py measures one GPU: the scan runs on a single MI355X and the library has no multi-GPU "
               f"path (asked for --gpus {args.gpus}).", file=sys.stderr)
         return 2
 
