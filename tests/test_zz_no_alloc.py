@@ -20,6 +20,7 @@ from selective_state_space_sscan_amd import _lib  # noqa: E402
 CALLS = [
     # B, T, D, DS, io, plan (lanes, chunks, layout), with_H
     (8, 600, 1024, 16, "f32", (0, 0, None), True),              # writing H through the state-group layout
+    (1, 4096, 256, 16, "f32", (0, 0, None), False),             # the library's plan: state groups in 16 T-chunks
     (4, 1000, 256, 16, "bf16", (0, 0, "state_groups"), False),  # packed b/c in the scratch (~2 MB)
     (2, 300, 70, 16, "f32", (8, 3, "lanes"), False),            # carry pairs of a 3-chunk two-level scan
     (1, 129, 33, 8, "f32", (0, 0, None), True),                 # the library's own plan, writing H
@@ -33,8 +34,8 @@ def _one(gpu, B, T, D, DS, io, plan, with_H, seed):
     pl = Plan(*plan)
     need = sscan_fwd_workspace(B, T, D, DS, g["x"].dtype, pl)
     assert 0 < need <= _lib.SSCAN_NOALLOC_SCRATCH_BYTES or (need == 0 and plan[2] is None)
-    if with_H and DS == 16 and plan[2] is None:  # the library's plan writes H in state groups here
-        assert sscan_plan_select(B, T, D, DS, g["x"].dtype, with_H=True).layout == "state_groups"
+    if DS == 16 and plan[2] is None and D >= 256:  # the library's plan takes state groups here
+        assert sscan_plan_select(B, T, D, DS, g["x"].dtype, with_H=with_H).layout == "state_groups"
     ref = sscan_fwd(g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"], plan=pl, return_H=with_H)
     y = torch.full_like(g["x"], float("nan"))
     hT = torch.full((B, D, DS), float("nan"), device=gpu)
