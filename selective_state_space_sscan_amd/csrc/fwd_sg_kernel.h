@@ -32,18 +32,22 @@ namespace {
 
 // Packed b/c: element (bb, g, t, e) at ((bb * NG + g) * tpad + t) * 2K + e holds
 // b[bb, t, gK + e] for e < K and c[bb, t, gK + e - K] otherwise (state group g of NG =
-// DS/K); zero for t >= T.  One thread per (bb, g, t) writes its 2K floats together;
-// neighbouring threads take neighbouring steps, so the stores are contiguous.
+// DS/K); zero for t >= T.  One thread per (bb, t, g) writes its 2K floats together.
+// Neighbouring threads take neighbouring state groups of a step, so a wave reads whole
+// rows of b and c, each element once, and writes 64 / NG consecutive steps of each
+// group's row (with steps fastest, every row of b and c is read once per group, by
+// workgroups on different XCDs: 6.3 against 5.7 us at 16x4096x16 bf16; at the smaller
+// sizes the kernel takes ~4.9 us either way, the latency of one cold read and write).
 template <typename IO, int DS, int K>
 __global__ __launch_bounds__(kThreads) void bc_pack_kernel(const FwdParams p) {
   constexpr int NG = DS / K;
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   const int64_t total = (int64_t)p.B * NG * p.tpad;
   if (i >= total) return;
-  const int t = static_cast<int>(i % p.tpad);
-  const int64_t r = i / p.tpad;
-  const int g = static_cast<int>(r % NG);
-  const int64_t bb = r / NG;
+  const int g = static_cast<int>(i % NG);
+  const int64_t r = i / NG;
+  const int t = static_cast<int>(r % p.tpad);
+  const int64_t bb = r / p.tpad;
   float v[2 * K];
 #pragma unroll
   for (int e = 0; e < 2 * K; ++e) v[e] = 0.f;
@@ -56,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void bc_pack_kernel(const FwdParams p) {
       v[K + e] = to_f32(c[e]);
     }
   }
-  store_state<2 * K>(p.bcp + i * 2 * K, v);
+  store_state<2 * K>(p.bcp + ((bb * NG + g) * p.tpad + t) * 2 * K, v);
 }
 
 // Lane LANE of v's 16-lane row, for every lane of the row (DPP row_newbcast); the
