@@ -66,6 +66,8 @@ _lib = None
 def load() -> ctypes.CDLL:
     """Load libsscan.so (built in-tree by ``selective_state_space_sscan_amd.build``)."""
     global _lib
+    if _lib is not None:  # loaded: no lock needed to read the reference
+        return _lib
     with _lock:
         if _lib is not None:
             return _lib

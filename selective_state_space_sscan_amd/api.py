@@ -54,26 +54,61 @@ def _plan_ptr(plan: Optional[Plan]):
     return c, ctypes.byref(c)
 
 
+# The entry points' pointer arguments are declared c_void_p, so plain integers (and None
+# for NULL) pass straight through ctypes.
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
+
+
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream(device: torch.device):
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    """torch's current HIP stream on ``device``, as the integer handle the C ABI takes."""
+    if _raw_stream is not None:
+        return _raw_stream(device.index)
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _call(device: torch.device, fn, *args):
+    """``fn(*args)`` with ``device`` current (the library launches on, and plans for, the
+    current device); no device switch when it already is."""
+    if device.index == torch.cuda.current_device():
+        return fn(*args)
+    with torch.cuda.device(device):
+        return fn(*args)
+
+
+_ws_cache = {}
+
+
+def _ws_bytes(device: torch.device, kind: str, query, d: sscan_desc, plan: Optional[Plan], pp, *extra) -> int:
+    """Workspace bytes of an entry point for (desc, plan), asked of the library once per
+    shape, layout, plan and device (the answer depends on nothing else)."""
+    key = (kind, device.index, d.B, d.T, d.D, d.DS, d.io, d.x_bstride, d.bc_bstride, d.y_bstride,
+           None if plan is None else (plan.lanes, plan.chunks, plan.layout)) + extra
+    n = _ws_cache.get(key)
+    if n is None:
+        nws = ctypes.c_size_t(0)
+        _lib.check(_call(device, query, ctypes.byref(d), pp, *extra, ctypes.byref(nws)))
+        n = _ws_cache[key] = int(nws.value)
+    return n
 
 
 def _batch_stride(t: torch.Tensor, name: str) -> int:
     """Batch stride of a (B, R, C) tensor whose trailing (R, C) block is contiguous and
     whose batch rows do not overlap.  A tensor broadcast over the batch dimension (stride
     0, e.g. from ``expand``) is rejected: the C ABI reads a batch stride of 0 as R*C."""
-    if t.dim() != 3:
-        raise ValueError(f"{name} must be 3-D, got shape {tuple(t.shape)}")
-    B, R, C = t.shape
-    if C > 1 and t.stride(2) != 1 or R > 1 and t.stride(1) != C:
+    shape = t.shape
+    if len(shape) != 3:
+        raise ValueError(f"{name} must be 3-D, got shape {tuple(shape)}")
+    B, R, C = shape
+    s0, s1, s2 = t.stride()
+    if C > 1 and s2 != 1 or R > 1 and s1 != C:
         raise ValueError(f"{name}: the last two dimensions must be contiguous")
-    if B > 1 and t.stride(0) < R * C:
-        raise ValueError(f"{name}: batch rows overlap (batch stride {t.stride(0)} < {R * C})")
-    return t.stride(0) if B > 1 else R * C
+    if B > 1 and s0 < R * C:
+        raise ValueError(f"{name}: batch rows overlap (batch stride {s0} < {R * C})")
+    return s0 if B > 1 else R * C
 
 
 def _rows_view(t: torch.Tensor, name: str) -> Tuple[torch.Tensor, int]:
@@ -86,6 +121,12 @@ def _rows_view(t: torch.Tensor, name: str) -> Tuple[torch.Tensor, int]:
 
 def _same_stride(ts, names):
     """Bring tensors that must share one batch stride to a common layout."""
+    try:  # the common case: every tensor already has the row layout, with one stride
+        strides = [_batch_stride(t, n) for t, n in zip(ts, names)]
+        if all(s_ == strides[0] for s_ in strides):
+            return list(ts), strides[0]
+    except ValueError:
+        pass
     strides = []
     out = []
     for t, n in zip(ts, names):
@@ -286,26 +327,21 @@ def _fwd_call(mamba, x, delta, A, b, c, Dskip, h0, y, hT, H, return_H, plan, wor
     d = _desc(B, T, D, DS, _IO[x.dtype], x_bs, bc_bs, y_bs)
     pc, pp = _plan_ptr(plan)
     if noalloc:
-        with torch.cuda.device(device):
-            st = lib.sscan_fwd_noalloc(ctypes.byref(d), pp, _ptr(x), _ptr(delta), _ptr(A), _ptr(b), _ptr(c),
-                                       _ptr(h0), _ptr(y), _ptr(hT), _ptr(H), _stream(device))
+        st = _call(device, lib.sscan_fwd_noalloc, ctypes.byref(d), pp, _ptr(x), _ptr(delta), _ptr(A), _ptr(b),
+                   _ptr(c), _ptr(h0), _ptr(y), _ptr(hT), _ptr(H), _stream(device))
         _lib.check(st)
         return (y, hT, H) if (return_H or H is not None) else (y, hT)
-    nws = ctypes.c_size_t(0)
-    _lib.check(lib.sscan_fwd_workspace(ctypes.byref(d), pp, ctypes.byref(nws)))
-    ws, wsn = _workspace(int(nws.value), device, workspace)
-    with torch.cuda.device(device):
-        if ckpt:
-            st = lib.sscan_fwd_ckpt(ctypes.byref(d), pp, int(bool(mamba)), _ptr(x), _ptr(delta), _ptr(A), _ptr(b),
-                                    _ptr(c), _ptr(Dskip), _ptr(h0), _ptr(y), _ptr(hT), _ptr(hck), _ptr(ws),
-                                    ctypes.c_size_t(wsn), _stream(device))
-        elif mamba:
-            st = lib.sscan_mamba_fwd(ctypes.byref(d), pp, _ptr(x), _ptr(delta), _ptr(A), _ptr(b), _ptr(c),
-                                     _ptr(Dskip), _ptr(h0), _ptr(y), _ptr(hT), _ptr(H), _ptr(ws),
-                                     ctypes.c_size_t(wsn), _stream(device))
-        else:
-            st = lib.sscan_fwd(ctypes.byref(d), pp, _ptr(x), _ptr(delta), _ptr(A), _ptr(b), _ptr(c), _ptr(h0),
-                               _ptr(y), _ptr(hT), _ptr(H), _ptr(ws), ctypes.c_size_t(wsn), _stream(device))
+    ws, wsn = _workspace(_ws_bytes(device, "fwd", lib.sscan_fwd_workspace, d, plan, pp), device, workspace)
+    if ckpt:
+        st = _call(device, lib.sscan_fwd_ckpt, ctypes.byref(d), pp, int(bool(mamba)), _ptr(x), _ptr(delta), _ptr(A),
+                   _ptr(b), _ptr(c), _ptr(Dskip), _ptr(h0), _ptr(y), _ptr(hT), _ptr(hck), _ptr(ws), wsn,
+                   _stream(device))
+    elif mamba:
+        st = _call(device, lib.sscan_mamba_fwd, ctypes.byref(d), pp, _ptr(x), _ptr(delta), _ptr(A), _ptr(b),
+                   _ptr(c), _ptr(Dskip), _ptr(h0), _ptr(y), _ptr(hT), _ptr(H), _ptr(ws), wsn, _stream(device))
+    else:
+        st = _call(device, lib.sscan_fwd, ctypes.byref(d), pp, _ptr(x), _ptr(delta), _ptr(A), _ptr(b), _ptr(c),
+                   _ptr(h0), _ptr(y), _ptr(hT), _ptr(H), _ptr(ws), wsn, _stream(device))
     _lib.check(st)
     if ckpt:
         return y, hT, hck
@@ -407,28 +443,25 @@ def _bwd_call(mamba, dy, x, delta, A, b, c, Dskip, h0, H, dhT, need_gh0, need_gD
         gD = torch.empty((D,), **f32) if (mamba and need_gD) else None
     d = _desc(B, T, D, DS, _IO[x.dtype], x_bs, bc_bs, 0)
     pc, pp = _plan_ptr(plan)
-    nws = ctypes.c_size_t(0)
     if ckpt:
-        _lib.check(lib.sscan_bwd_ckpt_workspace(ctypes.byref(d), pp, int(bool(mamba)), ctypes.byref(nws)))
+        nws = _ws_bytes(device, "bwd_ckpt", lib.sscan_bwd_ckpt_workspace, d, plan, pp, int(bool(mamba)))
+    elif mamba:
+        nws = _ws_bytes(device, "mamba_bwd", lib.sscan_mamba_bwd_workspace, d, plan, pp)
     else:
-        query = lib.sscan_mamba_bwd_workspace if mamba else lib.sscan_bwd_workspace
-        _lib.check(query(ctypes.byref(d), pp, ctypes.byref(nws)))
-    ws, wsn = _workspace(int(nws.value), device, workspace)
-    with torch.cuda.device(device):
-        if ckpt:
-            st = lib.sscan_bwd_ckpt(ctypes.byref(d), pp, int(bool(mamba)), _ptr(dy), _ptr(dhT), _ptr(x), _ptr(delta),
-                                    _ptr(A), _ptr(b), _ptr(c), _ptr(Dskip), _ptr(hck), _ptr(gx), _ptr(gdelta),
-                                    _ptr(gb), _ptr(gc), _ptr(gA), _ptr(gD), _ptr(gh0), _ptr(ws),
-                                    ctypes.c_size_t(wsn), _stream(device))
-        elif mamba:
-            st = lib.sscan_mamba_bwd(ctypes.byref(d), pp, _ptr(dy), _ptr(dhT), _ptr(x), _ptr(delta), _ptr(A),
-                                     _ptr(b), _ptr(c), _ptr(Dskip), _ptr(h0), _ptr(H), _ptr(gx), _ptr(gdelta),
-                                     _ptr(gA), _ptr(gb), _ptr(gc), _ptr(gD), _ptr(gh0), _ptr(ws),
-                                     ctypes.c_size_t(wsn), _stream(device))
-        else:
-            st = lib.sscan_bwd(ctypes.byref(d), pp, _ptr(dy), _ptr(dhT), _ptr(x), _ptr(delta), _ptr(A), _ptr(b),
-                               _ptr(c), _ptr(h0), _ptr(H), _ptr(gx), _ptr(gdelta), _ptr(gb), _ptr(gc), _ptr(gA),
-                               _ptr(gh0), _ptr(ws), ctypes.c_size_t(wsn), _stream(device))
+        nws = _ws_bytes(device, "bwd", lib.sscan_bwd_workspace, d, plan, pp)
+    ws, wsn = _workspace(nws, device, workspace)
+    if ckpt:
+        st = _call(device, lib.sscan_bwd_ckpt, ctypes.byref(d), pp, int(bool(mamba)), _ptr(dy), _ptr(dhT), _ptr(x),
+                   _ptr(delta), _ptr(A), _ptr(b), _ptr(c), _ptr(Dskip), _ptr(hck), _ptr(gx), _ptr(gdelta), _ptr(gb),
+                   _ptr(gc), _ptr(gA), _ptr(gD), _ptr(gh0), _ptr(ws), wsn, _stream(device))
+    elif mamba:
+        st = _call(device, lib.sscan_mamba_bwd, ctypes.byref(d), pp, _ptr(dy), _ptr(dhT), _ptr(x), _ptr(delta),
+                   _ptr(A), _ptr(b), _ptr(c), _ptr(Dskip), _ptr(h0), _ptr(H), _ptr(gx), _ptr(gdelta), _ptr(gA),
+                   _ptr(gb), _ptr(gc), _ptr(gD), _ptr(gh0), _ptr(ws), wsn, _stream(device))
+    else:
+        st = _call(device, lib.sscan_bwd, ctypes.byref(d), pp, _ptr(dy), _ptr(dhT), _ptr(x), _ptr(delta), _ptr(A),
+                   _ptr(b), _ptr(c), _ptr(h0), _ptr(H), _ptr(gx), _ptr(gdelta), _ptr(gb), _ptr(gc), _ptr(gA),
+                   _ptr(gh0), _ptr(ws), wsn, _stream(device))
     _lib.check(st)
     if mamba:
         return gx, gdelta, gb, gc, gA, gh0, gD
@@ -483,9 +516,8 @@ def sscan_decode(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, b: torch
         raise ValueError("y must have x's dtype and shape")
     y_bs = _batch_stride(y3, "y")
     d = _desc(B, 1, D, DS, _IO[x.dtype], x_bs, bc_bs, y_bs)
-    with torch.cuda.device(device):
-        st = lib.sscan_decode(ctypes.byref(d), _ptr(x3), _ptr(d3), _ptr(A), _ptr(b3), _ptr(c3), _ptr(state),
-                              _ptr(state_out), _ptr(y3), _stream(device))
+    st = _call(device, lib.sscan_decode, ctypes.byref(d), _ptr(x3), _ptr(d3), _ptr(A), _ptr(b3), _ptr(c3),
+               _ptr(state), _ptr(state_out), _ptr(y3), _stream(device))
     _lib.check(st)
     return (y3.squeeze(1) if squeeze else y3), state_out
 

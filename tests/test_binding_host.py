@@ -73,3 +73,36 @@ def test_supplied_fp32_output_passes_through():
     t = torch.empty(2, 8, 4)
     assert api._f32_out(t, (2, 8, 4), "hT") is t
     assert api._f32_out(None, (2, 8, 4), "hT") is None
+
+
+def test_workspace_sizes_are_remembered_per_shape_plan_and_device(monkeypatch):
+    """The binding asks the library for a workspace size once per (entry point, device,
+    shape, strides, plan) and reuses the answer: every remembered size equals a fresh
+    query, and shapes or plans that differ get entries of their own."""
+    import ctypes
+
+    from selective_state_space_sscan_amd import _lib
+    lib = _lib.load()
+    monkeypatch.setattr(api, "_call", lambda device, fn, *args: fn(*args))
+    monkeypatch.setattr(api, "_ws_cache", {})
+    dev = torch.device("cpu")
+    fwd_cases = [(8, 1024, 256, 16, None), (8, 1024, 256, 16, api.Plan(8, 4, "lanes")), (2, 300, 70, 16, None),
+                 (1, 4096, 256, 16, api.Plan(0, 16, "state_groups")), (2, 50, 7, 2, None)]
+    bwd_cases = [(8, 1024, 256, 16, None), (8, 1024, 256, 16, api.Plan(16, 2)), (2, 300, 70, 16, None),
+                 (2, 50, 8, 8, api.Plan(8, 1))]
+    for rep in range(2):
+        for B, T, D, DS, plan in fwd_cases:
+            d = api._desc(B, T, D, DS, 0)
+            _, pp = api._plan_ptr(plan)
+            got = api._ws_bytes(dev, "fwd", lib.sscan_fwd_workspace, d, plan, pp)
+            assert got == api.sscan_fwd_workspace(B, T, D, DS, torch.float32, plan)
+        for B, T, D, DS, plan in bwd_cases:
+            d = api._desc(B, T, D, DS, 0)
+            _, pp = api._plan_ptr(plan)
+            got = api._ws_bytes(dev, "bwd", lib.sscan_bwd_workspace, d, plan, pp)
+            assert got == api.sscan_bwd_workspace(B, T, D, DS, torch.float32, plan)
+            got = api._ws_bytes(dev, "bwd_ckpt", lib.sscan_bwd_ckpt_workspace, d, plan, pp, 1)
+            n = ctypes.c_size_t(0)
+            _lib.check(lib.sscan_bwd_ckpt_workspace(ctypes.byref(d), pp, 1, ctypes.byref(n)))
+            assert got == n.value
+        assert len(api._ws_cache) == len(fwd_cases) + 2 * len(bwd_cases)
