@@ -506,15 +506,23 @@ def bench_fwd_only(dev, warmup, reps):
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
+        # time at least ~25 ms of work: ten calls of the small workload (~0.03 ms each) are
+        # too short a window for a steady figure
         e0.record()
-        for i in range(reps):
+        for i in range(5):
             run(sets[i % ncopy])
         e1.record()
         torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
+        n = max(reps, min(2000, int(25.0 / max(e0.elapsed_time(e1) / 5, 1e-3))))
+        e0.record()
+        for i in range(n):
+            run(sets[i % ncopy])
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n
         elems = w.B * w.T * w.D
         states = elems * w.DS
-        out[name] = {"workload": w.note, "calls": len(bounds),
+        out[name] = {"workload": w.note, "calls": len(bounds), "timed_runs": n,
                      "plan": {"lanes": plan.lanes, "chunks": plan.chunks, "layout": plan.layout},
                      "ms": round(ms, 5), "elems_per_s": elems / (ms * 1e-3),
                      "alu_frac": round(states / (ms * 1e-3) / peak, 4),
