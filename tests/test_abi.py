@@ -156,6 +156,23 @@ def test_layout_validation_and_choice(lib):
     assert n.value >= 16 * 4032 * 2 * 16 * 4
 
 
+def test_state_group_layout_stops_below_2_24_steps(lib):
+    """The state-group forward addresses a batch row's packed b/c (8 DS bytes per step)
+    with 32-bit buffer offsets below 2^31, so it runs only for T < 2^24: at T = 2^24 the
+    library picks the lanes layout by itself and refuses an explicit state-group plan."""
+    LANES, SG = 1, 2
+    for kind in (0, 4):  # the forward, and the forward keeping boundary states
+        for T, layout in ((2 ** 24 - 64, SG), (2 ** 24 - 1, SG), (2 ** 24, LANES), (2 ** 24 + 64, LANES)):
+            d = desc(B=1, T=T, D=4, DS=4)
+            q = sscan_plan()
+            assert lib.sscan_plan_select(ctypes.byref(d), kind, ctypes.byref(q)) == OK
+            assert q.layout == layout, (kind, T)
+    p = sscan_plan()
+    p.layout = SG
+    assert fwd(lib, desc(B=1, T=2 ** 24 - 1, D=4, DS=4), plan=p) == E_WS  # valid; needs its workspace
+    assert fwd(lib, desc(B=1, T=2 ** 24, D=4, DS=4), plan=p) == E_UNSUP
+
+
 def test_plan_select_per_forward_kind(lib):
     # 8x2048x768x16 (0.75 waves per SIMD in one pass): every forward, without H, keeping
     # boundary states or writing H, runs the state-group layout in one pass (192 workgroups

@@ -156,3 +156,23 @@ def test_inputs_broadcast_over_the_batch(gpu):
                      dense["dhT"])
     for name, a, r in zip(GRADS, grads, ref):
         assert_close(name, a, r, TOL_F32)
+
+
+@pytest.mark.parametrize("T,layout", [(2 ** 24 - 64, "state_groups"), (2 ** 24 + 64, "lanes")])
+def test_longest_sequences_on_both_sides_of_the_state_group_limit(gpu, T, layout):
+    """The state-group forward addresses a batch row's packed b/c with 32-bit offsets and
+    runs for T < 2^24; at 2^24 - 64 steps the library's plan is that layout (16 T-chunks of
+    about a million steps), at 2^24 + 64 the lanes layout.  Every element of y and hT of
+    both against the oracle, over the whole sequence."""
+    announce(f"longest sequence 1x{T}x4x4 fp32, {layout} layout")
+    assert sscan.sscan_plan_select(1, T, 4, 4).layout == layout
+    w = workloads.custom(1, T, 4, 4, io="f32", seed=23, h0_std=0.3, delta_mu=-1.0)
+    inp = workloads.make_inputs(w)
+    g = to_dev(inp, gpu)
+    y, hT = sscan_fwd(g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"])
+    torch.cuda.synchronize()
+    y, hT = y.cpu(), hT.cpu()
+    del g
+    yr, hTr = oracle.fwd(inp["x"], inp["delta"], inp["A"], inp["b"], inp["c"], inp["h0"])
+    assert_close("y", y, yr, TOL_F32)
+    assert_close("hT", hT, hTr, TOL_F32)
