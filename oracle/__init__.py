@@ -70,8 +70,10 @@ def default_threads() -> int:
         return max(1, os.cpu_count() or 1)
 
 
-def _f64(a, shape=None, name="array"):
+def _f64(a, shape=None, name="array", required=False):
     if a is None:
+        if required:  # a NULL input the C loops would read
+            raise ValueError(f"{name} is required")
         return None
     if hasattr(a, "detach"):  # torch tensor
         a = a.detach().to("cpu")
@@ -93,14 +95,14 @@ def fwd(x, delta, A, b, c, h0=None, *, return_H=False, nthreads=None):
 
     x, delta: (B,T,D); A: (D,DS); b, c: (B,T,DS); h0: (B,D,DS) or None (zeros).
     """
-    x = _f64(x, name="x")
+    x = _f64(x, name="x", required=True)
     B, T, D = x.shape
-    A = _f64(A, name="A")
+    A = _f64(A, name="A", required=True)
     DS = A.shape[1]
-    delta = _f64(delta, (B, T, D), "delta")
+    delta = _f64(delta, (B, T, D), "delta", required=True)
     A = _f64(A, (D, DS), "A")
-    b = _f64(b, (B, T, DS), "b")
-    c = _f64(c, (B, T, DS), "c")
+    b = _f64(b, (B, T, DS), "b", required=True)
+    c = _f64(c, (B, T, DS), "c", required=True)
     h0 = _f64(h0, (B, D, DS), "h0")
     y = np.empty((B, T, D))
     hT = np.empty((B, D, DS))
@@ -118,14 +120,14 @@ def bwd(dy, x, delta, A, b, c, h0=None, dhT=None, *, nthreads=None):
     gb, gc are summed over channels, gA over batch rows and steps (totals).
     dhT: (B,D,DS) or None (zeros).
     """
-    x = _f64(x, name="x")
+    x = _f64(x, name="x", required=True)
     B, T, D = x.shape
-    A = _f64(A, name="A")
+    A = _f64(A, name="A", required=True)
     DS = A.shape[1]
-    dy = _f64(dy, (B, T, D), "dy")
-    delta = _f64(delta, (B, T, D), "delta")
-    b = _f64(b, (B, T, DS), "b")
-    c = _f64(c, (B, T, DS), "c")
+    dy = _f64(dy, (B, T, D), "dy", required=True)
+    delta = _f64(delta, (B, T, D), "delta", required=True)
+    b = _f64(b, (B, T, DS), "b", required=True)
+    c = _f64(c, (B, T, DS), "c", required=True)
     h0 = _f64(h0, (B, D, DS), "h0")
     dhT = _f64(dhT, (B, D, DS), "dhT")
     gx = np.empty((B, T, D))

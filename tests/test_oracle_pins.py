@@ -342,3 +342,19 @@ def test_workload_generator_is_deterministic():
         if a[k] is not None:
             assert torch.equal(a[k], b[k])
     assert bool((a["delta"] > 0).all()) and bool((a["A"] < 0).all())
+
+
+def test_missing_required_inputs_raise_instead_of_reading_null():
+    """x, delta, A, b, c (and dy for the backward) are required; a None among them raises
+    before the C loops run (they would otherwise read through a NULL pointer)."""
+    inp = workloads.make_inputs(workloads.custom(1, 3, 2, 2, seed=4, with_dy=True))
+    args = [inp[k] for k in ("x", "delta", "A", "b", "c")]
+    for i, name in enumerate(("x", "delta", "A", "b", "c")):
+        bad = list(args)
+        bad[i] = None
+        with pytest.raises(ValueError, match=name):
+            oracle.fwd(*bad)
+        with pytest.raises(ValueError, match=name):
+            oracle.bwd(inp["dy"], *bad)
+    with pytest.raises(ValueError, match="dy"):
+        oracle.bwd(None, *args)
