@@ -85,6 +85,18 @@ def test_descriptor_validation(lib, kw, status):
     assert lib.sscan_last_error()
 
 
+def test_size_limits_are_exact(lib):
+    """The largest accepted sizes (B = 65535, D*DS = 2^22, T = 2^31 - 1) pass validation,
+    one more is refused: the kernels' 32-bit tile offsets are sized for exactly these."""
+    def sizes_ok(**kw):
+        n = ctypes.c_size_t()
+        return lib.sscan_fwd_workspace(ctypes.byref(desc(**kw)), None, ctypes.byref(n))
+    assert sizes_ok(B=65535) == OK and sizes_ok(B=65536) == E_UNSUP
+    assert sizes_ok(D=2 ** 18, DS=16) == OK and sizes_ok(D=2 ** 18 + 1, DS=16) == E_UNSUP
+    assert sizes_ok(D=2 ** 22, DS=1) == OK and sizes_ok(D=2 ** 22 + 1, DS=1) == E_UNSUP
+    assert sizes_ok(B=1, T=2 ** 31 - 1) == OK and sizes_ok(B=1, T=2 ** 31) == E_UNSUP
+
+
 def test_null_descriptor(lib):
     assert fwd(lib, None) == E_NULL
     n = ctypes.c_size_t()

@@ -176,3 +176,25 @@ def test_longest_sequences_on_both_sides_of_the_state_group_limit(gpu, T, layout
     yr, hTr = oracle.fwd(inp["x"], inp["delta"], inp["A"], inp["b"], inp["c"], inp["h0"])
     assert_close("y", y, yr, TOL_F32)
     assert_close("hT", hT, hTr, TOL_F32)
+
+
+@pytest.mark.parametrize("B,T,D,DS", [(65535, 3, 4, 4), (1, 40, 2 ** 18, 16)])
+def test_largest_batch_and_channel_counts(gpu, B, T, D, DS):
+    """The largest batch (B = 65535) and channel count (D*DS = 2^22) the library accepts,
+    forward writing H and backward with the library's own plans: every element of every
+    output against the oracle."""
+    announce(f"largest sizes {B}x{T}x{D}x{DS} fp32: forward writing H + backward")
+    w = workloads.custom(B, T, D, DS, io="f32", seed=29, h0_std=0.3, delta_mu=-1.0, with_dy=True, with_dhT=True)
+    inp = workloads.make_inputs(w)
+    g = to_dev(inp, gpu)
+    y, hT, H = sscan_fwd(g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"], return_H=True)
+    grads = sscan_bwd(g["dy"], g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"], H, g["dhT"])
+    torch.cuda.synchronize()
+    yr, hTr, Hr = oracle.fwd(inp["x"], inp["delta"], inp["A"], inp["b"], inp["c"], inp["h0"], return_H=True)
+    assert_close("y", y, yr, TOL_F32)
+    assert_close("hT", hT, hTr, TOL_F32)
+    assert_close("H", H, Hr, TOL_F32)
+    del Hr, H
+    ref = oracle.bwd(inp["dy"], inp["x"], inp["delta"], inp["A"], inp["b"], inp["c"], inp["h0"], inp["dhT"])
+    for name, got, r in zip(GRADS, grads, ref):
+        assert_close(name, got, r, TOL_F32)
