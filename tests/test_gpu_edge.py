@@ -181,8 +181,8 @@ def test_longest_sequences_on_both_sides_of_the_state_group_limit(gpu, T, layout
 @pytest.mark.parametrize("B,T,D,DS", [(65535, 3, 4, 4), (1, 40, 2 ** 18, 16)])
 def test_largest_batch_and_channel_counts(gpu, B, T, D, DS):
     """The largest batch (B = 65535) and channel count (D*DS = 2^22) the library accepts,
-    forward writing H and backward with the library's own plans: every element of every
-    output against the oracle."""
+    forward writing H and backward with the library's own plans (and at DS = 16 the H-free
+    forward and backward): every element of every output against the oracle."""
     announce(f"largest sizes {B}x{T}x{D}x{DS} fp32: forward writing H + backward")
     w = workloads.custom(B, T, D, DS, io="f32", seed=29, h0_std=0.3, delta_mu=-1.0, with_dy=True, with_dhT=True)
     inp = workloads.make_inputs(w)
@@ -198,3 +198,12 @@ def test_largest_batch_and_channel_counts(gpu, B, T, D, DS):
     ref = oracle.bwd(inp["dy"], inp["x"], inp["delta"], inp["A"], inp["b"], inp["c"], inp["h0"], inp["dhT"])
     for name, got, r in zip(GRADS, grads, ref):
         assert_close(name, got, r, TOL_F32)
+    if DS >= 8:  # the H-free path (its backward runs 8 or 16 lanes per channel)
+        del grads
+        y2, hT2, hck = sscan.sscan_fwd_ckpt(g["x"], g["delta"], g["A"], g["b"], g["c"], g["h0"])
+        grads2 = sscan.sscan_bwd_ckpt(g["dy"], g["x"], g["delta"], g["A"], g["b"], g["c"], hck, g["dhT"])
+        torch.cuda.synchronize()
+        assert_close("y (H-free path)", y2, yr, TOL_F32)
+        assert_close("hT (H-free path)", hT2, hTr, TOL_F32)
+        for name, got, r in zip(GRADS, grads2, ref):
+            assert_close(name + " (H-free path)", got, r, TOL_F32)
