@@ -28,6 +28,8 @@
  *      H              : (B,T,D,DS) contiguous
  *    Only the batch strides are free, so a T-slice of a longer sequence is a
  *    valid argument (input or output) without a copy.
+ *  - Sizes: B <= 65535, T < 2^31 and D*DS <= 2^22 (the kernels address a tile
+ *    with 32-bit offsets); larger ones give SSCAN_ERR_UNSUPPORTED.
  *  - dtypes: x, delta, b, c, y and dy have the descriptor's io dtype (fp32 or
  *    bf16).  A, h0, hT, H, dhT and every gradient are fp32.  Arithmetic and
  *    the state are fp32; y is rounded to bf16 with round-to-nearest-even.
