@@ -91,6 +91,8 @@ def _ws_bytes(device: torch.device, kind: str, query, d: sscan_desc, plan: Optio
     if n is None:
         nws = ctypes.c_size_t(0)
         _lib.check(_call(device, query, ctypes.byref(d), pp, *extra, ctypes.byref(nws)))
+        if len(_ws_cache) >= 4096:  # many distinct shapes (e.g. a varying T): start over
+            _ws_cache.clear()
         n = _ws_cache[key] = int(nws.value)
     return n
 
