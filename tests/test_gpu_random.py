@@ -2,9 +2,10 @@
 without H, either layout where it applies; at DS = 16 also H through the state-group
 layout, bitwise the lanes layout's on one pass) and the backward (any lane count and T-chunk
 count), and the H-free pair where DS >= 8, against the fp64 oracle; then the same for the
-Mamba-style wrapper against its oracle.  The shapes are small
+Mamba-style wrapper against its oracle.  Most shapes are small
 (the oracle finishes in well under a second each) but cover ragged T and D, single steps
-and channels, every DS and both I/O dtypes."""
+and channels, every DS and both I/O dtypes; a dozen medium ones (up to ~2e7 state updates)
+run the same checks with longer sequences and more T-chunks."""
 import numpy as np
 import pytest
 import torch
@@ -49,9 +50,40 @@ def draw_case(i, force_sg=None):
     return B, T, D, DS, io, h0, dhT, (f_lanes, f_chunks, layout), (b_lanes, b_chunks)
 
 
+def draw_medium_case(i):
+    """Shapes up to ~2e7 state updates (a few thousand steps, up to ~1100 channels) with any
+    plan, the library's own included."""
+    rng = np.random.default_rng(90000 + i)
+    B = int(rng.integers(1, 9))
+    T = int(rng.integers(1, 5000))
+    DS = int(rng.choice([1, 2, 4, 8, 16]))
+    D = int(rng.choice([int(rng.integers(1, 1100)), 4 * int(rng.integers(1, 275))]))
+    T = max(1, min(T, int(2e7 // (B * D * DS))))
+    io = "bf16" if rng.random() < 0.3 else "f32"
+    h0 = bool(rng.random() < 0.7)
+    dhT = bool(rng.random() < 0.6)
+    lane_opts = [0] + [l for l in (1, 2, 4, 8, 16) if l <= DS]
+    f_lanes = int(rng.choice(lane_opts + ([DS // 2] * 2 if DS >= 4 else [])))
+    f_chunks = int(rng.choice([0, 0, 1, 2, 3, 5, 8, 16]))
+    sg_ok = DS in (4, 8, 16) and D % 4 == 0 and f_lanes in (0, DS // 2)
+    layout = rng.choice([None, None, "lanes", "state_groups"] if sg_ok else [None, "lanes"])
+    b_lanes = int(rng.choice(lane_opts))
+    b_chunks = int(rng.choice([0, 0, 1, 2, 4, 8, 16]))
+    return B, T, D, DS, io, h0, dhT, (f_lanes, f_chunks, layout), (b_lanes, b_chunks)
+
+
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_shape_and_plan(gpu, i):
-    B, T, D, DS, io, h0, dhT, fplan, bplan = draw_case(i)
+    check_case(gpu, i, draw_case(i))
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_medium_shape_and_plan(gpu, i):
+    check_case(gpu, 10000 + i, draw_medium_case(i))
+
+
+def check_case(gpu, i, case):
+    B, T, D, DS, io, h0, dhT, fplan, bplan = case
     announce(f"random #{i}: B={B} T={T} D={D} DS={DS} io={io} h0={h0} dhT={dhT} fwd plan={fplan} bwd plan={bplan}")
     w = workloads.custom(B, T, D, DS, io=io, seed=7000 + i, h0_std=0.3 if h0 else 0.0, delta_mu=-1.0,
                          with_dy=True, with_dhT=dhT)
