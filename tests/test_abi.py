@@ -97,6 +97,33 @@ def test_size_limits_are_exact(lib):
     assert sizes_ok(B=1, T=2 ** 31 - 1) == OK and sizes_ok(B=1, T=2 ** 31) == E_UNSUP
 
 
+def test_last_error_is_per_thread(lib):
+    """sscan_last_error reports the last failure of the calling thread: threads that fail
+    validation with different sizes at the same time each read back their own message
+    (the ctypes calls release the interpreter lock, so the calls do overlap)."""
+    import threading
+
+    errors = []
+
+    def worker(k):
+        d = desc(B=-1 - k)
+        for _ in range(300):
+            if fwd(lib, d) != E_SHAPE:
+                errors.append((k, "status"))
+                return
+            msg = lib.sscan_last_error().decode()
+            if f"B={-1 - k} " not in msg:
+                errors.append((k, msg))
+                return
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:3]
+
+
 def test_null_descriptor(lib):
     assert fwd(lib, None) == E_NULL
     n = ctypes.c_size_t()
