@@ -465,7 +465,7 @@ def bench_fwd_only(dev, warmup, reps):
     out = {}
     peak = alu_peak_states_per_s()
     # what bounds each workload, from the kernel traces and vector-ALU counters (profiles/)
-    bound = {"fwd_f32": "latency: 3.4e7 state updates and 26 MB, run as two passes over 128-step chunks "
+    bound = {"fwd_f32": "latency: 3.4e7 state updates and 26 MB, run as two passes over 16 chunks of 64 steps "
                         "(local pass, full pass)",
              "fwd_bf16": "VALU issue: the SIMDs issue ~84% of cycles at ~5.8 instructions per state "
                          "(floor 5 without packed FP32)",

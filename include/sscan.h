@@ -110,7 +110,9 @@ typedef struct sscan_desc {
  * AUTO: the forwards without H (keeping boundary states or not) take state groups wherever
  * they apply, split into T-chunks (of at least 256 steps) when one pass has under 512
  * compute waves; the forward writing H takes them at DS = 16 for a single pass with enough
- * workgroups; the lanes layout otherwise (sscan_plan_select reports the choice). */
+ * workgroups; the lanes layout otherwise, where the forward without H or boundary states
+ * splits below one wave per SIMD into T-chunks of whole tiles for up to four waves per SIMD
+ * (sscan_plan_select reports the choice). */
 typedef enum sscan_layout { SSCAN_LAYOUT_AUTO = 0, SSCAN_LAYOUT_LANES = 1, SSCAN_LAYOUT_STATE_GROUPS = 2 } sscan_layout;
 
 /* Launch plan.  Pass NULL wherever a plan is accepted to let the library choose. */

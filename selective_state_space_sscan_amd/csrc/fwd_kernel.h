@@ -148,7 +148,9 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(const FwdParams p) {
   const uint32_t hstep = static_cast<uint32_t>(D) * DS * 4u;  // bytes between steps of H
   const uint32_t hlane = dvalid ? static_cast<uint32_t>(d * DS + j * K) * 4u : kOutOfRange;
 
-  float rx[PER], rd[PER], rb[PER_BC], rc[PER_BC];
+  // the next tile as loaded (raw bits, a bf16 zero-extended): widened only when parked in
+  // LDS, since a widening next to the load makes the compiler wait for the load right there
+  uint32_t rx[PER], rd[PER], rb[PER_BC], rc[PER_BC];
   int pend_rows = 0;  // rows of the tile whose loads are in flight
   // Past the end of the chunk the resource is empty and every load returns 0: the
   // prefetch is issued unconditionally, so that the wait for it never has to cover the
@@ -162,13 +164,13 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(const FwdParams p) {
     const rsrc_t rC = make_rsrc(crow + (int64_t)ts * DS, static_cast<uint32_t>(rows * DS) * ES);
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-      rx[e] = buf_load_elem<IO>(rX, xoff[e]);
-      rd[e] = buf_load_elem<IO>(rD, xoff[e]);
+      rx[e] = buf_load_bits<IO>(rX, xoff[e]);
+      rd[e] = buf_load_bits<IO>(rD, xoff[e]);
     }
 #pragma unroll
     for (int e = 0; e < PER_BC; ++e) {
-      rb[e] = buf_load_elem<IO>(rB, bcoff[e]);
-      rc[e] = buf_load_elem<IO>(rC, bcoff[e]);
+      rb[e] = buf_load_bits<IO>(rB, bcoff[e]);
+      rc[e] = buf_load_bits<IO>(rC, bcoff[e]);
     }
   };
   // The channel a thread stages is the same in every row of a tile (256 is a multiple of CPW).
@@ -184,16 +186,17 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(const FwdParams p) {
       // (a multiply by a 0/1 mask, not a select: a select lets the compiler branch around
       // the softplus, which costs registers across the step code)
       const float keep = ((tid + e * kThreads) / CPW < pend_rows && xoff[e] != kOutOfRange) ? 1.f : 0.f;
-      const float dl = MAMBA ? softplus_th(rd[e]) * keep : rd[e];
-      s_dw[tid + e * kThreads] = make_float2(dl, dl * rx[e]);
-      if constexpr (MAMBA && !LOCAL) s_skip[tid + e * kThreads] = dskip * rx[e];
+      const float xv = bits_to_f32<IO>(rx[e]), dv = bits_to_f32<IO>(rd[e]);
+      const float dl = MAMBA ? softplus_th(dv) * keep : dv;
+      s_dw[tid + e * kThreads] = make_float2(dl, dl * xv);
+      if constexpr (MAMBA && !LOCAL) s_skip[tid + e * kThreads] = dskip * xv;
     }
 #pragma unroll
     for (int e = 0; e < PER_BC; ++e) {
       const int idx = tid + e * kThreads;
       if (BC % kThreads == 0 || idx < BC) {
-        s_b[idx] = rb[e];
-        s_c[idx] = rc[e];
+        s_b[idx] = bits_to_f32<IO>(rb[e]);
+        s_c[idx] = bits_to_f32<IO>(rc[e]);
       }
     }
   };

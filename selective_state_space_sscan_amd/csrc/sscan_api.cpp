@@ -29,8 +29,9 @@ int ok() {
   return SSCAN_OK;
 }
 
-// MI355X: 256 CUs x 4 SIMDs; one wave64 per SIMD is 65536 lanes.
-constexpr int64_t kLanesOneWavePerSimd = 65536;
+// MI355X: 256 CUs x 4 SIMDs; one wave64 per SIMD is 1024 waves, 65536 lanes.
+constexpr int64_t kWavesOnePerSimd = 1024;
+constexpr int64_t kLanesOneWavePerSimd = 64 * kWavesOnePerSimd;
 
 bool valid_ds(int64_t ds) { return ds == 1 || ds == 2 || ds == 4 || ds == 8 || ds == 16; }
 bool pow2_upto16(int64_t v) { return v == 1 || v == 2 || v == 4 || v == 8 || v == 16; }
@@ -140,8 +141,9 @@ int resolve_plan(const Resolved& r, const sscan_plan* plan, PlanKind kind, int* 
       c = plan->chunks;
     } else {
       // Split the sequence when the single pass would leave at least half of the
-      // SIMDs idle, aiming at two waves per SIMD; every chunk keeps at least 128 steps
-      // (8x1024x256x16 fp32: 8 chunks 0.031 ms, 4 chunks 0.036 ms, 16 chunks 0.034 ms).
+      // SIMDs idle, aiming at two waves per SIMD; every chunk keeps at least 128 steps.
+      // The forwards writing H or keeping boundary states in the lanes layout start from
+      // this count; the plain forward there takes lanes_fwd_chunks instead.
       const int64_t lanes_total = r.B * r.D * l;
       if (lanes_total > 0 && 2 * lanes_total <= kLanesOneWavePerSimd) {
         int64_t want = ceil_div(2 * kLanesOneWavePerSimd, lanes_total);
@@ -179,6 +181,28 @@ int sg_plain_chunks(const Resolved& r) {
   if (c > cap) c = cap;
   if (c < 2 || r.T / c < 256) return 0;
   return (int)c;
+}
+
+// T-chunks of a forward without H (or boundary states) in the lanes layout: split when one
+// pass would have under one wave per SIMD, into as many chunks as keep at most four waves
+// per SIMD (whole 256-thread workgroups of 256/L channels), at most 16, each a whole
+// number of the kernel's tiles (a chunk with a partial last tile pays for a whole one).
+// Measured (16 input copies in turn, 600 calls) against the earlier rule of two waves per
+// SIMD from below half a wave: 8x1024x256x16 fp32 16 chunks 25.9 us against 8 chunks 27.2;
+// 16x1024x257x8 6 chunks 44.2 against one pass 58.5; 4x4096x510x16 16 chunks 77.9 against 9
+// chunks 93.2; 2x1000x64x16 16 chunks 14.7 against 7 chunks 25.8; 32x512x130x16 4 chunks
+// 31.6 against one pass 37.5; equal on the other shapes tried (8x1024x258x16, where 14
+// chunks of 74 steps took 41.5 us, is what the whole-tile rounding fixes).
+int lanes_fwd_chunks(const Resolved& r, int l) {
+  const int64_t cpw = kThreads / l;
+  const int64_t waves = r.B * ceil_div(r.D, cpw) * (kThreads / 64);
+  if (waves <= 0 || waves >= kWavesOnePerSimd || r.T <= 0) return 1;
+  int64_t cmax = 4 * kWavesOnePerSimd / waves;
+  if (cmax > 16) cmax = 16;
+  const int64_t tb = sscan::fwd_tile_steps(l);
+  const int64_t chunk = ceil_div(ceil_div(r.T, tb), cmax) * tb;  // whole tiles per chunk
+  const int64_t c = ceil_div(r.T, chunk);
+  return c > 1 ? (int)c : 1;
 }
 
 // The forward's plan: lanes, T-chunks, whether the state-group layout runs and its
@@ -251,6 +275,7 @@ int resolve_fwd_plan(const Resolved& r, const sscan_plan* plan, bool with_H, boo
     *sg = *chunks == 1 && (with_H ? wgs32 >= 128 : (wgs64 >= 256 || wgs32 >= 128));
   }
   if (*sg) *lanes = sg_lanes;
+  if (!*sg && !with_H && !with_ck && (plan == nullptr || plan->chunks == 0)) *chunks = lanes_fwd_chunks(r, *lanes);
   return SSCAN_OK;
 }
 

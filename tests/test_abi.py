@@ -176,14 +176,15 @@ def test_layout_validation_and_choice(lib):
     assert bwd(lib, desc(DS=16), plan=p) == E_UNSUP           # the backward runs the lanes layout only
     # the library's choice for the plain forward: state groups wherever they apply, one pass
     # from 512 compute waves (B*D*DS/2 lanes / 64) up, else T-chunks towards 2048 waves (a
-    # power of two up to 16) if the chunks keep 256 steps; the lanes layout otherwise
-    for (B, T, D, DS), (layout, lanes, chunks) in {(16, 4096, 1024, 16): (SG, 8, 1), (8, 1024, 256, 16): (LANES, 8, 8),
+    # power of two up to 16) if the chunks keep 256 steps; the lanes layout otherwise, split
+    # below one wave per SIMD into chunks of whole tiles for at most four waves per SIMD
+    for (B, T, D, DS), (layout, lanes, chunks) in {(16, 4096, 1024, 16): (SG, 8, 1), (8, 1024, 256, 16): (LANES, 8, 16),
                                                    (4, 2048, 2048, 16): (SG, 8, 1), (8, 2048, 768, 16): (SG, 8, 1),
                                                    (2, 4096, 1024, 16): (SG, 8, 8), (1, 8192, 2048, 16): (SG, 8, 8),
                                                    (4, 4096, 1536, 8): (SG, 4, 8), (8, 2048, 1024, 8): (SG, 4, 1),
                                                    (2, 8192, 512, 8): (SG, 4, 16), (16, 2048, 2048, 4): (SG, 2, 1),
-                                                   (8, 1024, 256, 2): (LANES, 2, 8), (8, 1024, 258, 16): (LANES, 8, 8),
-                                                   (1, 300, 64, 16): (LANES, 8, 2), (1, 4096, 1024, 16): (SG, 8, 16)}.items():
+                                                   (8, 1024, 256, 2): (LANES, 2, 16), (8, 1024, 258, 16): (LANES, 8, 8),
+                                                   (1, 300, 64, 16): (LANES, 8, 5), (1, 4096, 1024, 16): (SG, 8, 16)}.items():
         d = desc(B=B, T=T, D=D, DS=DS)
         q = sscan_plan()
         assert lib.sscan_plan_select(ctypes.byref(d), 0, ctypes.byref(q)) == OK
@@ -247,16 +248,16 @@ def test_plan_select_per_forward_kind(lib):
 
 
 def test_forward_workspace_covers_the_hfree_split(lib):
-    # 8x2048x770x16: the forward without H runs one pass in the lanes layout (no workspace)
-    # while the forward keeping boundary states splits into 4 T-chunks (three carry-pair
-    # blocks of B*D*DS float2); one query serves both calls
+    # 8x2048x770x16 (the lanes layout: D is not a multiple of 4): the forward without H
+    # splits into 5 T-chunks (800 waves in one pass, at most four per SIMD in whole tiles),
+    # the forward keeping boundary states into 4; one query serves both calls
     d = desc(B=8, T=2048, D=770, DS=16)
     n = ctypes.c_size_t()
     assert lib.sscan_fwd_workspace(ctypes.byref(d), None, ctypes.byref(n)) == OK
     assert n.value >= 3 * 8 * 770 * 16 * 8
     p = sscan_plan()
     assert lib.sscan_plan_select(ctypes.byref(d), 0, ctypes.byref(p)) == OK
-    assert (p.layout, p.chunks) == (1, 1)  # the lanes layout, one pass
+    assert (p.layout, p.chunks) == (1, 5)  # the lanes layout, 5 chunks of 448 steps
     # 8x2048x768x16: both forwards run one state-group pass (packed b/c, 2 MB)
     d = desc(B=8, T=2048, D=768, DS=16)
     assert lib.sscan_fwd_workspace(ctypes.byref(d), None, ctypes.byref(n)) == OK
@@ -321,11 +322,12 @@ def test_plan_select_and_workspace_sizes(lib):
         p = sscan_plan()
         assert lib.sscan_plan_select(ctypes.byref(d), 0, ctypes.byref(p)) == OK
         assert p.lanes == lanes, (B, T, D, DS, p.lanes)
-    # the small fp32 workload splits its sequence to fill the GPU
+    # the small fp32 workload splits its sequence to fill the GPU (256 waves in one pass:
+    # 16 chunks of one 64-step tile, four waves per SIMD)
     d = desc(B=8, T=1024, D=256, DS=16)
     p = sscan_plan()
     assert lib.sscan_plan_select(ctypes.byref(d), 0, ctypes.byref(p)) == OK
-    assert p.lanes == 8 and p.chunks == 8
+    assert p.lanes == 8 and p.chunks == 16
     assert lib.sscan_plan_select(ctypes.byref(d), 1, ctypes.byref(p)) == OK
     assert p.lanes == 4 and p.chunks == 16  # 2048 channels x 4 lanes x 16 chunks = 2 waves per SIMD (T caps it)
     d = desc(B=8, T=2048, D=768, DS=16)
