@@ -184,15 +184,16 @@ int sg_plain_chunks(const Resolved& r) {
 }
 
 // T-chunks of a forward without H (or boundary states) in the lanes layout: split when one
-// pass would have under one wave per SIMD, into as many chunks as keep at most four waves
-// per SIMD (whole 256-thread workgroups of 256/L channels), at most 16, each a whole
-// number of the kernel's tiles (a chunk with a partial last tile pays for a whole one).
+// pass would have under one wave per SIMD.  With at most four waves per SIMD (whole
+// 256-thread workgroups of 256/L channels) and at most 16 chunks, the longest chunk needs
+// at least ceil(tiles / cmax) of the kernel's tiles; take the fewest chunks that reach that
+// (a chunk with a partial last tile costs a whole tile, so more chunks would only add work).
 // Measured (16 input copies in turn, 600 calls) against the earlier rule of two waves per
 // SIMD from below half a wave: 8x1024x256x16 fp32 16 chunks 25.9 us against 8 chunks 27.2;
 // 16x1024x257x8 6 chunks 44.2 against one pass 58.5; 4x4096x510x16 16 chunks 77.9 against 9
 // chunks 93.2; 2x1000x64x16 16 chunks 14.7 against 7 chunks 25.8; 32x512x130x16 4 chunks
-// 31.6 against one pass 37.5; equal on the other shapes tried (8x1024x258x16, where 14
-// chunks of 74 steps took 41.5 us, is what the whole-tile rounding fixes).
+// 31.6 against one pass 37.5; equal on the other shapes tried (8x1024x258x16: 8 chunks of
+// two tiles, where 14 chunks of 74 steps, also two tiles each, took 41.5 us).
 int lanes_fwd_chunks(const Resolved& r, int l) {
   const int64_t cpw = kThreads / l;
   const int64_t waves = r.B * ceil_div(r.D, cpw) * (kThreads / 64);
@@ -200,7 +201,7 @@ int lanes_fwd_chunks(const Resolved& r, int l) {
   int64_t cmax = 4 * kWavesOnePerSimd / waves;
   if (cmax > 16) cmax = 16;
   const int64_t tb = sscan::fwd_tile_steps(l);
-  const int64_t chunk = ceil_div(ceil_div(r.T, tb), cmax) * tb;  // whole tiles per chunk
+  const int64_t chunk = ceil_div(ceil_div(r.T, tb), cmax) * tb;  // the longest chunk, in whole tiles
   const int64_t c = ceil_div(r.T, chunk);
   return c > 1 ? (int)c : 1;
 }

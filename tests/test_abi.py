@@ -249,7 +249,7 @@ def test_plan_select_per_forward_kind(lib):
 
 def test_forward_workspace_covers_the_hfree_split(lib):
     # 8x2048x770x16 (the lanes layout: D is not a multiple of 4): the forward without H
-    # splits into 5 T-chunks (800 waves in one pass, at most four per SIMD in whole tiles),
+    # splits into 5 T-chunks (800 waves in one pass: at most 5 chunks for four per SIMD),
     # the forward keeping boundary states into 4; one query serves both calls
     d = desc(B=8, T=2048, D=770, DS=16)
     n = ctypes.c_size_t()
@@ -257,7 +257,7 @@ def test_forward_workspace_covers_the_hfree_split(lib):
     assert n.value >= 3 * 8 * 770 * 16 * 8
     p = sscan_plan()
     assert lib.sscan_plan_select(ctypes.byref(d), 0, ctypes.byref(p)) == OK
-    assert (p.layout, p.chunks) == (1, 5)  # the lanes layout, 5 chunks of 448 steps
+    assert (p.layout, p.chunks) == (1, 5)  # the lanes layout, 5 chunks of at most 7 tiles
     # 8x2048x768x16: both forwards run one state-group pass (packed b/c, 2 MB)
     d = desc(B=8, T=2048, D=768, DS=16)
     assert lib.sscan_fwd_workspace(ctypes.byref(d), None, ctypes.byref(n)) == OK
